@@ -1,0 +1,194 @@
+/*
+ * moe.h -- C ABI of the routed mixture-of-experts FFN layer for AMD MI355X
+ * (gfx950).
+ *
+ * The layer (router softmax, top-k of E experts, SwiGLU experts with int8 or
+ * int4 block-quantised weights, weighted combine plus an always-on shared
+ * expert) is the MoE step of a Qwen3.6-35B-A3B-shaped model: 256 experts,
+ * top-8 ("Qwen3.6-35B-A3B: pictures, several requests at once and speed",
+ * introduction).  Its pieces follow the split the pages give the step: a
+ * routing rule, the shared expert and the router's input, each invoked once
+ * per layer and never from inside a kernel ("Models and backends", How a
+ * backend works).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller unless marked "host".
+ *    The library allocates no memory; all scratch lives in the caller's
+ *    workspace `ws`.  No hidden staging buffers are shared between calls (a
+ *    shared staging buffer silently corrupting an asynchronous expert group
+ *    is the failure "qwen36: CUDA VRAM expert tier", Placement, describes).
+ *  - Matrices are row-major with the reduction dimension contiguous; a weight
+ *    matrix is [N][K_in].
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    and the call returns without waiting; a device fault surfaces at the
+ *    caller's next synchronisation.
+ *  - A nonzero return means nothing was enqueued (argument errors) or a
+ *    launch failed (MOE_ERR_HIP).  moe_status_string() describes a status.
+ *  - Results are deterministic: identical inputs give identical bits on the
+ *    same GPU and build, and on the decode path a token's output does not
+ *    depend on which other tokens share the call.
+ *  - Calls that share a workspace must be ordered on one stream.
+ *
+ * Weight formats (struct moe_experts):
+ *  MOE_W_INT8_ROW  q int8 [E][N][K_in]; s float32 [E][N];  W = q * s[n].
+ *  MOE_W_INT4_B32  q uint8 [E][N][K_in/2]; s binary16 [E][N][K_in/32];
+ *                  byte j of a row holds element 2j in its low nibble and
+ *                  2j+1 in its high nibble, each stored as q + 8 with q in
+ *                  [-7, 7] (offset-binary nibbles: XOR with 8 gives the
+ *                  two's-complement value, "Every Public GGUF of This Model
+ *                  Is Missing Its Head", section 5); W = q * s[n][k/32].
+ *                  A 16-byte aligned load is exactly one 32-element block.
+ * Supported sizes: int4 hidden a multiple of 512 up to 4096 and ffn a
+ * multiple of 512 up to 2048; int8 hidden a multiple of 256 up to 2048 and
+ * ffn a multiple of 256 up to 1024; n_experts <= 1024;
+ * top_k <= min(n_experts, 64).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, inconsistent shapes */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside the supported sizes/formats */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -4          /* a HIP launch reported an error */
+} moe_status;
+
+typedef enum { MOE_W_INT8_ROW = 1, MOE_W_INT4_B32 = 2 } moe_wfmt;
+
+/* A set of SwiGLU experts: gate/up are [E][ffn][hidden], down is
+ * [E][hidden][ffn], in format `fmt`. */
+typedef struct moe_experts {
+  int32_t fmt;       /* moe_wfmt */
+  int32_t n_experts; /* E for the routed set; 1 for a shared expert; 0 = absent */
+  int32_t ffn;       /* SwiGLU width F */
+  int32_t reserved;  /* must be 0 */
+  const void *gate_q, *gate_s;
+  const void *up_q, *up_s;
+  const void *down_q, *down_s;
+} moe_experts;
+
+/* One MoE layer.  The router is float32 [E][hidden] (+ float32 [E] bias,
+ * added to the logits before selection and softmax).  renorm = 1: the k
+ * weights are a softmax over the k selected logits (softmax over all E then
+ * renormalised); renorm = 0: the full softmax's values at the selected
+ * experts. */
+typedef struct moe_layer {
+  int32_t hidden;    /* H */
+  int32_t n_experts; /* E */
+  int32_t top_k;     /* K */
+  int32_t renorm;
+  const float *router_w;    /* [E][H] */
+  const float *router_bias; /* [E] or NULL */
+  moe_experts routed;       /* n_experts == E */
+  moe_experts shared;       /* n_experts == 1, or 0 for no shared expert */
+} moe_layer;
+
+/* Residual epilogue of a layer stack (host struct).  residual_out =
+ * bf16_rne(residual_in + y); if normed_out is non-NULL it also receives
+ * bf16_rne(r / sqrt(mean_h(r^2) + eps)) of r = residual_out, the
+ * RMS-normalised input of the next layer (the pages' model normalises each
+ * layer's input, "Qwen3.6-35B-A3B: pictures, several requests at once and
+ * speed", Speed (0.1.45): add+norm in one launch).  residual_out may alias
+ * residual_in and normed_out may alias the layer's own input x. */
+typedef struct moe_residual {
+  const uint16_t *residual_in; /* bf16 [T][H], required */
+  uint16_t *residual_out;      /* bf16 [T][H], required */
+  uint16_t *normed_out;        /* bf16 [T][H] or NULL */
+  float eps;                   /* e.g. 1e-6 */
+  int32_t reserved;            /* must be 0 */
+} moe_residual;
+
+/* Bytes of workspace moe_layer_forward needs for up to max_tokens tokens
+ * (host, pure; 0 on invalid arguments). */
+size_t moe_workspace_bytes(const moe_layer *L, int32_t max_tokens);
+
+/* Prepares a workspace once before its first use (clears the control words
+ * the kernels keep zero between calls).  Enqueued on `stream`. */
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Router: logits[t][e] = sum_h Wr[e][h] * x[t][h] (+ bias[e]) in float32;
+ * topk_ids[t][k] = the K largest logits in descending order, equal logits
+ * going to the lower expert index (the pages' rule that the first of equal
+ * largest values wins, "Models and backends", What was tuned);
+ * topk_w[t][k] = routing weights per L->renorm.
+ * x_bf16 [T][H] bfloat16 bits; topk_ids int32 [T][K]; topk_w float [T][K];
+ * logits float [T][E] (required; receives the router logits). */
+int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *topk_ids, float *topk_w,
+              float *logits, void *stream);
+
+/* Workspace bytes moe_permute needs for T tokens, K slots, E experts. */
+size_t moe_permute_workspace_bytes(int32_t T, int32_t K, int32_t E);
+
+/* Token-by-expert permutation (the "grouping" that the pages move from a
+ * host thread onto the card: "Qwen3.6-35B-A3B ...", Speed (0.1.45); "Strata
+ * on an Intel Arc", Decode round 2).  Pair p = t*K + k goes to row
+ * inv_pos[t][k]; rows are grouped by expert (ascending), and within an
+ * expert ordered by p.  Outputs: counts int32 [E]; offsets int32 [E+1]
+ * (exclusive prefix sum, offsets[E] = T*K); row_tok int32 [T*K] (token of
+ * each row); row_w float [T*K] (topk_w of the pair, or 1 if topk_w is NULL);
+ * inv_pos int32 [T][K]; active int32 [E] (experts with rows, ascending,
+ * first *n_active entries valid); n_active int32 [1].  Integer results are
+ * exact and deterministic. */
+int moe_permute(const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t K, int32_t E, int32_t *counts,
+                int32_t *offsets, int32_t *row_tok, float *row_w, int32_t *inv_pos, int32_t *active,
+                int32_t *n_active, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes moe_expert_ffn needs for n_rows rows of width ffn. */
+size_t moe_expert_ffn_workspace_bytes(int32_t n_rows, int32_t ffn);
+
+/* Expert FFN over permuted rows: for each row r of expert e (offsets[e] <=
+ * r < offsets[e+1]), rows_out[r] = row_w[r] * D_e(silu(G_e x) * (U_e x))
+ * with x = x_bf16[row_tok[r]].  Every expert's weights are read once for
+ * all its rows ("Every Public GGUF of This Model Is Missing Its Head",
+ * section 3: read the expert weights once per row group instead of per
+ * token).  offsets/active/n_active as produced by moe_permute; when
+ * W->n_experts == 1 they may be NULL (all n_rows rows belong to expert 0);
+ * row_tok NULL means row r reads token r; row_w NULL means weight 1.
+ * rows_out float [n_rows][hidden]. */
+int moe_expert_ffn(const moe_experts *W, int32_t hidden, const uint16_t *x_bf16, int32_t T, int32_t n_rows,
+                   const int32_t *offsets, const int32_t *active, const int32_t *n_active, const int32_t *row_tok,
+                   const float *row_w, float *rows_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Combine ("the MoE end"): y[t][h] = sum_{k<K} rows_out[inv_pos[t][k]][h]
+ * (k in order) + shared_out[t][h]; rows with inv_pos < 0 are skipped.
+ * shared_out float [T][H] or NULL; y float [T][H]; res (host) or NULL: the
+ * residual epilogue above. */
+int moe_combine(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_t K, int32_t H,
+                const float *shared_out, float *y, const moe_residual *res, void *stream);
+
+/* The whole layer: route, permute, routed experts, shared expert, combine.
+ * y float [T][H]; res (host) or NULL: residual epilogue; topk_ids [T][K] /
+ * topk_w [T][K] or NULL (copies of the routing used).  ws: at least
+ * moe_workspace_bytes(L, T) bytes, prepared once by moe_workspace_init.
+ * T = 0 is a no-op. */
+int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
+                      int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* Profiling hook (host, process-wide): after moe_profile_events(stage,
+ * start, stop), every later moe_layer_forward records the hipEvent_t `start`
+ * on its stream just before that stage's kernels and `stop` just after
+ * them, so a caller can time a stage live (events must be created before
+ * use; each stage keeps its own pair).  Stages: 1 router + top-k,
+ * 2 permutation, 3 gate/up + SwiGLU (routed and shared experts), 4 down
+ * (routed and shared), 6 combine; 5 is reserved (the shared expert runs
+ * inside 3 and 4).  NULL events switch one stage off; stage 0 switches all
+ * off.  Not for concurrent use from several host threads. */
+enum { MOE_STAGE_NONE = 0, MOE_STAGE_ROUTE = 1, MOE_STAGE_PERMUTE = 2, MOE_STAGE_GATEUP = 3,
+       MOE_STAGE_DOWN = 4, MOE_STAGE_SHARED = 5, MOE_STAGE_COMBINE = 6 };
+int moe_profile_events(int32_t stage, void *start_event, void *stop_event);
+
+/* Static text for a status code (host). */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,388 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace carving and launch sequencing.  The library is stateless and
+// allocates nothing; every buffer is the caller's.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int check_experts(const moe_experts &W, int32_t H, bool required_routed, int32_t E) {
+  if (W.reserved != 0) return MOE_ERR_INVALID_ARG;
+  if (W.n_experts == 0) return required_routed ? MOE_ERR_INVALID_ARG : MOE_OK;
+  if (W.n_experts < 0) return MOE_ERR_INVALID_ARG;
+  if (required_routed && W.n_experts != E) return MOE_ERR_INVALID_ARG;
+  if (!required_routed && W.n_experts != 1) return MOE_ERR_INVALID_ARG;
+  if (W.fmt != MOE_W_INT8_ROW && W.fmt != MOE_W_INT4_B32) return MOE_ERR_UNSUPPORTED;
+  if (W.ffn <= 0) return MOE_ERR_INVALID_ARG;
+  const void *ptrs[6] = {W.gate_q, W.gate_s, W.up_q, W.up_s, W.down_q, W.down_s};
+  for (const void *p : ptrs)
+    if (!p) return MOE_ERR_INVALID_ARG;
+  if (!aligned(W.gate_q, 16) || !aligned(W.up_q, 16) || !aligned(W.down_q, 16)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(W.gate_s, 4) || !aligned(W.up_s, 4) || !aligned(W.down_s, 4)) return MOE_ERR_INVALID_ARG;
+  if (W.fmt == MOE_W_INT4_B32) {
+    if (H % 512 || W.ffn % 512 || H > 4096 || W.ffn > 2048) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (H % 256 || W.ffn % 256 || H > 2048 || W.ffn > 1024) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int check_layer(const moe_layer *L) {
+  if (!L) return MOE_ERR_INVALID_ARG;
+  if (L->hidden <= 0 || L->n_experts <= 0 || L->top_k <= 0) return MOE_ERR_INVALID_ARG;
+  if (L->top_k > L->n_experts) return MOE_ERR_INVALID_ARG;
+  if (L->n_experts > 1024 || L->top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (L->renorm != 0 && L->renorm != 1) return MOE_ERR_INVALID_ARG;
+  if (L->hidden % 256) return MOE_ERR_UNSUPPORTED;
+  if (!L->router_w || !aligned(L->router_w, 16)) return MOE_ERR_INVALID_ARG;
+  int rc = check_experts(L->routed, L->hidden, true, L->n_experts);
+  if (rc != MOE_OK) return rc;
+  return check_experts(L->shared, L->hidden, false, 1);
+}
+
+constexpr size_t kControlBytes = 256;  // control words kept zero between calls
+
+// profiling hook state (see moe_profile_events): one event pair per stage
+constexpr int kStages = MOE_STAGE_COMBINE + 1;
+hipEvent_t g_prof_start[kStages] = {}, g_prof_stop[kStages] = {};
+
+struct StageMark {
+  int32_t stage;
+  hipStream_t s;
+  StageMark(int32_t st, hipStream_t str) : stage(st), s(str) {
+    if (g_prof_start[stage]) (void)hipEventRecord(g_prof_start[stage], s);
+  }
+  ~StageMark() {
+    if (g_prof_stop[stage]) (void)hipEventRecord(g_prof_stop[stage], s);
+  }
+};
+
+struct LayerWs {
+  float *logits;
+  int32_t *ids;
+  float *w;
+  int32_t *counts, *offsets, *active, *n_active, *row_tok, *inv_pos, *rank, *tile_hist;
+  float *row_w;
+  float *act, *rows_out;
+  size_t bytes;
+};
+
+LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
+  Carver c{static_cast<char *>(base)};
+  c.take<char>(kControlBytes);
+  const size_t TK = static_cast<size_t>(T) * L->top_k;
+  const size_t E = L->n_experts;
+  const size_t n_tiles = (TK + kPermuteTile - 1) / kPermuteTile;
+  LayerWs w{};
+  w.logits = c.take<float>(static_cast<size_t>(T) * E);
+  w.ids = c.take<int32_t>(TK);
+  w.w = c.take<float>(TK);
+  w.counts = c.take<int32_t>(E);
+  w.offsets = c.take<int32_t>(E + 1);
+  w.active = c.take<int32_t>(E);
+  w.n_active = c.take<int32_t>(1);
+  w.row_tok = c.take<int32_t>(TK);
+  w.row_w = c.take<float>(TK);
+  w.inv_pos = c.take<int32_t>(TK);
+  w.rank = c.take<int32_t>(TK);
+  w.tile_hist = c.take<int32_t>(n_tiles * E);
+  // SwiGLU rows and expert output rows: the routed rows, then (with a shared
+  // expert) its T rows
+  const size_t Fs = L->shared.n_experts == 1 ? L->shared.ffn : 0;
+  w.act = c.take<float>(TK * L->routed.ffn + static_cast<size_t>(T) * Fs);
+  w.rows_out = c.take<float>((TK + (Fs ? T : 0)) * L->hidden);
+  w.bytes = align_up(c.off, 256);
+  return w;
+}
+
+FfnArgs ffn_args(const moe_experts &W, const moe_experts *S, int32_t H, const uint16_t *x, int32_t T,
+                 int32_t n_rows) {
+  FfnArgs a{};
+  a.fmt = W.fmt;
+  a.H = H;
+  a.F = W.ffn;
+  a.Fs = S ? S->ffn : 0;
+  a.gq = W.gate_q;
+  a.gs = W.gate_s;
+  a.uq = W.up_q;
+  a.us = W.up_s;
+  a.dq = W.down_q;
+  a.ds = W.down_s;
+  if (S) {
+    a.sgq = S->gate_q;
+    a.sgs = S->gate_s;
+    a.suq = S->up_q;
+    a.sus = S->up_s;
+    a.sdq = S->down_q;
+    a.sds = S->down_s;
+  }
+  a.x = x;
+  a.T = T;
+  a.n_rows = n_rows;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK:
+      return "ok";
+    case MOE_ERR_INVALID_ARG:
+      return "invalid argument";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported size or format";
+    case MOE_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case MOE_ERR_HIP:
+      return "HIP launch error";
+    default:
+      return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_layer *L, int32_t max_tokens) {
+  if (check_layer(L) != MOE_OK || max_tokens < 0) return 0;
+  return carve_layer(L, max_tokens, nullptr).bytes;
+}
+
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws || ws_bytes < kControlBytes || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_fill_zero(ws, kControlBytes, as_stream(stream)));
+}
+
+int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *topk_ids, float *topk_w, float *logits,
+              void *stream) {
+  int rc = check_layer(L);
+  if (rc != MOE_OK) return rc;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !topk_ids || !topk_w || !logits || !aligned(x_bf16, 16)) return MOE_ERR_INVALID_ARG;
+  RouteArgs a{L->router_w, L->router_bias, x_bf16, T, L->hidden, L->n_experts, L->top_k, L->renorm, logits,
+              topk_ids, topk_w};
+  hipError_t e = launch_router_logits(a, as_stream(stream));
+  if (e == hipSuccess) e = launch_topk(a, as_stream(stream));
+  return hip_status(e);
+}
+
+size_t moe_permute_workspace_bytes(int32_t T, int32_t K, int32_t E) {
+  if (T < 0 || K <= 0 || E <= 0) return 0;
+  const size_t TK = static_cast<size_t>(T) * K;
+  const size_t n_tiles = (TK + kPermuteTile - 1) / kPermuteTile;
+  Carver c{nullptr};
+  c.take<int32_t>(TK);
+  c.take<int32_t>(n_tiles * E);
+  return align_up(c.off, 256);
+}
+
+int moe_permute(const int32_t *topk_ids, const float *topk_w, int32_t T, int32_t K, int32_t E, int32_t *counts,
+                int32_t *offsets, int32_t *row_tok, float *row_w, int32_t *inv_pos, int32_t *active,
+                int32_t *n_active, void *ws, size_t ws_bytes, void *stream) {
+  if (T < 0 || K <= 0 || E <= 0 || K > E) return MOE_ERR_INVALID_ARG;
+  if (E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(T) * K > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets || !active || !n_active) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !row_tok || !row_w || !inv_pos)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_permute_workspace_bytes(T, K, E);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  Carver c{static_cast<char *>(ws)};
+  const size_t TK = static_cast<size_t>(T) * K;
+  PermuteArgs a{};
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.T = T;
+  a.K = K;
+  a.E = E;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.row_tok = row_tok;
+  a.row_w = row_w;
+  a.inv_pos = inv_pos;
+  a.active = active;
+  a.n_active = n_active;
+  a.rank = c.take<int32_t>(TK);
+  a.tile_hist = c.take<int32_t>((TK + kPermuteTile - 1) / kPermuteTile * E);
+  if (T == 0) {
+    // No pairs: zero counts/offsets/n_active through the scatter kernel's
+    // tile-0 path is unavailable (no tiles), so clear them directly.
+    hipError_t e = launch_fill_zero(counts, static_cast<size_t>(E) * 4, as_stream(stream));
+    if (e == hipSuccess) e = launch_fill_zero(offsets, static_cast<size_t>(E + 1) * 4, as_stream(stream));
+    if (e == hipSuccess) e = launch_fill_zero(n_active, 4, as_stream(stream));
+    return hip_status(e);
+  }
+  return hip_status(launch_permute(a, as_stream(stream)));
+}
+
+size_t moe_expert_ffn_workspace_bytes(int32_t n_rows, int32_t ffn) {
+  if (n_rows < 0 || ffn <= 0) return 0;
+  return align_up(static_cast<size_t>(n_rows) * ffn * sizeof(float), 256);
+}
+
+int moe_expert_ffn(const moe_experts *W, int32_t hidden, const uint16_t *x_bf16, int32_t T, int32_t n_rows,
+                   const int32_t *offsets, const int32_t *active, const int32_t *n_active, const int32_t *row_tok,
+                   const float *row_w, float *rows_out, void *ws, size_t ws_bytes, void *stream) {
+  if (!W || hidden <= 0 || T < 0 || n_rows < 0) return MOE_ERR_INVALID_ARG;
+  int rc = check_experts(*W, hidden, W->n_experts != 1, W->n_experts);
+  if (rc != MOE_OK) return rc;
+  if (W->n_experts == 0) return MOE_ERR_INVALID_ARG;
+  if (W->n_experts > 1 && (!offsets || !active || !n_active)) return MOE_ERR_INVALID_ARG;
+  if (!row_tok && n_rows > T) return MOE_ERR_INVALID_ARG;
+  if (n_rows == 0) return MOE_OK;
+  if (!x_bf16 || !rows_out || !aligned(x_bf16, 16) || !aligned(rows_out, 16)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe_expert_ffn_workspace_bytes(n_rows, W->ffn)) return MOE_ERR_WORKSPACE;
+  FfnArgs a = ffn_args(*W, nullptr, hidden, x_bf16, T, n_rows);
+  a.offsets = offsets;
+  a.active = offsets ? active : nullptr;
+  a.n_active = offsets ? n_active : nullptr;
+  a.row_tok = row_tok;
+  a.row_w = row_w;
+  a.act = static_cast<float *>(ws);
+  a.rows_out = rows_out;
+  a.max_units = offsets ? (n_rows < W->n_experts ? n_rows : W->n_experts) : 1;
+  hipError_t e = launch_gateup(a, as_stream(stream));
+  if (e == hipSuccess) e = launch_down(a, as_stream(stream));
+  return hip_status(e);
+}
+
+namespace {
+int check_residual(const moe_residual *res, int32_t H) {
+  if (!res) return MOE_OK;
+  if (res->reserved != 0 || !res->residual_in || !res->residual_out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(res->residual_in, 8) || !aligned(res->residual_out, 8) ||
+      (res->normed_out && !aligned(res->normed_out, 8)))
+    return MOE_ERR_INVALID_ARG;
+  if (!(res->eps >= 0.f)) return MOE_ERR_INVALID_ARG;
+  (void)H;
+  return MOE_OK;
+}
+
+CombineArgs combine_args(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_t K, int32_t H,
+                         const float *shared_out, float *y, const moe_residual *res) {
+  CombineArgs a{rows_out, inv_pos, T, K, H, shared_out, y, nullptr, nullptr, nullptr, 0.f};
+  if (res) {
+    a.residual_in = res->residual_in;
+    a.residual_out = res->residual_out;
+    a.normed_out = res->normed_out;
+    a.eps = res->eps;
+  }
+  return a;
+}
+}  // namespace
+
+int moe_combine(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_t K, int32_t H,
+                const float *shared_out, float *y, const moe_residual *res, void *stream) {
+  if (T < 0 || K <= 0 || H <= 0 || H % 256 || H > 8192) return MOE_ERR_INVALID_ARG;
+  if (K > 64) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!rows_out || !inv_pos || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(rows_out, 16) || !aligned(y, 16) || (shared_out && !aligned(shared_out, 16)))
+    return MOE_ERR_INVALID_ARG;
+  int rc = check_residual(res, H);
+  if (rc != MOE_OK) return rc;
+  return hip_status(launch_combine(combine_args(rows_out, inv_pos, T, K, H, shared_out, y, res), as_stream(stream)));
+}
+
+int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
+                      int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_layer(L);
+  if (rc != MOE_OK) return rc;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (static_cast<int64_t>(T) * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (!x_bf16 || !y || !aligned(x_bf16, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  rc = check_residual(res, L->hidden);
+  if (rc != MOE_OK) return rc;
+  if (!ws || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  LayerWs w = carve_layer(L, T, ws);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  const int32_t K = L->top_k, E = L->n_experts, H = L->hidden;
+  int32_t *ids = topk_ids ? topk_ids : w.ids;
+  float *tw = topk_w ? topk_w : w.w;
+
+  RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw};
+  hipError_t e;
+  {
+    StageMark m(MOE_STAGE_ROUTE, s);
+    e = launch_router_logits(ra, s);
+    if (e == hipSuccess) e = launch_topk(ra, s);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  PermuteArgs pa{};
+  pa.ids = ids;
+  pa.w = tw;
+  pa.T = T;
+  pa.K = K;
+  pa.E = E;
+  pa.counts = w.counts;
+  pa.offsets = w.offsets;
+  pa.row_tok = w.row_tok;
+  pa.row_w = w.row_w;
+  pa.inv_pos = w.inv_pos;
+  pa.active = w.active;
+  pa.n_active = w.n_active;
+  pa.rank = w.rank;
+  pa.tile_hist = w.tile_hist;
+  {
+    StageMark m(MOE_STAGE_PERMUTE, s);
+    e = launch_permute(pa, s);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  const int32_t TK = T * K;
+  const bool has_shared = L->shared.n_experts == 1;
+  FfnArgs xa = ffn_args(L->routed, has_shared ? &L->shared : nullptr, H, x_bf16, T, TK);
+  xa.offsets = w.offsets;
+  xa.active = w.active;
+  xa.n_active = w.n_active;
+  xa.row_tok = w.row_tok;
+  xa.row_w = w.row_w;
+  xa.act = w.act;
+  xa.rows_out = w.rows_out;
+  xa.max_units = TK < E ? TK : E;
+  {
+    StageMark m(MOE_STAGE_GATEUP, s);
+    e = launch_gateup(xa, s);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  {
+    StageMark m(MOE_STAGE_DOWN, s);
+    e = launch_down(xa, s);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  CombineArgs ca = combine_args(w.rows_out, w.inv_pos, T, K, H,
+                                has_shared ? w.rows_out + static_cast<size_t>(TK) * H : nullptr, y, res);
+  StageMark m(MOE_STAGE_COMBINE, s);
+  return hip_status(launch_combine(ca, s));
+}
+
+int moe_profile_events(int32_t stage, void *start_event, void *stop_event) {
+  if (stage < MOE_STAGE_NONE || stage > MOE_STAGE_COMBINE) return MOE_ERR_INVALID_ARG;
+  if (stage == MOE_STAGE_NONE) {
+    for (int i = 0; i < kStages; ++i) g_prof_start[i] = g_prof_stop[i] = nullptr;
+    return MOE_OK;
+  }
+  if (!start_event || !stop_event) {
+    g_prof_start[stage] = g_prof_stop[stage] = nullptr;
+    return MOE_OK;
+  }
+  g_prof_start[stage] = static_cast<hipEvent_t>(start_event);
+  g_prof_stop[stage] = static_cast<hipEvent_t>(stop_event);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Combine ("the MoE end"): y[t] = sum over k of the routed rows of token t,
+// in slot order, plus the shared expert's row; optionally the residual
+// epilogue of a layer stack, r' = bf16(r + y) and the RMS-normalised
+// bf16(r' / sqrt(mean(r'^2) + eps)) that feeds the next layer.  One launch
+// sums every expert of the call ("Models and backends", What was tuned); a
+// fixed summation order keeps the bits independent of scheduling.  One
+// 256-thread block owns one token row, so the row's sum of squares is a
+// block reduction in a fixed order.
+#include <math.h>
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kCombineChunks = 8;  // float4 chunks per thread: H <= 8192
+
+MOE_DEV void add4(float4 &a, const float4 &b) {
+  a.x += b.x;
+  a.y += b.y;
+  a.z += b.z;
+  a.w += b.w;
+}
+
+__global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
+  __shared__ float wave_sq[4];
+  __shared__ int rows[64];  // this token's K row indices (K <= 64)
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n4 = a.H / 4;
+  if (tid < a.K) rows[tid] = a.inv_pos[static_cast<size_t>(t) * a.K + tid];
+  __syncthreads();
+  float4 r[kCombineChunks];
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCombineChunks; ++i) {
+    const int c = tid + 256 * i;
+    if (c >= n4) break;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int k = 0;
+    // groups of four independent row loads, summed in slot order
+    for (; k + 4 <= a.K; k += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = rows[k + m];
+        v[m] = row >= 0 ? reinterpret_cast<const float4 *>(a.rows_out + static_cast<size_t>(row) * a.H)[c]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) add4(acc, v[m]);
+    }
+    for (; k < a.K; ++k) {
+      const int row = rows[k];
+      if (row >= 0) add4(acc, reinterpret_cast<const float4 *>(a.rows_out + static_cast<size_t>(row) * a.H)[c]);
+    }
+    const size_t o4 = static_cast<size_t>(t) * n4 + c;
+    if (a.shared_out) add4(acc, reinterpret_cast<const float4 *>(a.shared_out)[o4]);
+    reinterpret_cast<float4 *>(a.y)[o4] = acc;
+    if (a.residual_out) {
+      const uint2 xv = reinterpret_cast<const uint2 *>(a.residual_in)[o4];
+      const uint16_t b0 = f32_to_bf16_rne(bf16_lo(xv.x) + acc.x);
+      const uint16_t b1 = f32_to_bf16_rne(bf16_hi(xv.x) + acc.y);
+      const uint16_t b2 = f32_to_bf16_rne(bf16_lo(xv.y) + acc.z);
+      const uint16_t b3 = f32_to_bf16_rne(bf16_hi(xv.y) + acc.w);
+      reinterpret_cast<uint2 *>(a.residual_out)[o4] =
+          make_uint2(static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16),
+                     static_cast<uint32_t>(b2) | (static_cast<uint32_t>(b3) << 16));
+      r[i] = make_float4(bf16_to_f32(b0), bf16_to_f32(b1), bf16_to_f32(b2), bf16_to_f32(b3));
+      sq = fmaf(r[i].x, r[i].x, sq);
+      sq = fmaf(r[i].y, r[i].y, sq);
+      sq = fmaf(r[i].z, r[i].z, sq);
+      sq = fmaf(r[i].w, r[i].w, sq);
+    }
+  }
+  if (!a.normed_out) return;
+  sq = sum64(sq);
+  if ((tid & 63) == 0) wave_sq[tid >> 6] = sq;
+  __syncthreads();
+  const float total = ((wave_sq[0] + wave_sq[1]) + wave_sq[2]) + wave_sq[3];
+  const float inv_rms = 1.f / sqrtf(total / static_cast<float>(a.H) + a.eps);
+#pragma unroll
+  for (int i = 0; i < kCombineChunks; ++i) {
+    const int c = tid + 256 * i;
+    if (c >= n4) break;
+    const size_t o4 = static_cast<size_t>(t) * n4 + c;
+    const uint16_t b0 = f32_to_bf16_rne(r[i].x * inv_rms);
+    const uint16_t b1 = f32_to_bf16_rne(r[i].y * inv_rms);
+    const uint16_t b2 = f32_to_bf16_rne(r[i].z * inv_rms);
+    const uint16_t b3 = f32_to_bf16_rne(r[i].w * inv_rms);
+    reinterpret_cast<uint2 *>(a.normed_out)[o4] =
+        make_uint2(static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16),
+                   static_cast<uint32_t>(b2) | (static_cast<uint32_t>(b3) << 16));
+  }
+}
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  combine_kernel<<<a.T, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(uint32_t *p, size_t n) {
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256) p[i] = 0u;
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(n / 256 + 1 < 1024 ? n / 256 + 1 : 1024);
+  fill_zero_kernel<<<blocks, 256, 0, s>>>(static_cast<uint32_t *>(p), n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,143 @@
+// Device helpers shared by the HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#define MOE_DEV __device__ __forceinline__
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kStageBatch = 8;  // independent loads a thread issues before it stores them
+
+// ---- bit-level conversions --------------------------------------------------
+
+MOE_DEV float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+MOE_DEV float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// float32 -> bfloat16, round to nearest even (NaN kept quiet).
+MOE_DEV uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((b >> 16) | 0x40u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return static_cast<uint16_t>(b >> 16);
+}
+
+MOE_DEV float f16_bits_to_f32(uint16_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, h)); }
+
+// ---- DPP reductions ----------------------------------------------------------
+// DPP controls (GFX9 encoding): quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140.
+
+template <int CTRL>
+MOE_DEV float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of 16 lanes; every lane of the group gets it.
+MOE_DEV float sum16(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return v;
+}
+
+// Sum over the wave in a fixed order ((row0 + row1) + (row2 + row3)); the
+// result is uniform.
+MOE_DEV float sum64(float v) {
+  v = sum16(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+MOE_DEV int lane_id() { return __lane_id(); }
+
+// ---- workspace carving -------------------------------------------------------
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Carver {
+  char *base;
+  size_t off = 0;
+  template <typename T>
+  T *take(size_t count) {
+    off = align_up(off, 256);
+    T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+// ---- launch helpers declared by each translation unit -----------------------
+
+struct RouteArgs {
+  const float *router_w;
+  const float *router_bias;
+  const uint16_t *x;
+  int32_t T, H, E, K, renorm;
+  float *logits;
+  int32_t *ids;
+  float *w;
+};
+hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s);
+hipError_t launch_topk(const RouteArgs &a, hipStream_t s);
+
+struct PermuteArgs {
+  const int32_t *ids;
+  const float *w;
+  int32_t T, K, E;
+  int32_t *counts, *offsets, *row_tok, *inv_pos, *active, *n_active;
+  float *row_w;
+  int32_t *tile_hist; // [n_tiles][E]
+  int32_t *rank;      // [T*K]
+};
+constexpr int kPermuteTile = 1024;
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
+
+// Expert FFN over permuted rows (the GEMV path).  The routed units are the
+// active experts (offsets != NULL) or a single expert 0 owning rows
+// [0, n_rows) (offsets == NULL); when Fs > 0 the shared expert is one more
+// unit whose rows t = 0..T-1 follow the routed rows in act and rows_out.
+struct FfnArgs {
+  int32_t fmt, H, F, Fs;
+  const void *gq, *gs, *uq, *us, *dq, *ds;        // routed [E][..]
+  const void *sgq, *sgs, *suq, *sus, *sdq, *sds;  // shared [1][..]
+  const uint16_t *x;
+  int32_t T;
+  int32_t n_rows;           // routed rows
+  const int32_t *offsets;   // [E+1] or NULL
+  const int32_t *active;    // [E]
+  const int32_t *n_active;  // [1]
+  const int32_t *row_tok;   // NULL: row r reads token r
+  const float *row_w;       // NULL: weight 1
+  float *act;               // [n_rows*F + T*Fs]
+  float *rows_out;          // [n_rows + (Fs ? T : 0)][H]
+  int32_t max_units;        // upper bound of routed units (grid sizing)
+};
+hipError_t launch_gateup(const FfnArgs &a, hipStream_t s);
+hipError_t launch_down(const FfnArgs &a, hipStream_t s);
+
+struct CombineArgs {
+  const float *rows_out;
+  const int32_t *inv_pos;
+  int32_t T, K, H;
+  const float *shared_out;      // [T][H] or NULL
+  float *y;
+  const uint16_t *residual_in;  // with residual_out
+  uint16_t *residual_out;       // NULL: no residual epilogue
+  uint16_t *normed_out;         // NULL: no normalised copy
+  float eps;
+};
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace moe

@@ -78,6 +78,8 @@ def lib():
         L.oracle_expert_rows.restype = ctypes.c_int
         L.oracle_residual.argtypes = [vp, vp, i64, vp]
         L.oracle_residual.restype = None
+        L.oracle_rmsnorm.argtypes = [vp, i64, i64, f64, vp]
+        L.oracle_rmsnorm.restype = None
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = i32
         _lib = L
@@ -105,7 +107,7 @@ def _layer_struct(layer, keep):
     if layer.router_bias is not None:
         b = np.ascontiguousarray(layer.router_bias, np.float32)
         keep.append(b)
-    routed = _experts_struct(layer.routed, keep)
+    routed = _experts_struct(layer.routed, keep) if layer.routed is not None else _Experts()
     sh = None
     if layer.shared is not None:
         s = _experts_struct(layer.shared, keep)
@@ -228,6 +230,14 @@ def residual(x_bf16, y):
     y = np.ascontiguousarray(y, np.float64)
     out = np.empty(x.shape, np.uint16)
     lib().oracle_residual(_p(x), _p(y), x.size, _p(out))
+    return out
+
+
+def rmsnorm(r_bf16, eps=1e-6):
+    r = np.ascontiguousarray(r_bf16, np.uint16)
+    T, H = r.shape
+    out = np.empty_like(r)
+    lib().oracle_rmsnorm(_p(r), T, H, eps, _p(out))
     return out
 
 

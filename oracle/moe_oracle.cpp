@@ -332,4 +332,19 @@ void oracle_residual(const uint16_t *x_bf16, const double *y, int64_t n, uint16_
   for (int64_t i = 0; i < n; ++i) x_next[i] = bf16_round(bf16_value(x_bf16[i]) + y[i]);
 }
 
+// RMS normalisation of a layer stack's residual (no learned gain): the
+// pages' model normalises each layer's input ("Qwen3.6-35B-A3B: pictures,
+// several requests at once and speed", Speed (0.1.45)).
+void oracle_rmsnorm(const uint16_t *r_bf16, int64_t T, int64_t H, double eps, uint16_t *out) {
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      const double v = bf16_value(r_bf16[t * H + h]);
+      ss += v * v;
+    }
+    const double scale = 1.0 / std::sqrt(ss / static_cast<double>(H) + eps);
+    for (int64_t h = 0; h < H; ++h) out[t * H + h] = bf16_round(bf16_value(r_bf16[t * H + h]) * scale);
+  }
+}
+
 }  // extern "C"

@@ -84,6 +84,8 @@ int oracle_expert_rows(const oracle_experts *W, const uint16_t *x_bf16, const in
                        int32_t nthreads);
 /* x_next = bf16_rne(x + y) elementwise. */
 void oracle_residual(const uint16_t *x_bf16, const double *y, int64_t n, uint16_t *x_next);
+/* out[t] = bf16(r[t] / sqrt(mean_h r[t][h]^2 + eps)) per row of H values. */
+void oracle_rmsnorm(const uint16_t *r_bf16, int64_t T, int64_t H, double eps, uint16_t *out);
 int32_t oracle_threads(void);
 
 #ifdef __cplusplus

@@ -1,0 +1,112 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def mb():
+    from mixture_experts_decode_moe_amd import binding
+    return binding
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+                     "moe_workspace_bytes", "moe_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(mb):
+    lib = ctypes.CDLL(mb.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in moe.h but not exported"
+    assert set(declared_functions()) <= set(mb.EXPORTED) | {"moe_workspace_init"}
+
+
+def test_status_strings(mb):
+    assert mb.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert mb.status_string(s) not in ("ok", "unknown status")
+    assert mb.status_string(7) == "unknown status"
+
+
+def _fake_layer(mb, H=2048, E=256, K=8, F=512, fmt=2, shared=True):
+    p = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced by the host-only calls
+    ex = mb.MoeExperts(fmt, E, F, 0, p, p, p, p, p, p)
+    sh = mb.MoeExperts(fmt, 1, F, 0, p, p, p, p, p, p) if shared else mb.MoeExperts()
+    return mb.MoeLayer(H, E, K, 1, p, None, ex, sh)
+
+
+def test_workspace_bytes_is_pure_and_grows(mb):
+    lib = mb.raw_lib()
+    L = _fake_layer(mb)
+    a = lib.moe_workspace_bytes(ctypes.byref(L), 1)
+    b = lib.moe_workspace_bytes(ctypes.byref(L), 16)
+    c = lib.moe_workspace_bytes(ctypes.byref(L), 2048)
+    assert 0 < a < b < c and c % 256 == 0
+    assert lib.moe_workspace_bytes(ctypes.byref(L), -1) == 0
+    assert lib.moe_permute_workspace_bytes(2048, 8, 256) >= 2048 * 8 * 4
+    assert lib.moe_expert_ffn_workspace_bytes(10, 512) >= 10 * 512 * 4
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda L: setattr(L, "top_k", 0), -1),
+    (lambda L: setattr(L, "top_k", 300), -1),
+    (lambda L: setattr(L, "renorm", 2), -1),
+    (lambda L: setattr(L, "n_experts", 2048), -2),
+    (lambda L: setattr(L, "hidden", 1000), -2),
+    (lambda L: setattr(L.routed, "fmt", 9), -2),
+    (lambda L: setattr(L.routed, "n_experts", 7), -1),
+    (lambda L: setattr(L.routed, "ffn", 500), -2),
+    (lambda L: setattr(L.routed, "gate_q", None), -1),
+    (lambda L: setattr(L.routed, "reserved", 1), -1),
+    (lambda L: setattr(L.shared, "n_experts", 2), -1),
+    (lambda L: setattr(L, "router_w", None), -1),
+])
+def test_layer_validation_rejects_before_launch(mb, mutate, expect):
+    lib = mb.raw_lib()
+    L = _fake_layer(mb)
+    mutate(L)
+    p = ctypes.c_void_p(1 << 20)
+    rc = lib.moe_layer_forward(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, None)
+    assert rc == expect
+    assert lib.moe_workspace_bytes(ctypes.byref(L), 4) == 0
+
+
+def test_other_entry_points_reject_bad_arguments(mb):
+    lib = mb.raw_lib()
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.moe_layer_forward(None, p, 4, p, None, None, None, p, 1 << 30, None) == -1
+    L = _fake_layer(mb)
+    assert lib.moe_layer_forward(ctypes.byref(L), p, -1, p, None, None, None, p, 1 << 30, None) == -1
+    assert lib.moe_layer_forward(ctypes.byref(L), p, 0, p, None, None, None, p, 1 << 30, None) == 0
+    assert lib.moe_layer_forward(ctypes.byref(L), p, 4, p, None, None, None, None, 0, None) == -3
+    assert lib.moe_layer_forward(ctypes.byref(L), p, 4, p, None, None, None, p, 16, None) == -3
+    assert lib.moe_layer_forward(ctypes.byref(L), ctypes.c_void_p((1 << 20) + 2), 4, p, None, None, None, p,
+                                 1 << 30, None) == -1
+    assert lib.moe_route(ctypes.byref(L), p, 4, None, p, p, None) == -1
+    assert lib.moe_permute(p, p, 4, 9, 8, p, p, p, p, p, p, p, p, 1 << 20, None) == -1  # K > E
+    assert lib.moe_permute(p, p, 4, 2, 4096, p, p, p, p, p, p, p, p, 1 << 20, None) == -2
+    assert lib.moe_permute(p, p, 4, 2, 8, p, p, p, p, p, p, p, None, 0, None) == -3
+    ex = mb.MoeExperts(2, 256, 512, 0, p, p, p, p, p, p)
+    assert lib.moe_expert_ffn(ctypes.byref(ex), 2048, p, 4, 32, None, None, None, p, p, p, p, 1 << 30,
+                              None) == -1  # routed set without offsets
+    assert lib.moe_combine(p, p, 4, 8, 2046, None, p, None, None) == -1
+    bad = mb.MoeResidual(None, 1 << 20, None, 1e-6, 0)  # residual_out without residual_in
+    assert lib.moe_combine(p, p, 4, 8, 2048, None, p, ctypes.byref(bad), None) == -1
+    assert lib.moe_layer_forward(ctypes.byref(_fake_layer(mb)), p, 4, p, ctypes.byref(bad), None, None, p,
+                                 1 << 30, None) == -1
+    assert lib.moe_workspace_init(None, 0, None) == -3

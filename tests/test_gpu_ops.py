@@ -1,0 +1,138 @@
+"""GPU parity of the separate ABI steps: moe_route, moe_permute,
+moe_expert_ffn and moe_combine, each against the oracle (integers bit-exact,
+floating point within the layer's tolerances)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from mixture_experts_decode_moe_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mb():
+    from mixture_experts_decode_moe_amd import binding
+    return binding
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_route(mb, cfg):
+    """moe_route alone.  It reads only the router, so the expert pointers of
+    the layer descriptor are small placeholders."""
+    import torch
+    import parity_util as pu
+    shape = synth.CONFIGS[cfg]
+    say(f"route cfg{cfg}")
+    seed = synth.layer_seed(shape, 0)
+    E, H, K = shape.n_experts, shape.hidden, shape.top_k
+    wr = synth.normal_f32(seed, synth.S_ROUTER_W, E * H, 0.0, 0.02).reshape(E, H)
+    bias = synth.make_router_bias(shape, seed)
+    x = synth.make_x(shape)
+    T = x.shape[0]
+    dummy = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    routed = mb.Experts(shape.fmt, E, shape.ffn, dummy, dummy, dummy, dummy, dummy, dummy)
+    dl = mb.Layer(H, E, K, shape.renorm, torch.from_numpy(wr).cuda(),
+                  None if bias is None else torch.from_numpy(bias).cuda(), routed, None)
+    ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    mb.route(dl, pu.dev_u16(x), ids, w, lg)
+    torch.cuda.synchronize()
+    host = synth.LayerHost(H, E, K, shape.renorm, wr, bias, None)
+    ref = oracle.router_logits(host, x)
+    lg_h = lg.cpu().numpy().astype(np.float64)
+    # float32 accumulation over H terms: |err| <= H * 2^-24 * sum|w x| (+ bias rounding)
+    xf = pu.bf16_to_f64(x)
+    bound = H * 2.0 ** -24 * (xf.__abs__() @ np.abs(wr.astype(np.float64)).T) + 1e-6
+    assert np.all(np.abs(lg_h - ref) <= bound)
+    ids_ref, w_ref = oracle.select(ref, K, shape.renorm)
+    ids_h, w_h = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    tie = pu.check_selection(ids_h, ids_ref, ref, K)
+    ok = ~tie
+    same = np.all(ids_h == ids_ref, axis=1) & ok
+    assert np.all(np.abs(w_h[same] - w_ref[same]) <= pu.W_TOL)
+    assert np.all(np.abs(w_h.sum(axis=1) - 1.0) <= 1e-6)
+    say(f"route cfg{cfg}: near ties {int(tie.sum())} of {T}")
+
+
+@pytest.mark.parametrize("T,K,E,mode", [(1, 8, 256, "rand"), (16, 8, 256, "rand"), (2048, 8, 256, "rand"),
+                                        (700, 4, 64, "rand"), (300, 8, 256, "one"), (5, 2, 1024, "rand"),
+                                        (3000, 1, 16, "skew")])
+def test_permute_exact(mb, T, K, E, mode):
+    import torch
+    say(f"permute T={T} K={K} E={E} {mode}")
+    rng = np.random.default_rng(T * 7 + K)
+    if mode == "one":
+        ids = np.stack([np.r_[[3], rng.choice(np.setdiff1d(np.arange(E), [3]), K - 1, replace=False)]
+                        for _ in range(T)]).astype(np.int32)
+    elif mode == "skew":
+        ids = rng.choice(4, size=(T, K)).astype(np.int32)
+    else:
+        ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(size=(T, K)).astype(np.float32)
+    ref = oracle.permute(ids, w, E)
+    TK = T * K
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+               row_tok=torch.empty(TK, dtype=torch.int32, device="cuda"),
+               row_w=torch.empty(TK, dtype=torch.float32, device="cuda"),
+               inv_pos=torch.empty((T, K), dtype=torch.int32, device="cuda"),
+               active=torch.full((E,), -1, dtype=torch.int32, device="cuda"),
+               n_active=torch.empty(1, dtype=torch.int32, device="cuda"))
+    ws = torch.empty(mb.permute_workspace_bytes(T, K, E), dtype=torch.uint8, device="cuda")
+    mb.permute(torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), E, out, ws)
+    torch.cuda.synchronize()
+    for k in ("counts", "offsets", "row_tok", "row_w", "inv_pos"):
+        assert np.array_equal(out[k].cpu().numpy(), ref[k]), k
+    na = int(out["n_active"].cpu().numpy()[0])
+    assert na == ref["n_active"]
+    assert np.array_equal(out["active"].cpu().numpy()[:na], ref["active"])
+
+
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_expert_ffn_and_combine(mb, cfg):
+    """moe_expert_ffn on the oracle's permutation, then moe_combine, each
+    compared with the oracle's rows and layer output."""
+    import torch
+    import parity_util as pu
+    shape = synth.CONFIGS[cfg]
+    say(f"expert_ffn+combine cfg{cfg}")
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    T, K, E, H = x.shape[0], shape.top_k, shape.n_experts, shape.hidden
+    y_ref, ids, w, _ = oracle.layer_forward(layer, x)
+    p = oracle.permute(ids, w.astype(np.float32), E)
+    rows_ref = oracle.expert_rows(layer.routed, x, p["offsets"], p["row_tok"], p["row_w"])
+    dl = mb.layer_to_device(layer)
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    TK = T * K
+    rows = torch.empty((TK, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(mb.expert_ffn_workspace_bytes(TK, shape.ffn), dtype=torch.uint8, device="cuda")
+    xd = pu.dev_u16(x)
+    mb.expert_ffn(dl.routed, H, xd, TK, cu(p["offsets"]), cu(p["active"]), cu(np.array([p["n_active"]], np.int32)),
+                  cu(p["row_tok"]), cu(p["row_w"]), rows, ws)
+    shared = None
+    if dl.shared is not None:
+        shared = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        ws2 = torch.empty(mb.expert_ffn_workspace_bytes(T, shape.shared_ffn), dtype=torch.uint8, device="cuda")
+        mb.expert_ffn(dl.shared, H, xd, T, None, None, None, None, None, shared, ws2)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    r_out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    normed = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    mb.combine(rows, cu(p["inv_pos"]), T, K, H, shared, y, mb.residual(xd, r_out, normed))
+    torch.cuda.synchronize()
+    rows_h = rows.cpu().numpy().astype(np.float64)
+    assert pu.rel_max_err(rows_h, rows_ref) <= pu.Y_REL
+    assert pu.rel_max_err(y.cpu().numpy().astype(np.float64), y_ref) <= pu.Y_REL
+    r_ref = oracle.residual(x, y.cpu().numpy().astype(np.float64))
+    assert np.abs(r_ref.astype(np.int32) - pu.host_u16(r_out).astype(np.int32)).max() <= 1
+    n_ref = oracle.rmsnorm(pu.host_u16(r_out))
+    assert np.abs(n_ref.astype(np.int32) - pu.host_u16(normed).astype(np.int32)).max() <= 1

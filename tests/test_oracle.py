@@ -382,3 +382,20 @@ def test_residual_rounds_to_nearest_even():
     # -3 + 2^-7 sits halfway between -3 + 2^-6 (odd) and -3 (even); 1e-40 is
     # about 1.09 subnormal bf16 steps (2^-133)
     assert list(out) == [0x3F80, 0x3F82, 0xC040, 0x0001]
+
+
+def test_rmsnorm_closed_forms():
+    # a constant row c normalises to c / sqrt(c^2 + eps); alternating +-v to +-v / sqrt(v^2 + eps)
+    H = 64
+    r = np.zeros((3, H), np.uint16)
+    r[0] = synth.f64_to_bf16(np.full(H, 3.0))
+    r[1] = synth.f64_to_bf16(np.tile([2.0, -2.0], H // 2))
+    r[2] = synth.f64_to_bf16(np.r_[np.full(H // 2, 1.0), np.full(H // 2, 7.0)])  # mean square 25
+    out = oracle.rmsnorm(r, eps=0.0)
+    f = bf16_bits_to_f64(out)
+    assert np.all(f[0] == 1.0)
+    assert np.all(f[1] == np.tile([1.0, -1.0], H // 2))
+    assert np.all(f[2] == np.r_[np.full(H // 2, 0.2), np.full(H // 2, 1.4)].astype(np.float32).astype(
+        np.float64)) or np.allclose(f[2], np.r_[np.full(H // 2, 0.2), np.full(H // 2, 1.4)], rtol=2 ** -8)
+    out_eps = oracle.rmsnorm(r[:1], eps=7.0)  # 3 / sqrt(9 + 7) = 0.75 exactly
+    assert np.all(bf16_bits_to_f64(out_eps) == 0.75)
