@@ -68,6 +68,8 @@ struct StageMark {
 };
 
 struct LayerWs {
+  uint32_t *control;  // kControlBytes of words kept zero between calls; [0]: routing counter
+  float *part;        // fused routing: partial logits [S][T][E]
   float *logits;
   int32_t *ids;
   float *w;
@@ -79,11 +81,14 @@ struct LayerWs {
 
 LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
   Carver c{static_cast<char *>(base)};
-  c.take<char>(kControlBytes);
+  LayerWs w{};
+  w.control = c.take<uint32_t>(kControlBytes / 4);
   const size_t TK = static_cast<size_t>(T) * L->top_k;
   const size_t E = L->n_experts;
   const size_t n_tiles = (TK + kPermuteTile - 1) / kPermuteTile;
-  LayerWs w{};
+  const size_t S = static_cast<size_t>(L->hidden / route_fused_slice(L->hidden));
+  // sized for min(T, kFusedTokens) tokens so that the total grows with T
+  w.part = c.take<float>(S * static_cast<size_t>(T < kFusedTokens ? T : kFusedTokens) * E);
   w.logits = c.take<float>(static_cast<size_t>(T) * E);
   w.ids = c.take<int32_t>(TK);
   w.w = c.take<float>(TK);
@@ -312,31 +317,56 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
   int32_t *ids = topk_ids ? topk_ids : w.ids;
   float *tw = topk_w ? topk_w : w.w;
 
-  RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw};
   hipError_t e;
-  {
+  if (T <= kFusedTokens) {
+    // decode batch: router partials, then top-k and permutation in one block
+    RouteFusedArgs fa{};
+    fa.router_w = L->router_w;
+    fa.router_bias = L->router_bias;
+    fa.x = x_bf16;
+    fa.T = T;
+    fa.H = H;
+    fa.E = E;
+    fa.K = K;
+    fa.renorm = L->renorm;
+    fa.Hs = route_fused_slice(H);
+    fa.S = H / fa.Hs;
+    fa.logits = nullptr;
+    fa.ids = ids;
+    fa.w = tw;
+    fa.part = w.part;
+    fa.counts = w.counts;
+    fa.offsets = w.offsets;
+    fa.row_tok = w.row_tok;
+    fa.inv_pos = w.inv_pos;
+    fa.active = w.active;
+    fa.n_active = w.n_active;
+    fa.row_w = w.row_w;
     StageMark m(MOE_STAGE_ROUTE, s);
-    e = launch_router_logits(ra, s);
-    if (e == hipSuccess) e = launch_topk(ra, s);
-  }
-  if (e != hipSuccess) return MOE_ERR_HIP;
-
-  PermuteArgs pa{};
-  pa.ids = ids;
-  pa.w = tw;
-  pa.T = T;
-  pa.K = K;
-  pa.E = E;
-  pa.counts = w.counts;
-  pa.offsets = w.offsets;
-  pa.row_tok = w.row_tok;
-  pa.row_w = w.row_w;
-  pa.inv_pos = w.inv_pos;
-  pa.active = w.active;
-  pa.n_active = w.n_active;
-  pa.rank = w.rank;
-  pa.tile_hist = w.tile_hist;
-  {
+    e = launch_route_fused(fa, s);
+  } else {
+    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw};
+    {
+      StageMark m(MOE_STAGE_ROUTE, s);
+      e = launch_router_logits(ra, s);
+      if (e == hipSuccess) e = launch_topk(ra, s);
+    }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    PermuteArgs pa{};
+    pa.ids = ids;
+    pa.w = tw;
+    pa.T = T;
+    pa.K = K;
+    pa.E = E;
+    pa.counts = w.counts;
+    pa.offsets = w.offsets;
+    pa.row_tok = w.row_tok;
+    pa.row_w = w.row_w;
+    pa.inv_pos = w.inv_pos;
+    pa.active = w.active;
+    pa.n_active = w.n_active;
+    pa.rank = w.rank;
+    pa.tile_hist = w.tile_hist;
     StageMark m(MOE_STAGE_PERMUTE, s);
     e = launch_permute(pa, s);
   }

@@ -90,6 +90,26 @@ struct RouteArgs {
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s);
 hipError_t launch_topk(const RouteArgs &a, hipStream_t s);
 
+// Router partial logits, then top-k + permutation in one block, for a decode
+// batch.
+constexpr int kFusedTokens = 16;    // largest T routed by the fused kernel
+constexpr int kFusedMaxChunks = 2;  // router slice <= 512 floats: float4 per lane
+struct RouteFusedArgs {
+  const float *router_w;
+  const float *router_bias;
+  const uint16_t *x;
+  int32_t T, H, E, K, renorm;
+  int32_t Hs, S;      // H slice per block and number of slices
+  float *logits;      // [T][E] or NULL
+  int32_t *ids;       // [T][K]
+  float *w;           // [T][K]
+  float *part;        // [S][T][E] partial logits
+  int32_t *counts, *offsets, *row_tok, *inv_pos, *active, *n_active;
+  float *row_w;
+};
+hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s);
+__host__ __device__ inline int route_fused_slice(int H) { return H % 512 == 0 ? 512 : 256; }
+
 struct PermuteArgs {
   const int32_t *ids;
   const float *w;

@@ -133,4 +133,13 @@ MOE_DEV int quad_slot(int c, int qd) {
 // spread over the LDS banks
 MOE_DEV int act_slot(int c, int k) { return c * 8 + ((k + c) & 7); }  // float4 index inside a row
 
+// Launchers: the item kernels (any token count, both formats) and the
+// int4 matrix-core kernels for decode batches (act rows as bf16 hi/lo
+// planes); gate/up and down must use the same family for one call.
+hipError_t launch_gateup_items(const FfnArgs &a, hipStream_t s);
+hipError_t launch_down_items(const FfnArgs &a, hipStream_t s);
+bool mfma_decode_ok(const FfnArgs &a);
+hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t s);
+hipError_t launch_down_mfma(const FfnArgs &a, hipStream_t s);
+
 }  // namespace moe

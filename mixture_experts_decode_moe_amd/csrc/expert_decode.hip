@@ -281,13 +281,11 @@ __global__ void __launch_bounds__(256) down_kernel(FfnArgs a) {
       const uint4 *dq = reinterpret_cast<const uint4 *>(static_cast<const char *>(u.dq) +
                                                         (static_cast<size_t>(u.e) * H + h) * row_bytes);
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if (i < ni) wd[rq][i] = load_stream16(dq + j + 16 * i);
+      for (int i = 0; i < NI; ++i) wd[rq][i] = i < ni ? load_stream16(dq + j + 16 * i) : make_uint4(0, 0, 0, 0);
       if constexpr (FMT == MOE_W_INT4_B32) {
         const uint16_t *ds = static_cast<const uint16_t *>(u.ds) + (static_cast<size_t>(u.e) * H + h) * nch;
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-          if (i < ni) sd[rq][i] = f16_bits_to_f32(ds[j + 16 * i]);
+        for (int i = 0; i < NI; ++i) sd[rq][i] = i < ni ? f16_bits_to_f32(ds[j + 16 * i]) : 0.f;
         rsc[rq] = 1.f;
       } else {
         rsc[rq] = static_cast<const float *>(u.ds)[static_cast<size_t>(u.e) * H + h];
@@ -306,11 +304,10 @@ __global__ void __launch_bounds__(256) down_kernel(FfnArgs a) {
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
           const int idx = base + 256 * b;
-          if (idx < n4) {
-            const int t = idx / f4;
-            const int k4 = idx - t * f4;
-            v[b] = reinterpret_cast<const float4 *>(a.act + unit_act_off(a, u, u.r0 + rg + t))[k4];
-          }
+          const int t = idx / f4;
+          const int k4 = idx - t * f4;
+          v[b] = idx < n4 ? reinterpret_cast<const float4 *>(a.act + unit_act_off(a, u, u.r0 + rg + t))[k4]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
@@ -323,7 +320,8 @@ __global__ void __launch_bounds__(256) down_kernel(FfnArgs a) {
         }
       }
       __syncthreads();
-      // one row at a time (runtime loop keeps a single fp32 fragment live)
+      // one row at a time (runtime loop keeps a single fp32 fragment live;
+      // the selection below costs a few scratch accesses per row)
 #pragma unroll 1
       for (int rq = 0; rq < 4; ++rq) {
         uint4 wr[NI];
@@ -475,7 +473,11 @@ hipError_t launch_down_items(const FfnArgs &a, hipStream_t s) {
   return launch_down_fmt<MOE_W_INT8_ROW>(a, s);
 }
 
-hipError_t launch_gateup(const FfnArgs &a, hipStream_t s) { return launch_gateup_items(a, s); }
-hipError_t launch_down(const FfnArgs &a, hipStream_t s) { return launch_down_items(a, s); }
+hipError_t launch_gateup(const FfnArgs &a, hipStream_t s) {
+  return mfma_decode_ok(a) ? launch_gateup_mfma(a, s) : launch_gateup_items(a, s);
+}
+hipError_t launch_down(const FfnArgs &a, hipStream_t s) {
+  return mfma_decode_ok(a) ? launch_down_mfma(a, s) : launch_down_items(a, s);
+}
 
 }  // namespace moe

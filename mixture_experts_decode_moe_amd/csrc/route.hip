@@ -17,79 +17,111 @@
 namespace moe {
 
 constexpr int kRouterTokens = 16;  // tokens per block (x tile staged in LDS)
-constexpr int kRouterExperts = 4;  // one expert per wave
-constexpr int kRouterMaxChunks = 16;  // H <= 4096: 16-byte router chunks per lane
 
-// One wave per expert row, one block per (4 experts, 16 tokens).  The token
-// tile is staged in LDS once per block: every wave then reads its x values
-// from LDS instead of all waves re-reading the same global lines.
+// Router arithmetic shared by every router kernel, so that all of them give
+// the same bits: H is cut into slices of Hs elements; a slice's partial
+// logit for (token t, expert e) is computed by the wave owning e, lane
+// (t, g) summing elements 16 i + 4 g + {0..3} of the slice in order, the
+// four lanes of a token then added as (g0 + g2) + (g1 + g3); the logit is
+// ((0 + p_0) + p_1) + ... + p_{S-1}, plus the bias.
+
+// Sum over the four rows of 16 lanes, in the order (r0 + r2) + (r1 + r3);
+// every lane receives its column's sum.
+MOE_DEV float rows4_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float a = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint32_t ua = __float_as_uint(a);
+  const auto q = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Stages the router rows of the block's 4 experts (slice [h0, h0 + Hs)) and
+// the slice of nt token rows starting at token t0 into LDS.
+MOE_DEV void stage_router_slice(const float *__restrict__ router_w, const uint16_t *__restrict__ x, int E, int H,
+                                int Hs, int e0, int h0, int t0, int nt, float *wr_l, uint16_t *xs) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int e = e0 + wave;
+  const float4 *src = reinterpret_cast<const float4 *>(router_w + static_cast<size_t>(e < E ? e : 0) * H + h0);
+  float4 *dst = reinterpret_cast<float4 *>(wr_l + wave * Hs);
+  const int n4 = Hs / 256;  // float4 per lane, <= kFusedMaxChunks
+  float4 v[kFusedMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kFusedMaxChunks; ++c) v[c] = c < n4 ? src[c * 64 + lane] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const int per_row = Hs / 8;
+  const int n8 = nt * per_row;  // <= 256 * kStageBatch
+  const int xstride = Hs + 8;
+  uint4 xv[kStageBatch];
+#pragma unroll
+  for (int b = 0; b < kStageBatch; ++b) {
+    const int i = tid + 256 * b;
+    const int t = i / per_row, k = i - t * per_row;
+    // unconditional assignment keeps the batch in registers
+    xv[b] = i < n8 ? reinterpret_cast<const uint4 *>(x + static_cast<size_t>(t0 + t) * H + h0)[k]
+                   : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < kFusedMaxChunks; ++c)
+    if (c < n4) dst[c * 64 + lane] = v[c];
+#pragma unroll
+  for (int b = 0; b < kStageBatch; ++b) {
+    const int i = tid + 256 * b;
+    if (i < n8) {
+      const int t = i / per_row, k = i - t * per_row;
+      reinterpret_cast<uint4 *>(xs + t * xstride)[k] = xv[b];
+    }
+  }
+}
+
+// Partial logit of one staged slice for the calling wave's expert; lane
+// (t = lane & 15, g = lane >> 4); every lane of column t gets token t's sum.
+MOE_DEV float slice_partial(const float *wrow, const uint16_t *xs, int Hs, int nt, bool valid) {
+  const int lane = __lane_id();
+  const int t = lane & 15, g = lane >> 4;
+  float acc = 0.f;
+  if (valid && t < nt) {
+    const uint16_t *xrow = xs + t * (Hs + 8);
+    for (int i = 0; i < Hs / 16; ++i) {
+      const float4 w4 = *reinterpret_cast<const float4 *>(wrow + 16 * i + 4 * g);
+      const uint2 x4 = *reinterpret_cast<const uint2 *>(xrow + 16 * i + 4 * g);
+      acc = fmaf(w4.x, bf16_lo(x4.x), acc);
+      acc = fmaf(w4.y, bf16_hi(x4.x), acc);
+      acc = fmaf(w4.z, bf16_lo(x4.y), acc);
+      acc = fmaf(w4.w, bf16_hi(x4.y), acc);
+    }
+  }
+  return rows4_sum(acc);
+}
+
+size_t router_slice_lds_bytes(int Hs, int tokens) {
+  return static_cast<size_t>(4) * Hs * 4 + static_cast<size_t>(tokens) * (Hs + 8) * 2;
+}
+
+// One block per (4 experts, 16 tokens); the slices are visited in order.
 __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restrict__ wr,
                                                             const float *__restrict__ bias,
                                                             const uint16_t *__restrict__ x, int32_t T, int32_t H,
                                                             int32_t E, float *__restrict__ logits) {
-  extern __shared__ uint2 xs[];  // [kRouterTokens][H/4] groups of four bf16
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int e = blockIdx.x * kRouterExperts + wave;
+  extern __shared__ float4 smem_router[];
+  const int Hs = route_fused_slice(H);
+  float *wr_l = reinterpret_cast<float *>(smem_router);
+  uint16_t *xs = reinterpret_cast<uint16_t *>(wr_l + 4 * Hs);
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int e0 = blockIdx.x * 4;
+  const int e = e0 + wave;
   const int t0 = blockIdx.y * kRouterTokens;
   const int nt = min(kRouterTokens, T - t0);
-  const int h4 = H / 4;
-  // this wave's router row first (all loads in flight at once), then the x
-  // tile in batches of independent 16-byte loads
-  const int nc = H / 256;  // <= kRouterMaxChunks
-  float4 wv[kRouterMaxChunks];
-  const float4 *wrow = reinterpret_cast<const float4 *>(wr + static_cast<size_t>(e < E ? e : 0) * H);
-#pragma unroll
-  for (int c = 0; c < kRouterMaxChunks; ++c)
-    if (c < nc) wv[c] = wrow[c * 64 + lane];
-  const int h8 = H / 8;
-  const int n8 = nt * h8;
-  for (int base = tid; base < n8; base += 256 * kStageBatch) {
-    uint4 v[kStageBatch];
-#pragma unroll
-    for (int b = 0; b < kStageBatch; ++b) {
-      const int i = base + 256 * b;
-      if (i < n8) {
-        const int t = i / h8, k = i - t * h8;
-        v[b] = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(t0 + t) * H)[k];
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kStageBatch; ++b) {
-      const int i = base + 256 * b;
-      if (i < n8) reinterpret_cast<uint4 *>(xs)[i] = v[b];
-    }
+  float total = 0.f;
+  for (int h0 = 0; h0 < H; h0 += Hs) {
+    __syncthreads();  // the previous slice's readers are done
+    stage_router_slice(wr, x, E, H, Hs, e0, h0, t0, nt, wr_l, xs);
+    __syncthreads();
+    total += slice_partial(wr_l + wave * Hs, xs, Hs, nt, e < E);
   }
-  __syncthreads();
-  if (e >= E) return;
-  float acc[kRouterTokens];
-#pragma unroll
-  for (int i = 0; i < kRouterTokens; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int c = 0; c < kRouterMaxChunks; ++c) {
-    if (c >= nc) break;
-#pragma unroll
-    for (int i = 0; i < kRouterTokens; ++i) {
-      if (i < nt) {
-        const uint2 xv = xs[i * h4 + c * 64 + lane];
-        acc[i] = fmaf(wv[c].x, bf16_lo(xv.x), acc[i]);
-        acc[i] = fmaf(wv[c].y, bf16_hi(xv.x), acc[i]);
-        acc[i] = fmaf(wv[c].z, bf16_lo(xv.y), acc[i]);
-        acc[i] = fmaf(wv[c].w, bf16_hi(xv.y), acc[i]);
-      }
-    }
-  }
-  const float b = bias ? bias[e] : 0.f;
-  float mine = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRouterTokens; ++i) {
-    if (i < nt) {
-      const float s = sum64(acc[i]);
-      if (lane == i) mine = s + b;
-    }
-  }
-  if (lane < nt) logits[static_cast<size_t>(t0 + lane) * E + e] = mine;
+  if (e < E && lane < nt) logits[static_cast<size_t>(t0 + lane) * E + e] = total + (bias ? bias[e] : 0.f);
 }
 
 // Order-preserving map of a float onto uint32 (NaN must be excluded).
@@ -131,32 +163,18 @@ MOE_DEV void wave_key_max(uint32_t &hi, uint32_t &lo) {
   lo = bl;
 }
 
-// One wave per token.  Lane l holds experts l, l+64, ... (up to 16 each).
+// Top-k of one token's logits held by a whole wave: lane l holds experts
+// l, l+64, ... in v[] (NaN already replaced by -inf, absent experts -inf).
+// Lane k < K receives round k's expert and routing weight.
 template <int NPL>
-__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int32_t T, int32_t E,
-                                                   int32_t K, int32_t renorm, int32_t *__restrict__ ids,
-                                                   float *__restrict__ wout) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const float *l = logits + static_cast<size_t>(t) * E;
-  float v[NPL];
+MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t renorm, int &my_e, float &my_w) {
+  const int lane = __lane_id();
   uint32_t key[NPL];  // 0 = used or absent
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int e = lane + 64 * j;
-    float val = -INFINITY;
-    if (e < E) {
-      val = l[e];
-      if (val != val) val = -INFINITY;  // NaN never outranks a number
-    }
-    v[j] = val;
-    key[j] = (e < E) ? float_key(val) : 0u;
-  }
+  for (int j = 0; j < NPL; ++j) key[j] = (lane + 64 * j < E) ? float_key(v[j]) : 0u;
   float top_v = 0.f;
   float my_v = 0.f;  // lane k keeps round k's value and index
-  int my_e = 0;
+  my_e = 0;
   for (int k = 0; k < K; ++k) {
     uint32_t hi = 0, lo = 0;
 #pragma unroll
@@ -190,20 +208,190 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ log
       if (lane + 64 * j < E) part += expf(v[j] - top_v);
     denom = sum64(part);
   }
+  my_w = mine / denom;
+}
+
+// One wave per token.  Lane l holds experts l, l+64, ... (up to 16 each).
+template <int NPL>
+__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int32_t T, int32_t E,
+                                                   int32_t K, int32_t renorm, int32_t *__restrict__ ids,
+                                                   float *__restrict__ wout) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float *l = logits + static_cast<size_t>(t) * E;
+  float v[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane + 64 * j;
+    float val = -INFINITY;
+    if (e < E) {
+      val = l[e];
+      if (val != val) val = -INFINITY;  // NaN never outranks a number
+    }
+    v[j] = val;
+  }
+  int my_e;
+  float my_w;
+  wave_topk<NPL>(v, E, K, renorm, my_e, my_w);
   if (lane < K) {
     ids[static_cast<size_t>(t) * K + lane] = my_e;
-    wout[static_cast<size_t>(t) * K + lane] = mine / denom;
+    wout[static_cast<size_t>(t) * K + lane] = my_w;
   }
 }
 
-hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s) {
-  dim3 grid((a.E + kRouterExperts - 1) / kRouterExperts, (a.T + kRouterTokens - 1) / kRouterTokens);
-  const size_t lds = static_cast<size_t>(kRouterTokens) * a.H * 2;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&router_logits_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
+// ------------------------------------------------------- decode routing
+//
+// For a decode batch (T <= kFusedTokens) routing takes two launches: the
+// pages merge "router top-k and grouping" into one kernel ("Qwen3.6-35B-A3B:
+// pictures, several requests at once and speed", Speed (0.1.45)); here the
+// router's blocks (4 experts x one slice of H each) write partial logits,
+// and one block then adds the slices in a fixed order, selects the top-k of
+// every token and builds the permutation.  (A last-block hand-off inside
+// one launch would need a device-scope fence per block, which on this chip
+// writes back the issuing XCD's L2 and costs far more than a launch.)
+
+// Exclusive scan of one value per thread over a 256-thread block; `scratch`
+// holds 4 ints.  Also returns the block total.
+MOE_DEV int scan256(int v, int *scratch, int &total) {
+  const int lane = __lane_id();
+  const int wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
   }
+  if (lane == 63) scratch[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += scratch[w];
+  total = scratch[0] + scratch[1] + scratch[2] + scratch[3];
+  __syncthreads();
+  return before + inc - v;
+}
+
+__global__ void __launch_bounds__(256) route_partial_kernel(RouteFusedArgs a) {
+  extern __shared__ float4 smem_route[];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int T = a.T, E = a.E, H = a.H, Hs = a.Hs, S = a.S;
+  const int slice = blockIdx.x % S;
+  const int e = (blockIdx.x / S) * 4 + wave;
+  const int h0 = slice * Hs;
+  float *wr_l = reinterpret_cast<float *>(smem_route);        // [4][Hs]
+  uint16_t *xs = reinterpret_cast<uint16_t *>(wr_l + 4 * Hs);  // [T][Hs + 8]
+  stage_router_slice(a.router_w, a.x, E, H, Hs, e - wave, h0, 0, T, wr_l, xs);
+  __syncthreads();
+  const float p = slice_partial(wr_l + wave * Hs, xs, Hs, T, e < E);
+  if (lane < T && e < E) a.part[(static_cast<size_t>(slice) * T + lane) * E + e] = p;
+}
+
+// One block: logits from the partial sums, top-k per token, permutation.
+template <int NPL>
+__global__ void __launch_bounds__(256) route_select_kernel(RouteFusedArgs a) {
+  extern __shared__ float4 smem_route[];
+  __shared__ int scan_scratch[4];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int T = a.T, E = a.E, S = a.S, K = a.K;
+  const int TK = T * K;
+  int32_t *ids_l = reinterpret_cast<int32_t *>(smem_route);  // [TK]
+  float *w_l = reinterpret_cast<float *>(ids_l + TK);         // [TK]
+  int32_t *cnt = reinterpret_cast<int32_t *>(w_l + TK);       // [E]
+  int32_t *off = cnt + E;                                     // [E]
+  for (int i = tid; i < E; i += 256) cnt[i] = 0;
+  for (int t = wave; t < T; t += 4) {
+    float v[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int ex = lane + 64 * j;
+      float val = -INFINITY;
+      if (ex < E) {
+        float sum = 0.f;
+        for (int sl = 0; sl < S; ++sl) sum += a.part[(static_cast<size_t>(sl) * T + t) * E + ex];
+        sum = sum + (a.router_bias ? a.router_bias[ex] : 0.f);
+        if (a.logits) a.logits[static_cast<size_t>(t) * E + ex] = sum;
+        val = (sum != sum) ? -INFINITY : sum;  // NaN never outranks a number
+      }
+      v[j] = val;
+    }
+    int my_e;
+    float my_w;
+    wave_topk<NPL>(v, E, K, a.renorm, my_e, my_w);
+    if (lane < K) {
+      const size_t p = static_cast<size_t>(t) * K + lane;
+      a.ids[p] = my_e;
+      a.w[p] = my_w;
+      ids_l[p] = my_e;
+      w_l[p] = my_w;
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < TK; p += 256) atomicAdd(&cnt[ids_l[p]], 1);
+  __syncthreads();
+  // thread tid owns experts [4 tid, 4 tid + 4)
+  int c4[4], n_here = 0, nz_here = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = 4 * tid + i;
+    c4[i] = ex < E ? cnt[ex] : 0;
+    n_here += c4[i];
+    nz_here += c4[i] > 0;
+  }
+  int total = 0, n_act = 0;
+  int base = scan256(n_here, scan_scratch, total);
+  int abase = scan256(nz_here, scan_scratch, n_act);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = 4 * tid + i;
+    if (ex < E) {
+      off[ex] = base;
+      a.counts[ex] = c4[i];
+      a.offsets[ex] = base;
+      if (c4[i] > 0) a.active[abase++] = ex;
+    }
+    base += c4[i];
+  }
+  if (tid == 0) {
+    a.offsets[E] = total;
+    *a.n_active = n_act;
+  }
+  __syncthreads();
+  for (int p = tid; p < TK; p += 256) {
+    const int ex = ids_l[p];
+    int r = 0;
+    for (int q = 0; q < p; ++q) r += ids_l[q] == ex;
+    const int pos = off[ex] + r;
+    a.row_tok[pos] = p / K;
+    a.row_w[pos] = w_l[p];
+    a.inv_pos[p] = pos;
+  }
+}
+
+hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
+  const int groups = (a.E + 3) / 4;
+  route_partial_kernel<<<groups * a.S, 256, router_slice_lds_bytes(a.Hs, a.T), s>>>(a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t lds = static_cast<size_t>(a.T) * a.K * 8 + static_cast<size_t>(a.E) * 8;
+  const int npl = (a.E + 63) / 64;
+  if (npl <= 1)
+    route_select_kernel<1><<<1, 256, lds, s>>>(a);
+  else if (npl <= 2)
+    route_select_kernel<2><<<1, 256, lds, s>>>(a);
+  else if (npl <= 4)
+    route_select_kernel<4><<<1, 256, lds, s>>>(a);
+  else
+    route_select_kernel<16><<<1, 256, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s) {
+  dim3 grid((a.E + 3) / 4, (a.T + kRouterTokens - 1) / kRouterTokens);
+  const size_t lds = router_slice_lds_bytes(route_fused_slice(a.H), kRouterTokens);
   router_logits_kernel<<<grid, 256, lds, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits);
   return hipGetLastError();
 }
