@@ -28,7 +28,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
   const int tid = threadIdx.x;
   const int n4 = a.H / 4;
   if (tid < a.K) rows[tid] = a.inv_pos[static_cast<size_t>(t) * a.K + tid];
-  __syncthreads();
+  lds_barrier();
   float4 r[kCombineChunks];
   float sq = 0.f;
 #pragma unroll
@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
   if (!a.normed_out) return;
   sq = sum64(sq);
   if ((tid & 63) == 0) wave_sq[tid >> 6] = sq;
-  __syncthreads();
+  lds_barrier();
   const float total = ((wave_sq[0] + wave_sq[1]) + wave_sq[2]) + wave_sq[3];
   const float inv_rms = 1.f / sqrtf(total / static_cast<float>(a.H) + a.eps);
 #pragma unroll

@@ -60,6 +60,13 @@ MOE_DEV float sum64(float v) {
 
 MOE_DEV int lane_id() { return __lane_id(); }
 
+// Block barrier for data exchanged through LDS only.  __syncthreads() also
+// orders global memory at workgroup scope, which makes every wave wait for
+// all its outstanding global loads and stores (prefetches included); this
+// waits for the wave's LDS operations only.  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+MOE_DEV void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---- workspace carving -------------------------------------------------------
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

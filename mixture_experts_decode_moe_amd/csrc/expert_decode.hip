@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(FfnArgs a) {
 
     for (int rg = 0; rg < u.n; rg += kGuRows) {
       const int nt = min(kGuRows, u.n - rg);
-      __syncthreads();  // the previous pass's LDS readers are done
+      lds_barrier();  // the previous pass's LDS readers are done
       const int n_stage = nt * nch;
       for (int base = tid; base < n_stage; base += 256 * kGuStageItems) {
       uint4 raw[kGuStageItems][QUADS];
@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(FfnArgs a) {
         xsum_lds[tk * nch + c] = s;
       }
       }
-      __syncthreads();
+      lds_barrier();
 
       for (int t = 0; t < nt; ++t) {
         float acc = 0.f;
@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(FfnArgs a) {
         const float r = sum16(acc) * rs;
         if (j == 0) out_lds[t * 16 + qg] = r;
       }
-      __syncthreads();
+      lds_barrier();
       if (tid < nt * kGuSlice) {
         const int t = tid / kGuSlice, fl = tid - t * kGuSlice;
         const float g = out_lds[t * 16 + fl];
@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(256) down_kernel(FfnArgs a) {
 
     for (int rg = 0; rg < u.n; rg += kDnRows) {
       const int nt = min(kDnRows, u.n - rg);
-      __syncthreads();
+      lds_barrier();
       // batches of independent 16-byte loads, then their LDS stores
       const int n4 = nt * f4;
       for (int base = tid; base < n4; base += 256 * kStageBatch) {
@@ -319,7 +319,7 @@ __global__ void __launch_bounds__(256) down_kernel(FfnArgs a) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       // one row at a time (runtime loop keeps a single fp32 fragment live;
       // the selection below costs a few scratch accesses per row)
 #pragma unroll 1
@@ -377,7 +377,7 @@ __global__ void __launch_bounds__(256) down_kernel(FfnArgs a) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       {  // one float4 of the [nt][64] tile per thread, scaled by the row weight
         const int t = tid >> 4, h4 = tid & 15;
         if (t < nt) {

@@ -1,4 +1,4 @@
-// Expert FFN for int4 weights on the bf16 matrix cores, decode batches.
+// Expert FFN on the bf16 matrix cores, decode batches (int4 and int8).
 //
 // The pages stream every selected expert's weights once for all the tokens
 // that picked it ("Every Public GGUF of This Model Is Missing Its Head",
@@ -22,11 +22,19 @@
 // bfloat16 hi + lo parts, which represent it to about 2^-16 relative, and
 // both parts go through the matrix core.
 //
+// int8 weights (q stored as a two's-complement byte, fp32 scale per row):
+// byte ^ 0x80 = q + 128 in [1, 255] is exact in bfloat16 (converted through
+// fp32), the 16x16x16 MFMA takes four consecutive k per lane, the sums run
+// over the whole row in the MFMA accumulator, a second accumulator collects
+// -128 * sum(x), and the row scale is applied once at the end.  The
+// operands keep their natural element order.
+//
 // Operand layout (v_mfma_f32_16x16x32_bf16, wave64): lane l supplies A row
 // l % 16 and B column l % 16, k-group l / 16 (8 consecutive k of the 32);
 // the result element (m, n) lands in lane 16 * (m / 4) + n, register m % 4.
-// A lane's 16-byte weight load covers one whole 32-element block of one
-// row; four such loads (k-groups g = 0..3 of four consecutive blocks) are
+// (The 16x16x16 form is the same with 4 k per lane.)  A lane's 16-byte
+// weight load covers one whole k-block of one row (32 int4 or 16 int8
+// weights); four such loads (k-groups g = 0..3 of four consecutive blocks) are
 // transposed across the four 16-lane rows of the wave with two
 // permlane32 and two permlane16 swaps, after which register p of lane
 // (n, g) holds k-group g of block 4j + p: exactly the B operand of that
@@ -43,15 +51,35 @@
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kMagicPair = 0x43004300u;     // bf16 pair (128, 128)
 constexpr uint32_t kMinus136Pair = 0xC308C308u;  // bf16 pair (-136, -136)
-constexpr int kMfmaMaxWaves = 8;
+constexpr uint32_t kMinus128Pair = 0xC300C300u;  // bf16 pair (-128, -128)
+constexpr int kGuMaxWaves = 16;  // gate/up: waves splitting the hidden dimension
+constexpr int kDnMaxWaves = 8;   // down: waves splitting the SwiGLU dimension
 
 MOE_DEV f32x4_t mfma_bf16(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                  c, 0, 0, 0);
+}
+
+MOE_DEV f32x4_t mfma_bf16_k16(const u32x2_t &a, const u32x2_t &b, const f32x4_t &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                   0, 0, 0);
+}
+
+// Four int8 weights (one k-group) -> two bf16 pairs of q + 128 (exact).
+MOE_DEV u32x2_t byte_pairs(uint32_t w) {
+  const uint32_t v = w ^ 0x80808080u;
+  const float f0 = static_cast<float>(v & 0xFFu), f1 = static_cast<float>((v >> 8) & 0xFFu);
+  const float f2 = static_cast<float>((v >> 16) & 0xFFu), f3 = static_cast<float>(v >> 24);
+  u32x2_t r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);  // high halves
+  r.y = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+  return r;
 }
 
 // Eight nibbles (one k-group) -> four bf16 pairs (128 + n_s, 128 + n_{s+4}).
@@ -101,9 +129,52 @@ MOE_DEV f32x4_t fma4(float s, const f32x4_t &c, const f32x4_t &acc) {
   return r;
 }
 
-// Position of SwiGLU column f inside its row of the act planes: the pair
-// order of the MFMA operands, (f, f + 4) adjacent within each group of 8.
-MOE_DEV int act_pos(int f) { return (f & ~7) | ((f & 3) << 1) | ((f >> 2) & 1); }
+// Position of SwiGLU column f inside its row of the act planes: the
+// element order of the MFMA operands (int4: (f, f + 4) adjacent within each
+// group of 8; int8: natural order).
+template <int FMT>
+MOE_DEV int act_pos(int f) {
+  if constexpr (FMT == MOE_W_INT4_B32) return (f & ~7) | ((f & 3) << 1) | ((f >> 2) & 1);
+  return f;
+}
+
+// Per-format pieces of the MFMA kernels: k per block (one 16-byte chunk of a
+// weight row), the A operand from a bf16 row, the B operand from a weight
+// k-group word, and the MFMA.
+template <int FMT>
+struct MfmaFmt;
+template <>
+struct MfmaFmt<MOE_W_INT4_B32> {
+  static constexpr int kBlockK = 32;
+  using Vec = u32x4_t;
+  // k-group g of block b of a bf16 row, pair-permuted
+  static MOE_DEV Vec a_x(const uint16_t *row, int b, int g) {
+    return pair_permute(reinterpret_cast<const uint4 *>(row)[4 * b + g]);
+  }
+  // the same from a hi or lo act plane (already in operand order)
+  static MOE_DEV Vec a_plane(const uint16_t *plane, int b, int g) {
+    const uint4 v = reinterpret_cast<const uint4 *>(plane)[4 * b + g];
+    return Vec{v.x, v.y, v.z, v.w};
+  }
+  static MOE_DEV Vec zero() { return Vec{0u, 0u, 0u, 0u}; }
+  static MOE_DEV Vec b_w(uint32_t w) { return magic_pairs(w); }
+  static MOE_DEV Vec corr() { return Vec{kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair}; }
+  static MOE_DEV f32x4_t mfma(const Vec &a, const Vec &b, const f32x4_t &c) { return mfma_bf16(a, b, c); }
+};
+template <>
+struct MfmaFmt<MOE_W_INT8_ROW> {
+  static constexpr int kBlockK = 16;
+  using Vec = u32x2_t;
+  static MOE_DEV Vec a_x(const uint16_t *row, int b, int g) {
+    const uint2 v = reinterpret_cast<const uint2 *>(row)[4 * b + g];
+    return Vec{v.x, v.y};
+  }
+  static MOE_DEV Vec a_plane(const uint16_t *plane, int b, int g) { return a_x(plane, b, g); }
+  static MOE_DEV Vec zero() { return Vec{0u, 0u}; }
+  static MOE_DEV Vec b_w(uint32_t w) { return byte_pairs(w); }
+  static MOE_DEV Vec corr() { return Vec{kMinus128Pair, kMinus128Pair}; }
+  static MOE_DEV f32x4_t mfma(const Vec &a, const Vec &b, const f32x4_t &c) { return mfma_bf16_k16(a, b, c); }
+};
 
 // Units of the MFMA kernels: the shared expert's tiles first, then the
 // routed units' tiles.
@@ -164,106 +235,254 @@ MOE_DEV size_t mrow_act(const FfnArgs &a, const MUnit &u, int r) {
 
 // ------------------------------------------------------------------ gate/up
 //
-// Item: (unit, 16 SwiGLU columns f0..f0+15): the 16 gate rows and the 16 up
-// rows.  Wave w multiplies block-quads [w JW, w JW + JW) of the hidden
-// dimension (128 elements each).  Output: act rows as bf16 hi and lo planes
-// in the pair order above.
-template <int JW>
-__global__ void __launch_bounds__(512) gateup_mfma_kernel(FfnArgs a) {
-  __shared__ f32x4_t red[kMfmaMaxWaves][2][64];
+// Persistent: one block of KS waves per compute unit; block b takes items
+// b, b + G, b + 2G, ...  The T (<= 16) token rows of x are staged in LDS
+// once per block, in operand order.  Item: (unit, 8 SwiGLU columns
+// f0..f0+7) as one 16-column MFMA tile: columns 0-7 are the gate rows
+// f0..f0+7, columns 8-15 the matching up rows.  Wave w multiplies
+// block-quads [w JW, w JW + JW) of the hidden dimension; the partial tiles
+// are added in LDS in wave order.  The block's items (unit, rows, tokens)
+// are looked up once into an LDS table, and each item's weights are
+// requested while the previous item is computed and reduced.
+constexpr int kGuTable = 128;  // most items one block takes
+
+template <int FMT, int JW>
+struct GuWeights {
+  uint4 w[JW];
+  uint32_t s[JW][2];  // int4: the fp16 scales of the four blocks
+  float rs;           // int8: the row scale
+};
+
+// A global-memory pointer that is the same in every lane, held in scalar
+// registers (so that selecting between two of them per lane is a register
+// select, not a load from the argument block), and typed as global so that
+// the loads through it are global loads (a flat load would also count
+// against the LDS counter that every LDS wait drains).
+typedef __attribute__((address_space(1))) const char gchar_t;
+typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
+typedef __attribute__((address_space(1))) const uint32_t gu32_t;
+typedef __attribute__((address_space(1))) const float gf32_t;
+
+MOE_DEV gchar_t *uniform_gptr(const void *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<gchar_t *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+MOE_DEV uint4 load_stream16_g(gchar_t *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Loads this lane's part of item (e, f0): lanes n < 8 the gate row f0 + n,
+// lanes n >= 8 the up row f0 + n - 8 (e < 0: the shared expert).
+template <int FMT, int JW>
+MOE_DEV void gu_load(const FfnArgs &a, int e, int f0, int wave, int n, int g, GuWeights<FMT, JW> &w) {
+  using Fm = MfmaFmt<FMT>;
+  const bool shared = e < 0;
+  const bool up = n >= 8;
+  const int F = shared ? a.Fs : a.F;
+  const size_t row = static_cast<size_t>(shared ? 0 : e) * F + f0 + (n & 7);
+  gchar_t *gq = uniform_gptr(shared ? a.sgq : a.gq), *uq = uniform_gptr(shared ? a.suq : a.uq);
+  gchar_t *gs = uniform_gptr(shared ? a.sgs : a.gs), *us = uniform_gptr(shared ? a.sus : a.us);
+  gchar_t *q = up ? uq : gq;
+  gchar_t *sc = up ? us : gs;
+  const int nblk = a.H / Fm::kBlockK;
+  gchar_t *p = q + row * nblk * 16;
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) w.w[jj] = load_stream16_g(p + 16 * (4 * (wave * JW + jj) + g));
+  if constexpr (FMT == MOE_W_INT4_B32) {
+    gu32_t *sp = reinterpret_cast<gu32_t *>(sc + row * nblk * 2);
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+      const int j = wave * JW + jj;
+      w.s[jj][0] = sp[2 * j];
+      w.s[jj][1] = sp[2 * j + 1];
+    }
+    w.rs = 1.f;
+  } else {
+    w.rs = reinterpret_cast<gf32_t *>(sc)[row];
+  }
+}
+
+// Unit of item i: e (-1 for the shared expert), first row, rows, f0.
+MOE_DEV void gu_item(const FfnArgs &a, int i, int tiles_r, int tiles_s, int &e, int &r0, int &n, int &f0) {
+  if (i < tiles_s) {
+    e = -1;
+    r0 = 0;
+    n = a.T;
+    f0 = i * 8;
+    return;
+  }
+  const int k = (i - tiles_s) / tiles_r;
+  f0 = (i - tiles_s - k * tiles_r) * 8;
+  if (a.offsets) {
+    e = a.active[k];
+    r0 = a.offsets[e];
+    n = a.offsets[e + 1] - r0;
+  } else {
+    e = 0;
+    r0 = 0;
+    n = a.n_rows;
+  }
+}
+
+template <int FMT, int JW, int NI>
+__global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
+  using Fm = MfmaFmt<FMT>;
+  using Vec = typename Fm::Vec;
+  constexpr bool kInt4 = FMT == MOE_W_INT4_B32;
+  extern __shared__ uint4 xs_lds[];  // [T][H/8 + 1] 16-byte pieces of x
+  __shared__ f32x4_t red[kGuMaxWaves][64];
+  __shared__ int tab[kGuTable][4];   // e, r0, n (<= 16), f0
+  __shared__ int toks[kGuTable][16];
+  __shared__ uint32_t act_st[NI][16][8];  // SwiGLU outputs of a chunk: bf16 hi | lo << 16
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int KS = blockDim.x >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int H = a.H;
-  const int nsc = H / 32;
-  const size_t row_bytes = static_cast<size_t>(H) / 2;
+  const int H = a.H, T = a.T;
   const int U = routed_units(a);
-  const int tiles_r = a.F / 16;
-  const int tiles_s = a.Fs / 16;
+  const int tiles_r = a.F / 8, tiles_s = a.Fs / 8;
   const int n_items = tiles_s + U * tiles_r;
-  const u32x4_t m136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
+  // block b owns the contiguous items [b C, b C + C) (C <= kGuTable)
+  const int C = (n_items + gridDim.x - 1) / gridDim.x;
+  const int first = blockIdx.x * C;
+  const int my_items = n_items > first ? min(C, n_items - first) : 0;
+  if (my_items == 0) return;
+  const Vec cvec = Fm::corr();
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const int pieces = H / 8;  // 16-byte pieces per x row
+  const int xstride = pieces + 1;
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    MUnit u;
-    if (!mfma_unit(a, item, tiles_r, tiles_s, U, u) || u.n <= 0) continue;
-    const int f0 = u.tile * 16;
-    const size_t row = static_cast<size_t>(u.e) * u.F + f0 + n;
-    const uint4 *gp = reinterpret_cast<const uint4 *>(static_cast<const char *>(u.gq) + row * row_bytes);
-    const uint4 *up = reinterpret_cast<const uint4 *>(static_cast<const char *>(u.uq) + row * row_bytes);
-    const uint32_t *gsp = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(u.gs) + row * nsc);
-    const uint32_t *usp = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(u.us) + row * nsc);
-    uint4 wg[JW], wu[JW];
-    uint32_t sg[JW][2], su[JW][2];
+  // waves 0-1 look up the block's items (unit, rows, tokens; one thread per
+  // item, all in parallel) while the other waves stage the x rows in LDS
+  if (tid < kGuTable) {
+    if (tid < my_items) {
+      int e, r0, nn, f0;
+      gu_item(a, first + tid, tiles_r, tiles_s, e, r0, nn, f0);
+      nn = nn < 0 ? 0 : (nn > 16 ? 16 : nn);  // one 16-row tile (T <= 16)
+      tab[tid][0] = e;
+      tab[tid][1] = r0;
+      tab[tid][2] = nn;
+      tab[tid][3] = f0;
+      int tk[16];
+      const int last = a.n_rows > 0 ? a.n_rows - 1 : 0;
 #pragma unroll
-    for (int jj = 0; jj < JW; ++jj) {
-      const int j = wave * JW + jj;
-      wg[jj] = load_stream16(gp + 4 * j + g);
-      wu[jj] = load_stream16(up + 4 * j + g);
-      sg[jj][0] = gsp[2 * j];
-      sg[jj][1] = gsp[2 * j + 1];
-      su[jj][0] = usp[2 * j];
-      su[jj][1] = usp[2 * j + 1];
+      for (int m = 0; m < 16; ++m) {
+        // unconditional (clamped) loads, selected afterwards
+        const int ri = min(r0 + m, last);
+        const int raw = a.row_tok ? a.row_tok[ri] : ri;
+        const int t = m < nn ? (e < 0 ? m : raw) : 0;
+        tk[m] = t < 0 ? 0 : (t >= T ? T - 1 : t);  // memory safety for malformed row lists
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) toks[tid][m] = tk[m];
     }
+  } else {
+    const int nthr = blockDim.x - kGuTable;
+    for (int base = tid - kGuTable; base < T * pieces; base += nthr * kStageBatch) {
+      uint4 v[kStageBatch];
 #pragma unroll
-    for (int jj = 0; jj < JW; ++jj) {
-      xpose4(wg[jj]);
-      xpose4(wu[jj]);
-    }
-
-    for (int m0 = 0; m0 < u.n; m0 += 16) {
-      const int m = m0 + n;
-      const bool mv = m < u.n;
-      const uint4 *xp = reinterpret_cast<const uint4 *>(a.x + static_cast<size_t>(mrow_token(a, u, u.r0 + (mv ? m : 0))) * H);
-      u32x4_t xa[JW][4];
+      for (int b = 0; b < kStageBatch; ++b) {
+        const int i = base + b * nthr;
+        v[b] = i < T * pieces ? reinterpret_cast<const uint4 *>(a.x)[i] : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-      for (int jj = 0; jj < JW; ++jj)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int b = 4 * (wave * JW + jj) + p;
-          xa[jj][p] = pair_permute(mv ? xp[4 * b + g] : make_uint4(0, 0, 0, 0));
-        }
-      f32x4_t accg = zero4, accu = zero4;
-#pragma unroll
-      for (int jj = 0; jj < JW; ++jj)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const f32x4_t corr = mfma_bf16(xa[jj][p], m136, zero4);
-          const f32x4_t cg = mfma_bf16(xa[jj][p], magic_pairs(word(wg[jj], p)), corr);
-          const f32x4_t cu = mfma_bf16(xa[jj][p], magic_pairs(word(wu[jj], p)), corr);
-          accg = fma4(scale4(sg[jj][0], sg[jj][1], p), cg, accg);
-          accu = fma4(scale4(su[jj][0], su[jj][1], p), cu, accu);
-        }
-      red[wave][0][lane] = accg;
-      red[wave][1][lane] = accu;
-      __syncthreads();
-      if (wave == 0) {
-        f32x4_t G = red[0][0][lane], V = red[0][1][lane];
-        for (int w = 1; w < KS; ++w) {
-          G += red[w][0][lane];
-          V += red[w][1][lane];
-        }
-        const int f = f0 + n;
-        const int pos = act_pos(f);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int mm = m0 + 4 * g + i;
-          if (mm < u.n) {
-            const float gv = G[i], uv = V[i];
-            const float v = gv / (1.f + expf(-gv)) * uv;
-            const uint16_t hi = f32_to_bf16_rne(v);
-            const uint16_t lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
-            uint16_t *arow = reinterpret_cast<uint16_t *>(a.act + mrow_act(a, u, u.r0 + mm));
-            arow[pos] = hi;
-            arow[u.F + pos] = lo;
+      for (int b = 0; b < kStageBatch; ++b) {
+        const int i = base + b * nthr;
+        if (i < T * pieces) {
+          const int t = i / pieces, k = i - t * pieces;
+          uint4 o = v[b];
+          if constexpr (kInt4) {
+            const u32x4_t pp = pair_permute(v[b]);
+            o = make_uint4(pp.x, pp.y, pp.z, pp.w);
           }
+          xs_lds[t * xstride + k] = o;
         }
       }
-      __syncthreads();
     }
+  }
+  lds_barrier();
+
+  // Chunks of NI items as straight-line code: every weight load of a chunk
+  // is issued first (unconditionally: a missing item re-requests the
+  // chunk's first item, already in flight), so the wait before each item
+  // leaves the later items' loads in flight.
+  for (int c0 = 0; c0 < my_items; c0 += NI) {
+    GuWeights<FMT, JW> w[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int it = c0 + i < my_items ? c0 + i : c0;
+      gu_load<FMT, JW>(a, tab[it][0], tab[it][3], wave, n, g, w[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int it = c0 + i;
+      if (it < my_items) {
+        const int e = tab[it][0], nrows = tab[it][2];
+#pragma unroll
+        for (int jj = 0; jj < JW; ++jj) xpose4(w[i].w[jj]);
+        const bool mv = n < nrows;
+        const uint16_t *xrow = reinterpret_cast<const uint16_t *>(xs_lds + toks[it][n] * xstride);
+        f32x4_t acc = zero4, corr = zero4;
+#pragma unroll
+        for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            // staged x is already in operand order
+            const Vec xa = mv ? Fm::a_plane(xrow, 4 * (wave * JW + jj) + p, g) : Fm::zero();
+            if constexpr (kInt4) {
+              // per block: -136 * sum(x) as the accumulator input, then the scale
+              const f32x4_t c0v = Fm::mfma(xa, cvec, zero4);
+              const f32x4_t c = Fm::mfma(xa, Fm::b_w(word(w[i].w[jj], p)), c0v);
+              acc = fma4(scale4(w[i].s[jj][0], w[i].s[jj][1], p), c, acc);
+            } else {
+              acc = Fm::mfma(xa, Fm::b_w(word(w[i].w[jj], p)), acc);
+              corr = Fm::mfma(xa, cvec, corr);
+            }
+          }
+        if constexpr (!kInt4) acc = (acc + corr) * w[i].rs;
+        red[wave][lane] = acc;
+        lds_barrier();
+        // wave m adds token row m's partial sums (lanes 0-7: the gate and
+        // up columns f0 + lane) in wave order and keeps the SwiGLU output
+        if (wave < nrows && lane < 8) {
+          const int src = 16 * (wave >> 2) + lane, r = wave & 3;
+          float gv = 0.f, uv = 0.f;
+          for (int ww = 0; ww < KS; ++ww) {
+            gv += red[ww][src][r];
+            uv += red[ww][src + 8][r];
+          }
+          const float v = gv / (1.f + expf(-gv)) * uv;
+          const uint16_t hi = f32_to_bf16_rne(v);
+          const uint16_t lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
+          act_st[i][wave][lane] = static_cast<uint32_t>(hi) | (static_cast<uint32_t>(lo) << 16);
+        }
+        (void)e;
+        lds_barrier();
+      }
+    }
+    // the chunk's SwiGLU rows to global memory: thread (i, m, f)
+    if (tid < NI * 128) {
+      const int i = tid >> 7, m = (tid >> 3) & 15, f = tid & 7;
+      const int it = c0 + i;
+      if (it < my_items && m < tab[it][2]) {
+        const int e = tab[it][0], r0 = tab[it][1], f0 = tab[it][3];
+        const int F = e < 0 ? a.Fs : a.F;
+        const size_t off = e < 0 ? static_cast<size_t>(a.n_rows) * a.F + static_cast<size_t>(m) * a.Fs
+                                 : static_cast<size_t>(r0 + m) * a.F;
+        uint16_t *arow = reinterpret_cast<uint16_t *>(a.act + off);
+        const uint32_t v = act_st[i][m][f];
+        const int pos = act_pos<FMT>(f0 + f);
+        arow[pos] = static_cast<uint16_t>(v & 0xFFFFu);
+        arow[F + pos] = static_cast<uint16_t>(v >> 16);
+      }
+    }
+    lds_barrier();
   }
 }
 
@@ -272,9 +491,12 @@ __global__ void __launch_bounds__(512) gateup_mfma_kernel(FfnArgs a) {
 // Item: (unit, 64 output rows h0..h0+63 as four 16-row tiles).  Wave w
 // multiplies block-quads [w JW, w JW + JW) of the SwiGLU dimension.  The
 // routing weight is applied when the summed tile is stored.
-template <int JW>
+template <int FMT, int JW>
 __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
-  __shared__ f32x4_t red[kMfmaMaxWaves][4][64];
+  using Fm = MfmaFmt<FMT>;
+  using Vec = typename Fm::Vec;
+  constexpr bool kInt4 = FMT == MOE_W_INT4_B32;
+  __shared__ f32x4_t red[kDnMaxWaves][4][64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -285,7 +507,7 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
   const int U = routed_units(a);
   const int tiles = H / 64;
   const int n_items = (a.Fs > 0 ? tiles : 0) + U * tiles;
-  const u32x4_t m136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
+  const Vec cvec = Fm::corr();
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -293,62 +515,86 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
     if (!mfma_unit(a, item, tiles, a.Fs > 0 ? tiles : 0, U, u) || u.n <= 0) continue;
     const int h0 = u.tile * 64;
     const int F = u.F;
-    const int nsc = F / 32;
-    const size_t row_bytes = static_cast<size_t>(F) / 2;
+    const int nblk = F / Fm::kBlockK;
+    const size_t row_bytes = static_cast<size_t>(nblk) * 16;
     uint4 wd[JW][4];
     uint32_t sd[JW][4][2];
+    float rs[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const size_t row = static_cast<size_t>(u.e) * H + h0 + 16 * nt + n;
       const uint4 *dp = reinterpret_cast<const uint4 *>(static_cast<const char *>(u.dq) + row * row_bytes);
-      const uint32_t *sp = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(u.ds) + row * nsc);
 #pragma unroll
       for (int jj = 0; jj < JW; ++jj) {
         const int j = wave * JW + jj;
         wd[jj][nt] = load_stream16(dp + 4 * j + g);
-        sd[jj][nt][0] = sp[2 * j];
-        sd[jj][nt][1] = sp[2 * j + 1];
+        if constexpr (kInt4) {
+          const uint32_t *sp = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(u.ds) + row * nblk);
+          sd[jj][nt][0] = sp[2 * j];
+          sd[jj][nt][1] = sp[2 * j + 1];
+        }
       }
+      if constexpr (!kInt4) rs[nt] = static_cast<const float *>(u.ds)[row];
     }
+    // activation rows of the first 16 rows, requested before the weights are
+    // waited for
+    Vec ah[JW][4], al[JW][4];
+    auto load_a = [&](int m0) {
+      const int m = m0 + n;
+      const bool mv = m < u.n;
+      const uint16_t *hp = reinterpret_cast<const uint16_t *>(a.act + mrow_act(a, u, u.r0 + (mv ? m : 0)));
+      const uint16_t *lp = hp + F;  // lo plane follows the hi plane
+#pragma unroll
+      for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int b = 4 * (wave * JW + jj) + p;
+          ah[jj][p] = mv ? Fm::a_plane(hp, b, g) : Fm::zero();
+          al[jj][p] = mv ? Fm::a_plane(lp, b, g) : Fm::zero();
+        }
+    };
+    load_a(0);
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) xpose4(wd[jj][nt]);
 
     for (int m0 = 0; m0 < u.n; m0 += 16) {
-      const int m = m0 + n;
-      const bool mv = m < u.n;
-      const uint4 *hp = reinterpret_cast<const uint4 *>(a.act + mrow_act(a, u, u.r0 + (mv ? m : 0)));
-      const uint4 *lp = hp + F / 8;  // lo plane follows the hi plane
-      u32x4_t ah[JW][4], al[JW][4];
-#pragma unroll
-      for (int jj = 0; jj < JW; ++jj)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int b = 4 * (wave * JW + jj) + p;
-          const uint4 vh = mv ? hp[4 * b + g] : make_uint4(0, 0, 0, 0);
-          const uint4 vl = mv ? lp[4 * b + g] : make_uint4(0, 0, 0, 0);
-          ah[jj][p] = {vh.x, vh.y, vh.z, vh.w};
-          al[jj][p] = {vl.x, vl.y, vl.z, vl.w};
-        }
+      if (m0 > 0) load_a(m0);
       f32x4_t acc[4] = {zero4, zero4, zero4, zero4};
+      f32x4_t corr = zero4;
 #pragma unroll
       for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          f32x4_t corr = mfma_bf16(ah[jj][p], m136, zero4);
-          corr = mfma_bf16(al[jj][p], m136, corr);
+          if constexpr (kInt4) {
+            f32x4_t c0 = Fm::mfma(ah[jj][p], cvec, zero4);
+            c0 = Fm::mfma(al[jj][p], cvec, c0);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const u32x4_t bw = magic_pairs(word(wd[jj][nt], p));
-            f32x4_t c = mfma_bf16(ah[jj][p], bw, corr);
-            c = mfma_bf16(al[jj][p], bw, c);
-            acc[nt] = fma4(scale4(sd[jj][nt][0], sd[jj][nt][1], p), c, acc[nt]);
+            for (int nt = 0; nt < 4; ++nt) {
+              const Vec bw = Fm::b_w(word(wd[jj][nt], p));
+              f32x4_t c = Fm::mfma(ah[jj][p], bw, c0);
+              c = Fm::mfma(al[jj][p], bw, c);
+              acc[nt] = fma4(scale4(sd[jj][nt][0], sd[jj][nt][1], p), c, acc[nt]);
+            }
+          } else {
+            corr = Fm::mfma(ah[jj][p], cvec, corr);
+            corr = Fm::mfma(al[jj][p], cvec, corr);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+              const Vec bw = Fm::b_w(word(wd[jj][nt], p));
+              acc[nt] = Fm::mfma(ah[jj][p], bw, acc[nt]);
+              acc[nt] = Fm::mfma(al[jj][p], bw, acc[nt]);
+            }
           }
         }
+      if constexpr (!kInt4) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[nt] = (acc[nt] + corr) * rs[nt];
+      }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) red[wave][nt][lane] = acc[nt];
-      __syncthreads();
+      lds_barrier();
       if (wave < 4) {
         const int nt = wave;
         f32x4_t v = red[0][nt][lane];
@@ -365,7 +611,7 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 }
@@ -374,51 +620,91 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
 
 static int mfma_grid(int items) { return items < 1 ? 1 : (items < 4096 ? items : 4096); }
 
-template <int JW>
-static hipError_t launch_gateup_mfma_t(const FfnArgs &a, int ks, hipStream_t s) {
-  const int items = a.Fs / 16 + a.max_units * (a.F / 16);
-  gateup_mfma_kernel<JW><<<mfma_grid(items), 64 * ks, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-template <int JW>
-static hipError_t launch_down_mfma_t(const FfnArgs &a, int ks, hipStream_t s) {
-  const int tiles = a.H / 64;
-  const int items = (a.Fs > 0 ? tiles : 0) + a.max_units * tiles;
-  down_mfma_kernel<JW><<<mfma_grid(items), 64 * ks, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-// Block-quads J = K / 128 split over KS waves of JW each, KS in {4, 8}.
-static bool split_k(int K, int &jw, int &ks) {
-  const int J = K / 128;
-  if (K % 128 || J < 4) return false;
-  ks = J <= 8 ? J : 8;
-  if (ks != 4 && ks != 8) return false;
+// Block-quads J = K / (4 kBlockK) split over KS waves of JW each, KS a
+// power of two in [4, max_waves], JW in {1, 2, 4}.
+static bool split_k(int K, int block_k, int max_waves, int &jw, int &ks) {
+  const int quad = 4 * block_k;
+  const int J = K / quad;
+  if (K % quad || J < 4) return false;
+  ks = J <= max_waves ? J : max_waves;
+  if (ks & (ks - 1)) return false;
   jw = J / ks;
   return jw * ks == J && (jw == 1 || jw == 2 || jw == 4);
 }
 
+static int block_k(int fmt) { return fmt == MOE_W_INT4_B32 ? 32 : 16; }
+
 bool mfma_decode_ok(const FfnArgs &a) {
   int jw, ks;
-  return a.fmt == MOE_W_INT4_B32 && a.T <= kFusedTokens && (a.Fs == 0 || a.Fs == a.F) && split_k(a.H, jw, ks) &&
-         split_k(a.F, jw, ks);
+  return (a.fmt == MOE_W_INT4_B32 || a.fmt == MOE_W_INT8_ROW) && a.T <= kFusedTokens &&
+         (a.Fs == 0 || a.Fs == a.F) && split_k(a.H, block_k(a.fmt), kGuMaxWaves, jw, ks) &&
+         split_k(a.F, block_k(a.fmt), kDnMaxWaves, jw, ks);
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+template <int FMT, int JW>
+static hipError_t launch_gateup_mfma_t(const FfnArgs &a, int ks, hipStream_t s) {
+  // items per chunk: about 128 KiB of weights in flight per block
+  constexpr int D = FMT == MOE_W_INT4_B32 ? (JW == 1 ? 8 : 4) : (JW == 1 ? 8 : 4);
+  const size_t lds = static_cast<size_t>(a.T) * (a.H / 8 + 1) * 16;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_mfma_kernel<FMT, JW, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  // one block per compute unit, at most kGuTable items each (the grid is
+  // sized for the largest possible routing; blocks past the last item exit)
+  const int items = a.Fs / 8 + a.max_units * (a.F / 8);
+  const int cus = cu_count();
+  int grid = (items + kGuTable - 1) / kGuTable;
+  if (grid < cus) grid = items < cus ? (items < 1 ? 1 : items) : cus;
+  gateup_mfma_kernel<FMT, JW, D><<<grid, 64 * ks, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_gateup_mfma_f(const FfnArgs &a, hipStream_t s) {
+  int jw, ks;
+  split_k(a.H, block_k(FMT), kGuMaxWaves, jw, ks);
+  if (jw == 1) return launch_gateup_mfma_t<FMT, 1>(a, ks, s);
+  if (jw == 2) return launch_gateup_mfma_t<FMT, 2>(a, ks, s);
+  return launch_gateup_mfma_t<FMT, 4>(a, ks, s);
+}
+
+template <int FMT>
+static hipError_t launch_down_mfma_f(const FfnArgs &a, hipStream_t s) {
+  int jw, ks;
+  split_k(a.F, block_k(FMT), kDnMaxWaves, jw, ks);
+  const int tiles = a.H / 64;
+  const int grid = mfma_grid((a.Fs > 0 ? tiles : 0) + a.max_units * tiles);
+  if (jw == 1)
+    down_mfma_kernel<FMT, 1><<<grid, 64 * ks, 0, s>>>(a);
+  else if (jw == 2)
+    down_mfma_kernel<FMT, 2><<<grid, 64 * ks, 0, s>>>(a);
+  else
+    down_mfma_kernel<FMT, 4><<<grid, 64 * ks, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t s) {
-  int jw, ks;
-  split_k(a.H, jw, ks);
-  if (jw == 1) return launch_gateup_mfma_t<1>(a, ks, s);
-  if (jw == 2) return launch_gateup_mfma_t<2>(a, ks, s);
-  return launch_gateup_mfma_t<4>(a, ks, s);
+  return a.fmt == MOE_W_INT4_B32 ? launch_gateup_mfma_f<MOE_W_INT4_B32>(a, s)
+                                 : launch_gateup_mfma_f<MOE_W_INT8_ROW>(a, s);
 }
 
 hipError_t launch_down_mfma(const FfnArgs &a, hipStream_t s) {
-  int jw, ks;
-  split_k(a.F, jw, ks);
-  if (jw == 1) return launch_down_mfma_t<1>(a, ks, s);
-  if (jw == 2) return launch_down_mfma_t<2>(a, ks, s);
-  return launch_down_mfma_t<4>(a, ks, s);
+  return a.fmt == MOE_W_INT4_B32 ? launch_down_mfma_f<MOE_W_INT4_B32>(a, s) : launch_down_mfma_f<MOE_W_INT8_ROW>(a, s);
 }
 
 }  // namespace moe

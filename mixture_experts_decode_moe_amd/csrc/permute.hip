@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(kPermuteTile) permute_tile_kernel(const int32_
     if (e < 0 || e >= E) e = -1;  // out-of-range ids are dropped
   }
   const bool valid = e >= 0;
-  __syncthreads();
+  lds_barrier();
   uint64_t todo = __ballot(valid);
   uint64_t peers = 0;
   while (todo) {
@@ -48,7 +48,7 @@ __global__ void __launch_bounds__(kPermuteTile) permute_tile_kernel(const int32_
   }
   const int rank_w = __popcll(peers & lanemask_lt());
   if (valid && rank_w == 0) wcnt[wave * E + e] = static_cast<uint16_t>(__popcll(peers));
-  __syncthreads();
+  lds_barrier();
   if (valid) {
     int r = rank_w;
     for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
@@ -72,14 +72,14 @@ MOE_DEV int block_exclusive_scan(int v, int *scratch /* >= kWaves ints */, int &
     if (lane >= off) inc += o;
   }
   if (lane == 63) scratch[wave] = inc;
-  __syncthreads();
+  lds_barrier();
   int before = 0, all = 0;
   for (int w = 0; w < kWaves; ++w) {
     const int s = scratch[w];
     if (w < wave) before += s;
     all += s;
   }
-  __syncthreads();
+  lds_barrier();
   total = all;
   return before + inc - v;
 }
@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(kPermuteTile) permute_scatter_kernel(
       *n_active = n_act;
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int64_t p = static_cast<int64_t>(tile) * kPermuteTile + tid;
   if (p < TK) {
     const int e = ids[p];

@@ -116,9 +116,9 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restr
   const int nt = min(kRouterTokens, T - t0);
   float total = 0.f;
   for (int h0 = 0; h0 < H; h0 += Hs) {
-    __syncthreads();  // the previous slice's readers are done
+    lds_barrier();  // the previous slice's readers are done
     stage_router_slice(wr, x, E, H, Hs, e0, h0, t0, nt, wr_l, xs);
-    __syncthreads();
+    lds_barrier();
     total += slice_partial(wr_l + wave * Hs, xs, Hs, nt, e < E);
   }
   if (e < E && lane < nt) logits[static_cast<size_t>(t0 + lane) * E + e] = total + (bias ? bias[e] : 0.f);
@@ -134,33 +134,19 @@ MOE_DEV float key_float(uint32_t k) {
 }
 
 template <int CTRL>
-MOE_DEV void key_max_step(uint32_t &hi, uint32_t &lo) {
-  const uint32_t ph = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi), CTRL, 0xF, 0xF, true));
-  const uint32_t pl = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo), CTRL, 0xF, 0xF, true));
-  const bool take = (ph > hi) || (ph == hi && pl > lo);
-  hi = take ? ph : hi;
-  lo = take ? pl : lo;
+MOE_DEV uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 
-MOE_DEV void key_take(uint32_t &hi, uint32_t &lo, uint32_t oh, uint32_t ol) {
-  if (oh > hi || (oh == hi && ol > lo)) {
-    hi = oh;
-    lo = ol;
-  }
-}
-
-// Wave-wide maximum of 64-bit keys (hi, lo); the result is uniform.
-MOE_DEV void wave_key_max(uint32_t &hi, uint32_t &lo) {
-  key_max_step<0xB1>(hi, lo);   // quad_perm [1,0,3,2]
-  key_max_step<0x4E>(hi, lo);   // quad_perm [2,3,0,1]
-  key_max_step<0x141>(hi, lo);  // row_half_mirror
-  key_max_step<0x140>(hi, lo);  // row_mirror
-  uint32_t bh = __builtin_amdgcn_readlane(hi, 0), bl = __builtin_amdgcn_readlane(lo, 0);
-  key_take(bh, bl, __builtin_amdgcn_readlane(hi, 16), __builtin_amdgcn_readlane(lo, 16));
-  key_take(bh, bl, __builtin_amdgcn_readlane(hi, 32), __builtin_amdgcn_readlane(lo, 32));
-  key_take(bh, bl, __builtin_amdgcn_readlane(hi, 48), __builtin_amdgcn_readlane(lo, 48));
-  hi = bh;
-  lo = bl;
+// Wave-wide maximum (uniform result).
+MOE_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 // Top-k of one token's logits held by a whole wave: lane l holds experts
@@ -176,22 +162,27 @@ MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t reno
   float my_v = 0.f;  // lane k keeps round k's value and index
   my_e = 0;
   for (int k = 0; k < K; ++k) {
-    uint32_t hi = 0, lo = 0;
+    // the largest remaining key, then the lowest expert index holding it
+    uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      key_take(hi, lo, key[j], key[j] ? 0xFFFFu - static_cast<uint32_t>(lane + 64 * j) : 0u);
-    wave_key_max(hi, lo);
-    const int sel_e = static_cast<int>(0xFFFFu - (lo & 0xFFFFu));
-    const float sel_v = key_float(hi);
-    if ((sel_e & 63) == lane) {
+    for (int j = 0; j < NPL; ++j) m = max(m, key[j]);
+    m = wave_max_u32(m);
+    int sel = 0;
+#pragma unroll
+    for (int j = NPL - 1; j >= 0; --j) {
+      const uint64_t hit = __ballot(key[j] == m);
+      if (hit) sel = 64 * j + __builtin_ctzll(hit);
+    }
+    if ((sel & 63) == lane) {
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
-        if (lane + 64 * j == sel_e) key[j] = 0u;
+        if (j == (sel >> 6)) key[j] = 0u;
     }
+    const float sel_v = key_float(m);
     if (k == 0) top_v = sel_v;
     if (lane == k) {
       my_v = sel_v;
-      my_e = sel_e;
+      my_e = sel;
     }
   }
   // Softmax over the selected logits (renorm) or over all E, the largest
@@ -252,26 +243,6 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ log
 // one launch would need a device-scope fence per block, which on this chip
 // writes back the issuing XCD's L2 and costs far more than a launch.)
 
-// Exclusive scan of one value per thread over a 256-thread block; `scratch`
-// holds 4 ints.  Also returns the block total.
-MOE_DEV int scan256(int v, int *scratch, int &total) {
-  const int lane = __lane_id();
-  const int wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
-  if (lane == 63) scratch[wave] = inc;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += scratch[w];
-  total = scratch[0] + scratch[1] + scratch[2] + scratch[3];
-  __syncthreads();
-  return before + inc - v;
-}
-
 __global__ void __launch_bounds__(256) route_partial_kernel(RouteFusedArgs a) {
   extern __shared__ float4 smem_route[];
   const int wave = threadIdx.x >> 6;
@@ -283,16 +254,45 @@ __global__ void __launch_bounds__(256) route_partial_kernel(RouteFusedArgs a) {
   float *wr_l = reinterpret_cast<float *>(smem_route);        // [4][Hs]
   uint16_t *xs = reinterpret_cast<uint16_t *>(wr_l + 4 * Hs);  // [T][Hs + 8]
   stage_router_slice(a.router_w, a.x, E, H, Hs, e - wave, h0, 0, T, wr_l, xs);
-  __syncthreads();
+  lds_barrier();
   const float p = slice_partial(wr_l + wave * Hs, xs, Hs, T, e < E);
   if (lane < T && e < E) a.part[(static_cast<size_t>(slice) * T + lane) * E + e] = p;
 }
 
-// One block: logits from the partial sums, top-k per token, permutation.
+// Exclusive scan of one value per thread over the block (up to 16 waves);
+// `scratch` holds 16 ints.  Also returns the block total.
+MOE_DEV int block_scan(int v, int *scratch, int &total) {
+  const int lane = __lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  lds_barrier();
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int x = scratch[w];
+    before += w < wave ? x : 0;
+    all += x;
+  }
+  total = all;
+  lds_barrier();
+  return before + inc - v;
+}
+
+// One block of kSelectThreads: wave t adds token t's partial logits in
+// order and selects its top-k; then the permutation of the T*K pairs
+// (thread = expert for the counts and offsets, thread = pair for the rows).
+constexpr int kSelectThreads = 1024;
+
 template <int NPL>
-__global__ void __launch_bounds__(256) route_select_kernel(RouteFusedArgs a) {
+__global__ void __launch_bounds__(kSelectThreads) route_select_kernel(RouteFusedArgs a) {
   extern __shared__ float4 smem_route[];
-  __shared__ int scan_scratch[4];
+  __shared__ int scan_scratch[16];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -301,22 +301,37 @@ __global__ void __launch_bounds__(256) route_select_kernel(RouteFusedArgs a) {
   int32_t *ids_l = reinterpret_cast<int32_t *>(smem_route);  // [TK]
   float *w_l = reinterpret_cast<float *>(ids_l + TK);         // [TK]
   int32_t *cnt = reinterpret_cast<int32_t *>(w_l + TK);       // [E]
-  int32_t *off = cnt + E;                                     // [E]
-  for (int i = tid; i < E; i += 256) cnt[i] = 0;
-  for (int t = wave; t < T; t += 4) {
+  if (tid < E) cnt[tid] = 0;
+  if (wave < T) {
+    const int t = wave;
+    // the partials of four slices at a time as independent loads, then
+    // their sums in slice order
+    const float *__restrict__ part = a.part;
+    float acc[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float pv[NPL][4];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ex = lane + 64 * j;
+          pv[j][q] = (ex < E && s0 + q < S) ? part[(static_cast<size_t>(s0 + q) * T + t) * E + ex] : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (s0 + q < S) acc[j] += pv[j][q];
+    }
     float v[NPL];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int ex = lane + 64 * j;
-      float val = -INFINITY;
-      if (ex < E) {
-        float sum = 0.f;
-        for (int sl = 0; sl < S; ++sl) sum += a.part[(static_cast<size_t>(sl) * T + t) * E + ex];
-        sum = sum + (a.router_bias ? a.router_bias[ex] : 0.f);
-        if (a.logits) a.logits[static_cast<size_t>(t) * E + ex] = sum;
-        val = (sum != sum) ? -INFINITY : sum;  // NaN never outranks a number
-      }
-      v[j] = val;
+      const float sum = acc[j] + (a.router_bias && ex < E ? a.router_bias[ex] : 0.f);
+      v[j] = (ex < E && sum == sum) ? sum : -INFINITY;  // NaN never outranks a number
+      if (a.logits && ex < E) a.logits[static_cast<size_t>(t) * E + ex] = sum;
     }
     int my_e;
     float my_w;
@@ -329,45 +344,33 @@ __global__ void __launch_bounds__(256) route_select_kernel(RouteFusedArgs a) {
       w_l[p] = my_w;
     }
   }
-  __syncthreads();
-  for (int p = tid; p < TK; p += 256) atomicAdd(&cnt[ids_l[p]], 1);
-  __syncthreads();
-  // thread tid owns experts [4 tid, 4 tid + 4)
-  int c4[4], n_here = 0, nz_here = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ex = 4 * tid + i;
-    c4[i] = ex < E ? cnt[ex] : 0;
-    n_here += c4[i];
-    nz_here += c4[i] > 0;
-  }
+  lds_barrier();
+  if (tid < TK) atomicAdd(&cnt[ids_l[tid]], 1);
+  lds_barrier();
+  const int c = tid < E ? cnt[tid] : 0;
   int total = 0, n_act = 0;
-  int base = scan256(n_here, scan_scratch, total);
-  int abase = scan256(nz_here, scan_scratch, n_act);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ex = 4 * tid + i;
-    if (ex < E) {
-      off[ex] = base;
-      a.counts[ex] = c4[i];
-      a.offsets[ex] = base;
-      if (c4[i] > 0) a.active[abase++] = ex;
-    }
-    base += c4[i];
+  const int base = block_scan(c, scan_scratch, total);
+  const int abase = block_scan(c > 0 ? 1 : 0, scan_scratch, n_act);
+  if (tid < E) {
+    a.counts[tid] = c;
+    a.offsets[tid] = base;
+    if (c > 0) a.active[abase] = tid;
   }
   if (tid == 0) {
     a.offsets[E] = total;
     *a.n_active = n_act;
   }
-  __syncthreads();
-  for (int p = tid; p < TK; p += 256) {
-    const int ex = ids_l[p];
+  lds_barrier();          // every thread has read its count
+  if (tid < E) cnt[tid] = base;  // cnt now holds the offsets
+  lds_barrier();
+  if (tid < TK) {
+    const int ex = ids_l[tid];
     int r = 0;
-    for (int q = 0; q < p; ++q) r += ids_l[q] == ex;
-    const int pos = off[ex] + r;
-    a.row_tok[pos] = p / K;
-    a.row_w[pos] = w_l[p];
-    a.inv_pos[p] = pos;
+    for (int q = 0; q < tid; ++q) r += ids_l[q] == ex;
+    const int pos = cnt[ex] + r;
+    a.row_tok[pos] = tid / K;
+    a.row_w[pos] = w_l[tid];
+    a.inv_pos[tid] = pos;
   }
 }
 
@@ -376,16 +379,16 @@ hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
   route_partial_kernel<<<groups * a.S, 256, router_slice_lds_bytes(a.Hs, a.T), s>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds = static_cast<size_t>(a.T) * a.K * 8 + static_cast<size_t>(a.E) * 8;
+  const size_t lds = static_cast<size_t>(a.T) * a.K * 8 + static_cast<size_t>(a.E) * 4;
   const int npl = (a.E + 63) / 64;
   if (npl <= 1)
-    route_select_kernel<1><<<1, 256, lds, s>>>(a);
+    route_select_kernel<1><<<1, kSelectThreads, lds, s>>>(a);
   else if (npl <= 2)
-    route_select_kernel<2><<<1, 256, lds, s>>>(a);
+    route_select_kernel<2><<<1, kSelectThreads, lds, s>>>(a);
   else if (npl <= 4)
-    route_select_kernel<4><<<1, 256, lds, s>>>(a);
+    route_select_kernel<4><<<1, kSelectThreads, lds, s>>>(a);
   else
-    route_select_kernel<16><<<1, 256, lds, s>>>(a);
+    route_select_kernel<16><<<1, kSelectThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 
