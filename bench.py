@@ -50,6 +50,24 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of a stage's kernel from the committed counter
+    runs (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a
+    plain copy of known size), or None when there is no such run or the
+    kernel's source has changed since it was taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+                return None
+    except (OSError, ValueError, KeyError):
+        return None
+    kernel = {"gateup": "gateup_mfma_kernel", "down": "down_mfma_kernel"}[stage]
+    return rec.get("bytes_per_launch", {}).get(workload, {}).get(kernel)
+
+
 def expert_bytes(fmt, H, F):
     """Bytes of one expert's gate+up and down weights and scales."""
     if fmt == 1:
@@ -123,7 +141,22 @@ def main():
     ap.add_argument("--ring", type=int, default=40, help="distinct layer instances (decode workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (20 times), the known-size reference for "
+                         "the HBM byte counters, and exit")
     args = ap.parse_args()
+
+    if args.calibrate_copy_mib:
+        import torch
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 20}), flush=True)
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (expert-parallel sharding is a "
@@ -308,7 +341,8 @@ def main():
                    "distinct_layer_instances": len(dev_layers),
                    "unique_experts_per_call": U, "layer_GBps": layer_bytes / (ms_per_step / n_calls_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.workload, dom) if T <= 16 else None,
                      "kernel": dom, "kernel_us": dom_us, "kernel_bytes": dom_bytes,
                      "stage_us": stage_us},
         "cpu_baseline": cpu,

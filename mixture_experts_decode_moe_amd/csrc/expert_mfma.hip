@@ -245,6 +245,7 @@ MOE_DEV size_t mrow_act(const FfnArgs &a, const MUnit &u, int r) {
 // are looked up once into an LDS table, and each item's weights are
 // requested while the previous item is computed and reduced.
 constexpr int kGuTable = 128;  // most items one block takes
+constexpr int kGuGroup = 4;    // items reduced together
 
 template <int FMT, int JW>
 struct GuWeights {
@@ -334,7 +335,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   using Vec = typename Fm::Vec;
   constexpr bool kInt4 = FMT == MOE_W_INT4_B32;
   extern __shared__ uint4 xs_lds[];  // [T][H/8 + 1] 16-byte pieces of x
-  __shared__ f32x4_t red[kGuMaxWaves][64];
+  __shared__ f32x4_t red[kGuGroup][kGuMaxWaves][64];  // partial tiles of a group of items
   __shared__ int tab[kGuTable][4];   // e, r0, n (<= 16), f0
   __shared__ int toks[kGuTable][16];
   __shared__ uint32_t act_st[NI][16][8];  // SwiGLU outputs of a chunk: bf16 hi | lo << 16
@@ -419,52 +420,61 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
       const int it = c0 + i < my_items ? c0 + i : c0;
       gu_load<FMT, JW>(a, tab[it][0], tab[it][3], wave, n, g, w[i]);
     }
+    // groups of kGuGroup items: every wave's partial tiles of the group go to
+    // LDS, then one pass adds them and applies SwiGLU (two barriers a group)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int it = c0 + i;
-      if (it < my_items) {
-        const int e = tab[it][0], nrows = tab[it][2];
+    for (int g0 = 0; g0 < NI; g0 += kGuGroup) {
 #pragma unroll
-        for (int jj = 0; jj < JW; ++jj) xpose4(w[i].w[jj]);
-        const bool mv = n < nrows;
-        const uint16_t *xrow = reinterpret_cast<const uint16_t *>(xs_lds + toks[it][n] * xstride);
-        f32x4_t acc = zero4, corr = zero4;
+      for (int j = 0; j < kGuGroup; ++j) {
+        const int i = g0 + j;
+        const int it = c0 + i;
+        if (i < NI && it < my_items) {
+          const int nrows = tab[it][2];
 #pragma unroll
-        for (int jj = 0; jj < JW; ++jj)
+          for (int jj = 0; jj < JW; ++jj) xpose4(w[i].w[jj]);
+          const bool mv = n < nrows;
+          const uint16_t *xrow = reinterpret_cast<const uint16_t *>(xs_lds + toks[it][n] * xstride);
+          f32x4_t acc = zero4, corr = zero4;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            // staged x is already in operand order
-            const Vec xa = mv ? Fm::a_plane(xrow, 4 * (wave * JW + jj) + p, g) : Fm::zero();
-            if constexpr (kInt4) {
-              // per block: -136 * sum(x) as the accumulator input, then the scale
-              const f32x4_t c0v = Fm::mfma(xa, cvec, zero4);
-              const f32x4_t c = Fm::mfma(xa, Fm::b_w(word(w[i].w[jj], p)), c0v);
-              acc = fma4(scale4(w[i].s[jj][0], w[i].s[jj][1], p), c, acc);
-            } else {
-              acc = Fm::mfma(xa, Fm::b_w(word(w[i].w[jj], p)), acc);
-              corr = Fm::mfma(xa, cvec, corr);
+          for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              // staged x is already in operand order
+              const Vec xa = mv ? Fm::a_plane(xrow, 4 * (wave * JW + jj) + p, g) : Fm::zero();
+              if constexpr (kInt4) {
+                // per block: -136 * sum(x) as the accumulator input, then the scale
+                const f32x4_t c0v = Fm::mfma(xa, cvec, zero4);
+                const f32x4_t c = Fm::mfma(xa, Fm::b_w(word(w[i].w[jj], p)), c0v);
+                acc = fma4(scale4(w[i].s[jj][0], w[i].s[jj][1], p), c, acc);
+              } else {
+                acc = Fm::mfma(xa, Fm::b_w(word(w[i].w[jj], p)), acc);
+                corr = Fm::mfma(xa, cvec, corr);
+              }
             }
-          }
-        if constexpr (!kInt4) acc = (acc + corr) * w[i].rs;
-        red[wave][lane] = acc;
-        lds_barrier();
-        // wave m adds token row m's partial sums (lanes 0-7: the gate and
-        // up columns f0 + lane) in wave order and keeps the SwiGLU output
-        if (wave < nrows && lane < 8) {
-          const int src = 16 * (wave >> 2) + lane, r = wave & 3;
+          if constexpr (!kInt4) acc = (acc + corr) * w[i].rs;
+          red[j][wave][lane] = acc;
+        }
+      }
+      lds_barrier();
+      // thread (j, m, f): token row m of item g0 + j, gate and up columns
+      // f0 + f and their 8 + f partner, added in wave order
+      if (tid < kGuGroup * 128) {
+        const int j = tid >> 7, m = (tid >> 3) & 15, f = tid & 7;
+        const int i = g0 + j, it = c0 + i;
+        if (i < NI && it < my_items && m < tab[it][2]) {
+          const int src = 16 * (m >> 2) + f, r = m & 3;
           float gv = 0.f, uv = 0.f;
           for (int ww = 0; ww < KS; ++ww) {
-            gv += red[ww][src][r];
-            uv += red[ww][src + 8][r];
+            gv += red[j][ww][src][r];
+            uv += red[j][ww][src + 8][r];
           }
           const float v = gv / (1.f + expf(-gv)) * uv;
           const uint16_t hi = f32_to_bf16_rne(v);
           const uint16_t lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
-          act_st[i][wave][lane] = static_cast<uint32_t>(hi) | (static_cast<uint32_t>(lo) << 16);
+          act_st[i][m][f] = static_cast<uint32_t>(hi) | (static_cast<uint32_t>(lo) << 16);
         }
-        (void)e;
-        lds_barrier();
       }
+      lds_barrier();
     }
     // the chunk's SwiGLU rows to global memory: thread (i, m, f)
     if (tid < NI * 128) {
@@ -636,7 +646,10 @@ static int block_k(int fmt) { return fmt == MOE_W_INT4_B32 ? 32 : 16; }
 
 bool mfma_decode_ok(const FfnArgs &a) {
   int jw, ks;
-  return (a.fmt == MOE_W_INT4_B32 || a.fmt == MOE_W_INT8_ROW) && a.T <= kFusedTokens &&
+  // staged x plus the gate/up kernel's fixed LDS (partial tiles, item
+  // table, SwiGLU staging) must fit one compute unit's 160 KiB
+  const size_t lds = static_cast<size_t>(a.T) * (a.H / 8 + 1) * 16 + 80 * 1024;
+  return (a.fmt == MOE_W_INT4_B32 || a.fmt == MOE_W_INT8_ROW) && a.T <= kFusedTokens && lds <= 160 * 1024 &&
          (a.Fs == 0 || a.Fs == a.F) && split_k(a.H, block_k(a.fmt), kGuMaxWaves, jw, ks) &&
          split_k(a.F, block_k(a.fmt), kDnMaxWaves, jw, ks);
 }
