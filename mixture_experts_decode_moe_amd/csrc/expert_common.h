@@ -141,5 +141,8 @@ hipError_t launch_down_items(const FfnArgs &a, hipStream_t s);
 bool mfma_decode_ok(const FfnArgs &a);
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t s);
 hipError_t launch_down_mfma(const FfnArgs &a, hipStream_t s);
+bool prefill_ok(const FfnArgs &a);
+hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s);
+hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s);
 
 }  // namespace moe

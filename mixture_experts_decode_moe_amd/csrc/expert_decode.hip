@@ -473,11 +473,17 @@ hipError_t launch_down_items(const FfnArgs &a, hipStream_t s) {
   return launch_down_fmt<MOE_W_INT8_ROW>(a, s);
 }
 
+// Gate/up and down always take the same family (the SwiGLU rows' format
+// differs between them).
 hipError_t launch_gateup(const FfnArgs &a, hipStream_t s) {
-  return mfma_decode_ok(a) ? launch_gateup_mfma(a, s) : launch_gateup_items(a, s);
+  if (mfma_decode_ok(a)) return launch_gateup_mfma(a, s);
+  if (prefill_ok(a)) return launch_gateup_prefill(a, s);
+  return launch_gateup_items(a, s);
 }
 hipError_t launch_down(const FfnArgs &a, hipStream_t s) {
-  return mfma_decode_ok(a) ? launch_down_mfma(a, s) : launch_down_items(a, s);
+  if (mfma_decode_ok(a)) return launch_down_mfma(a, s);
+  if (prefill_ok(a)) return launch_down_prefill(a, s);
+  return launch_down_items(a, s);
 }
 
 }  // namespace moe

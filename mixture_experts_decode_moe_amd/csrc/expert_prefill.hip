@@ -1,0 +1,449 @@
+// Expert FFN for large batches (prefill chunks), int4 weights: grouped
+// GEMMs on the bf16 matrix cores.
+//
+// Which path runs depends on how many rows each expert serves; the pages
+// measure the crossover from per-row kernels to a dense contraction in rows
+// per expert ("Strata on an Intel Arc", prompt processing).  A prefill chunk
+// gives every expert tens of rows (2048 tokens x 8 slots over 256 experts is
+// 64 on average), enough to tile each expert's rows as the M dimension of a
+// GEMM and reuse every weight tile across them.
+//
+// Arithmetic as in the decode kernels (expert_mfma.hip): the int4 weights
+// enter the MFMA as the exact bfloat16 values 128 + nibble = q + 136, the
+// other operand is exact (x in bf16; the SwiGLU output as bf16 hi + lo), the
+// fp32 accumulator input of each 32-element block is -136 * sum(other
+// operand over the block) (computed while the operand tile is staged), and
+// the block's fp16 scale is applied with an fp32 FMA.
+//
+// Tiles.  An item is (unit, 64 rows, 64 output columns); a block of 4 waves
+// works on it, wave w owning the 16 columns 16w..16w+15 of all 64 rows (four
+// 16x16 MFMA tiles along M).  Gate/up items hold 64 SwiGLU columns, i.e. 64
+// gate and the matching 64 up columns, so wave w has both halves of its
+// SwiGLU columns in registers.  The reduction dimension advances in steps
+// of 128 (four 32-element blocks): the A tile (the unit's rows, gathered
+// for gate/up) is double-buffered in LDS with its block sums, the weight
+// chunks of the next step are loaded into registers while the current step
+// is multiplied.  Blocks loop over the items; units and their row tiles are
+// enumerated once per block into an LDS table.
+#include <math.h>
+
+#include "mfma_common.h"
+
+namespace moe {
+
+constexpr int kPfRows = 64;      // rows per item
+constexpr int kPfCols = 64;      // output columns per item (gate/up: SwiGLU columns)
+constexpr int kPfMaxUnits = 1040;  // shared expert + up to 1024 routed + slack
+constexpr int kPfThreads = 256;
+
+// Unit u of the call: the shared expert first (when present), then the
+// routed active experts in order.
+struct PfUnit {
+  int e;   // expert index (-1: shared)
+  int r0;  // first row
+  int n;   // rows
+};
+
+MOE_DEV PfUnit pf_unit(const FfnArgs &a, int u) {
+  PfUnit x;
+  if (a.Fs > 0) {
+    if (u == 0) {
+      x.e = -1;
+      x.r0 = 0;
+      x.n = a.T;
+      return x;
+    }
+    --u;
+  }
+  if (a.offsets) {
+    x.e = a.active[u];
+    x.r0 = a.offsets[x.e];
+    x.n = a.offsets[x.e + 1] - x.r0;
+  } else {
+    x.e = 0;
+    x.r0 = 0;
+    x.n = a.n_rows;
+  }
+  return x;
+}
+
+// Fills pre[u] = first row tile of unit u (exclusive prefix of the row
+// tiles), pre[n_units] = total; returns the number of units.
+MOE_DEV int pf_tiles(const FfnArgs &a, int *pre, int *scratch) {
+  const int n_units = (a.Fs > 0 ? 1 : 0) + routed_units(a);
+  const int tid = threadIdx.x;
+  constexpr int kPer = (kPfMaxUnits + kPfThreads - 1) / kPfThreads;
+  int cnt[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int u = tid * kPer + i;
+    int c = 0;
+    if (u < n_units) {
+      const PfUnit x = pf_unit(a, u);
+      c = x.n > 0 ? (x.n + kPfRows - 1) / kPfRows : 0;
+    }
+    cnt[i] = c;
+    mine += c;
+  }
+  // block exclusive scan of the per-thread totals
+  const int lane = tid & 63, wave = tid >> 6;
+  int inc = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  lds_barrier();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += scratch[w];
+  base += inc - mine;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int u = tid * kPer + i;
+    if (u <= n_units) pre[u] = base;
+    base += cnt[i];
+  }
+  lds_barrier();
+  return n_units;
+}
+
+// Unit of row tile j (binary search in the prefix table).
+MOE_DEV int pf_find(const int *pre, int n_units, int j) {
+  int lo = 0, hi = n_units - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= j)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// LDS tile of the A operand: 64 rows x one k-step, 16-byte pieces (8 bf16 in
+// operand order), rows padded by one piece; plus -136 * block sums [4][64].
+template <int PLANES>
+struct PfTile {
+  uint4 a[PLANES][kPfRows][17];
+  float corr[4][kPfRows];
+};
+
+// ------------------------------------------------------------------ gate/up
+
+__global__ void __launch_bounds__(kPfThreads) gateup_prefill_kernel(FfnArgs a) {
+  __shared__ PfTile<1> tile[2];
+  __shared__ int pre[kPfMaxUnits + 1];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int H = a.H, T = a.T;
+  const int n_units = pf_tiles(a, pre, scratch);
+  const int col_groups = a.F / kPfCols;  // the shared expert has Fs == F on this path
+  const int n_items = pre[n_units] * col_groups;
+  const int steps = H / 128;
+  const int nblk = H / 32;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int j = item / col_groups;
+    const int cg = item - j * col_groups;
+    const int u = pf_find(pre, n_units, j);
+    const PfUnit un = pf_unit(a, u);
+    const int m0 = (j - pre[u]) * kPfRows;  // first row of the tile inside the unit
+    const int rows = min(kPfRows, un.n - m0);
+    const bool shared = un.e < 0;
+    const int F = shared ? a.Fs : a.F;
+    const int f = cg * kPfCols + 16 * wave + n;  // this lane's SwiGLU column
+    const size_t wrow = static_cast<size_t>(shared ? 0 : un.e) * F + f;
+    gchar_t *gq = uniform_gptr(shared ? a.sgq : a.gq) + wrow * nblk * 16;
+    gchar_t *uq = uniform_gptr(shared ? a.suq : a.uq) + wrow * nblk * 16;
+    gu32_t *gs = reinterpret_cast<gu32_t *>(uniform_gptr(shared ? a.sgs : a.gs) + wrow * nblk * 2);
+    gu32_t *us = reinterpret_cast<gu32_t *>(uniform_gptr(shared ? a.sus : a.us) + wrow * nblk * 2);
+
+    // A staging: thread t owns pieces t + 256 i (i < 4): row p / 16, piece p % 16
+    int tok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 4) + 16 * i;
+      int t = 0;
+      if (r < rows) {
+        const int rr = un.r0 + m0 + r;
+        t = shared ? rr : (a.row_tok ? a.row_tok[rr] : rr);
+        t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+      }
+      tok[i] = t;
+    }
+    const int pc = tid & 15;
+    auto load_a = [&](int s, uint4 (&v)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        v[i] = r < rows ? reinterpret_cast<const uint4 *>(a.x + static_cast<size_t>(tok[i]) * H)[16 * s + pc]
+                        : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store_a = [&](int buf, const uint4 (&v)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        const u32x4_t pp = pair_permute(v[i]);
+        tile[buf].a[0][r][pc] = make_uint4(pp.x, pp.y, pp.z, pp.w);
+        float sum = 0.f;
+        const uint32_t d[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum += bf16_lo(d[q]) + bf16_hi(d[q]);
+        // four consecutive lanes hold one 32-element block of the row
+        sum += dpp_f32<0xB1>(sum);
+        sum += dpp_f32<0x4E>(sum);
+        if ((pc & 3) == 0) tile[buf].corr[pc >> 2][r] = -136.f * sum;
+      }
+    };
+    auto load_b = [&](int s, uint4 &wg, uint4 &wu, uint32_t (&sg)[2], uint32_t (&su)[2]) {
+      wg = load_stream16_g(gq + 16 * (4 * s + g));
+      wu = load_stream16_g(uq + 16 * (4 * s + g));
+      sg[0] = gs[2 * s];
+      sg[1] = gs[2 * s + 1];
+      su[0] = us[2 * s];
+      su[1] = us[2 * s + 1];
+    };
+
+    f32x4_t accg[4], accu[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) accg[mt] = accu[mt] = zero4;
+    uint4 av[4];
+    uint4 wg, wu;
+    uint32_t sg[2], su[2];
+    load_a(0, av);
+    load_b(0, wg, wu, sg, su);
+    store_a(0, av);
+    lds_barrier();
+    for (int s = 0; s < steps; ++s) {
+      const int buf = s & 1;
+      uint4 nwg, nwu;
+      uint32_t nsg[2], nsu[2];
+      const bool more = s + 1 < steps;
+      if (more) {
+        load_a(s + 1, av);
+        load_b(s + 1, nwg, nwu, nsg, nsu);
+      }
+      xpose4(wg);
+      xpose4(wu);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const u32x4_t bg = magic_pairs(word(wg, p));
+        const u32x4_t bu = magic_pairs(word(wu, p));
+        const float scg = scale4(sg[0], sg[1], p), scu = scale4(su[0], su[1], p);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint4 av4 = tile[buf].a[0][16 * mt + n][4 * p + g];
+          const u32x4_t A = {av4.x, av4.y, av4.z, av4.w};
+          const float4 c4 = *reinterpret_cast<const float4 *>(&tile[buf].corr[p][16 * mt + 4 * g]);
+          const f32x4_t C = {c4.x, c4.y, c4.z, c4.w};
+          accg[mt] = fma4(scg, mfma_bf16(A, bg, C), accg[mt]);
+          accu[mt] = fma4(scu, mfma_bf16(A, bu, C), accu[mt]);
+        }
+      }
+      if (more) {
+        store_a(buf ^ 1, av);
+        wg = nwg;
+        wu = nwu;
+        sg[0] = nsg[0];
+        sg[1] = nsg[1];
+        su[0] = nsu[0];
+        su[1] = nsu[1];
+      }
+      lds_barrier();
+    }
+    // SwiGLU; lane (n, g) holds rows 16 mt + 4 g + i of column f
+    const int pos = act_pos<MOE_W_INT4_B32>(f);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * g + i;
+        if (r < rows) {
+          const float gv = accg[mt][i], uv = accu[mt][i];
+          const float v = gv / (1.f + expf(-gv)) * uv;
+          const uint16_t hi = f32_to_bf16_rne(v);
+          const uint16_t lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
+          const int rr = m0 + r;
+          const size_t off = shared ? static_cast<size_t>(a.n_rows) * a.F + static_cast<size_t>(rr) * a.Fs
+                                    : static_cast<size_t>(un.r0 + rr) * a.F;
+          uint16_t *arow = reinterpret_cast<uint16_t *>(a.act + off);
+          arow[pos] = hi;
+          arow[F + pos] = lo;
+        }
+      }
+  }
+}
+
+// --------------------------------------------------------------------- down
+
+__global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
+  __shared__ PfTile<2> tile[2];
+  __shared__ int pre[kPfMaxUnits + 1];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int H = a.H;
+  const int n_units = pf_tiles(a, pre, scratch);
+  const int col_groups = H / kPfCols;
+  const int n_items = pre[n_units] * col_groups;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int j = item / col_groups;
+    const int cg = item - j * col_groups;
+    const int u = pf_find(pre, n_units, j);
+    const PfUnit un = pf_unit(a, u);
+    const int m0 = (j - pre[u]) * kPfRows;
+    const int rows = min(kPfRows, un.n - m0);
+    const bool shared = un.e < 0;
+    const int F = shared ? a.Fs : a.F;
+    const int steps = F / 128;
+    const int nblk = F / 32;
+    const int h = cg * kPfCols + 16 * wave + n;  // this lane's output column
+    const size_t wrow = static_cast<size_t>(shared ? 0 : un.e) * H + h;
+    gchar_t *dq = uniform_gptr(shared ? a.sdq : a.dq) + wrow * nblk * 16;
+    gu32_t *ds = reinterpret_cast<gu32_t *>(uniform_gptr(shared ? a.sds : a.ds) + wrow * nblk * 2);
+
+    // A staging: thread t owns pieces t + 256 i (i < 4) of both planes
+    const int pc = tid & 15;
+    auto arow = [&](int r) -> const uint4 * {
+      const int rr = m0 + r;
+      const size_t off = shared ? static_cast<size_t>(a.n_rows) * a.F + static_cast<size_t>(rr) * a.Fs
+                                : static_cast<size_t>(un.r0 + rr) * a.F;
+      return reinterpret_cast<const uint4 *>(a.act + off);
+    };
+    auto load_a = [&](int s, uint4 (&vh)[4], uint4 (&vl)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        const uint4 *p = arow(r < rows ? r : 0);
+        vh[i] = r < rows ? p[16 * s + pc] : make_uint4(0, 0, 0, 0);
+        vl[i] = r < rows ? p[F / 8 + 16 * s + pc] : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store_a = [&](int buf, const uint4 (&vh)[4], const uint4 (&vl)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 4) + 16 * i;
+        tile[buf].a[0][r][pc] = vh[i];
+        tile[buf].a[1][r][pc] = vl[i];
+        float sum = 0.f;
+        const uint32_t d[8] = {vh[i].x, vh[i].y, vh[i].z, vh[i].w, vl[i].x, vl[i].y, vl[i].z, vl[i].w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sum += bf16_lo(d[q]) + bf16_hi(d[q]);
+        sum += dpp_f32<0xB1>(sum);
+        sum += dpp_f32<0x4E>(sum);
+        if ((pc & 3) == 0) tile[buf].corr[pc >> 2][r] = -136.f * sum;
+      }
+    };
+    auto load_b = [&](int s, uint4 &w, uint32_t (&sc)[2]) {
+      w = load_stream16_g(dq + 16 * (4 * s + g));
+      sc[0] = ds[2 * s];
+      sc[1] = ds[2 * s + 1];
+    };
+
+    f32x4_t acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = zero4;
+    uint4 vh[4], vl[4];
+    uint4 w;
+    uint32_t sc[2];
+    load_a(0, vh, vl);
+    load_b(0, w, sc);
+    store_a(0, vh, vl);
+    lds_barrier();
+    for (int s = 0; s < steps; ++s) {
+      const int buf = s & 1;
+      uint4 nw;
+      uint32_t nsc[2];
+      const bool more = s + 1 < steps;
+      if (more) {
+        load_a(s + 1, vh, vl);
+        load_b(s + 1, nw, nsc);
+      }
+      xpose4(w);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const u32x4_t b = magic_pairs(word(w, p));
+        const float scp = scale4(sc[0], sc[1], p);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint4 h4 = tile[buf].a[0][16 * mt + n][4 * p + g];
+          const uint4 l4 = tile[buf].a[1][16 * mt + n][4 * p + g];
+          const u32x4_t Ah = {h4.x, h4.y, h4.z, h4.w}, Al = {l4.x, l4.y, l4.z, l4.w};
+          const float4 c4 = *reinterpret_cast<const float4 *>(&tile[buf].corr[p][16 * mt + 4 * g]);
+          const f32x4_t C = {c4.x, c4.y, c4.z, c4.w};
+          f32x4_t c = mfma_bf16(Ah, b, C);
+          c = mfma_bf16(Al, b, c);
+          acc[mt] = fma4(scp, c, acc[mt]);
+        }
+      }
+      if (more) {
+        store_a(buf ^ 1, vh, vl);
+        w = nw;
+        sc[0] = nsc[0];
+        sc[1] = nsc[1];
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * g + i;
+        if (r < rows) {
+          const int rr = m0 + r;
+          const int row = un.r0 + rr;
+          const float wgt = shared || !a.row_w ? 1.f : a.row_w[row];
+          const size_t orow = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(row);
+          a.rows_out[orow * H + h] = acc[mt][i] * wgt;
+        }
+      }
+  }
+}
+
+// ----------------------------------------------------------------- launches
+
+bool prefill_ok(const FfnArgs &a) {
+  const int units = (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1);
+  return a.fmt == MOE_W_INT4_B32 && a.T > kFusedTokens && (a.Fs == 0 || a.Fs == a.F) && a.H % 128 == 0 &&
+         a.F % 128 == 0 && a.F % kPfCols == 0 && a.H % kPfCols == 0 && units <= kPfMaxUnits;
+}
+
+static int pf_grid(int items_upper) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const int cap = 4 * cus;  // four resident blocks per compute unit
+  return items_upper < 1 ? 1 : (items_upper < cap ? items_upper : cap);
+}
+
+// Upper bound of the row tiles: every routed row tile plus one partial tile
+// per unit, plus the shared expert's.
+static int pf_tiles_upper(const FfnArgs &a) {
+  const int units = a.offsets ? a.max_units : 1;
+  return (a.n_rows + kPfRows - 1) / kPfRows + units + (a.Fs > 0 ? (a.T + kPfRows - 1) / kPfRows : 0);
+}
+
+hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
+  gateup_prefill_kernel<<<pf_grid(pf_tiles_upper(a) * (a.F / kPfCols)), kPfThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
+  down_prefill_kernel<<<pf_grid(pf_tiles_upper(a) * (a.H / kPfCols)), kPfThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe
