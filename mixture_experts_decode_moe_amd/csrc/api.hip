@@ -317,9 +317,23 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
   int32_t *ids = topk_ids ? topk_ids : w.ids;
   float *tw = topk_w ? topk_w : w.w;
 
+  const int32_t TK = T * K;
+  const bool has_shared = L->shared.n_experts == 1;
+  FfnArgs xa = ffn_args(L->routed, has_shared ? &L->shared : nullptr, H, x_bf16, T, TK);
+  xa.offsets = w.offsets;
+  xa.active = w.active;
+  xa.n_active = w.n_active;
+  xa.row_tok = w.row_tok;
+  xa.row_w = w.row_w;
+  xa.act = w.act;
+  xa.rows_out = w.rows_out;
+  xa.max_units = TK < E ? TK : E;
+
   hipError_t e;
   if (T <= kFusedTokens) {
-    // decode batch: router partials, then top-k and permutation in one block
+    // decode batch: the router's partial logits; the top-k and the
+    // permutation then run inside the gate/up kernel when it is the
+    // matrix-core one, else in one block of their own
     RouteFusedArgs fa{};
     fa.router_w = L->router_w;
     fa.router_bias = L->router_bias;
@@ -342,8 +356,10 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
     fa.active = w.active;
     fa.n_active = w.n_active;
     fa.row_w = w.row_w;
+    xa.route_here = (mfma_decode_ok(xa) && E <= 256) ? 1 : 0;
+    xa.route = fa;
     StageMark m(MOE_STAGE_ROUTE, s);
-    e = launch_route_fused(fa, s);
+    e = xa.route_here ? launch_route_partial(fa, s) : launch_route_fused(fa, s);
   } else {
     RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw};
     {
@@ -372,17 +388,6 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
 
-  const int32_t TK = T * K;
-  const bool has_shared = L->shared.n_experts == 1;
-  FfnArgs xa = ffn_args(L->routed, has_shared ? &L->shared : nullptr, H, x_bf16, T, TK);
-  xa.offsets = w.offsets;
-  xa.active = w.active;
-  xa.n_active = w.n_active;
-  xa.row_tok = w.row_tok;
-  xa.row_w = w.row_w;
-  xa.act = w.act;
-  xa.rows_out = w.rows_out;
-  xa.max_units = TK < E ? TK : E;
   {
     StageMark m(MOE_STAGE_GATEUP, s);
     e = launch_gateup(xa, s);

@@ -114,7 +114,8 @@ struct RouteFusedArgs {
   int32_t *counts, *offsets, *row_tok, *inv_pos, *active, *n_active;
   float *row_w;
 };
-hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s);
+hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s);    // partials + selection
+hipError_t launch_route_partial(const RouteFusedArgs &a, hipStream_t s);  // partials only
 __host__ __device__ inline int route_fused_slice(int H) { return H % 512 == 0 ? 512 : 256; }
 
 struct PermuteArgs {
@@ -148,8 +149,16 @@ struct FfnArgs {
   float *act;               // [n_rows*F + T*Fs]
   float *rows_out;          // [n_rows + (Fs ? T : 0)][H]
   int32_t max_units;        // upper bound of routed units (grid sizing)
+  // decode layer calls (E <= 256): the gate/up kernel routes the batch
+  // itself from the router's partial logits and its block 0 publishes the
+  // routing (the
+  // offsets, active, n_active, row_tok and row_w above point at the same
+  // buffers for the kernels that follow)
+  int32_t route_here;
+  RouteFusedArgs route;
 };
 hipError_t launch_gateup(const FfnArgs &a, hipStream_t s);
+bool mfma_decode_ok(const FfnArgs &a);  // the decode matrix-core kernels take this call
 hipError_t launch_down(const FfnArgs &a, hipStream_t s);
 
 struct CombineArgs {

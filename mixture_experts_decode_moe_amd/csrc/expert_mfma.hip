@@ -47,6 +47,7 @@
 #include <math.h>
 
 #include "mfma_common.h"
+#include "route_common.h"
 
 namespace moe {
 
@@ -198,7 +199,58 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   const int n = lane & 15;
   const int g = lane >> 4;
   const int H = a.H, T = a.T;
-  const int U = routed_units(a);
+  const int pieces = H / 8;  // 16-byte pieces per x row
+  const int xstride = pieces + 1;
+  const Vec cvec = Fm::corr();
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  // the in-kernel routing's LDS shares the partial-tile buffer
+  RouteLds &L = *reinterpret_cast<RouteLds *>(&red[0][0][0]);
+  static_assert(sizeof(RouteLds) <= sizeof(red), "routing LDS must fit the partial-tile buffer");
+
+  auto stage_x = [&](int t0, int nthr) {  // threads t0.. stage the x rows in LDS
+    for (int base = tid - t0; base < T * pieces; base += nthr * kStageBatch) {
+      uint4 v[kStageBatch];
+#pragma unroll
+      for (int b = 0; b < kStageBatch; ++b) {
+        const int i = base + b * nthr;
+        v[b] = i < T * pieces ? reinterpret_cast<const uint4 *>(a.x)[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < kStageBatch; ++b) {
+        const int i = base + b * nthr;
+        if (i < T * pieces) {
+          const int t = i / pieces, k = i - t * pieces;
+          uint4 o = v[b];
+          if constexpr (kInt4) {
+            const u32x4_t pp = pair_permute(v[b]);
+            o = make_uint4(pp.x, pp.y, pp.z, pp.w);
+          }
+          xs_lds[t * xstride + k] = o;
+        }
+      }
+    }
+  };
+
+  int U;
+  uint4 xv[4];  // route_here: the first x pieces, requested before the routing
+  if (a.route_here) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = tid + b * blockDim.x;
+      xv[b] = i < T * pieces ? reinterpret_cast<const uint4 *>(a.x)[i] : make_uint4(0, 0, 0, 0);
+    }
+    // every block routes the batch (block 0 also publishes it)
+    const int npl = (a.route.E + 63) / 64;
+    if (npl <= 1)
+      route_in_block<1>(a.route, L, blockIdx.x == 0);
+    else if (npl <= 2)
+      route_in_block<2>(a.route, L, blockIdx.x == 0);
+    else
+      route_in_block<4>(a.route, L, blockIdx.x == 0);  // E <= 256 on this path
+    U = L.n_active;
+  } else {
+    U = routed_units(a);
+  }
   const int tiles_r = a.F / 8, tiles_s = a.Fs / 8;
   const int n_items = tiles_s + U * tiles_r;
   // block b owns the contiguous items [b C, b C + C) (C <= kGuTable)
@@ -206,14 +258,59 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   const int first = blockIdx.x * C;
   const int my_items = n_items > first ? min(C, n_items - first) : 0;
   if (my_items == 0) return;
-  const Vec cvec = Fm::corr();
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const int pieces = H / 8;  // 16-byte pieces per x row
-  const int xstride = pieces + 1;
 
-  // waves 0-1 look up the block's items (unit, rows, tokens; one thread per
-  // item, all in parallel) while the other waves stage the x rows in LDS
-  if (tid < kGuTable) {
+  if (a.route_here) {
+    // the item table from the routing in LDS, then the x rows
+    if (tid < my_items) {
+      const int i = first + tid;
+      int e, r0, nn, f0;
+      if (i < tiles_s) {
+        e = -1;
+        r0 = 0;
+        nn = T;
+        f0 = i * 8;
+      } else {
+        const int k = (i - tiles_s) / tiles_r;
+        f0 = (i - tiles_s - k * tiles_r) * 8;
+        e = L.active[k];
+        r0 = L.off[e];
+        nn = L.cnt[e];
+      }
+      nn = nn > 16 ? 16 : nn;
+      tab[tid][0] = e;
+      tab[tid][1] = r0;
+      tab[tid][2] = nn;
+      tab[tid][3] = f0;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) toks[tid][m] = m < nn ? (e < 0 ? m : L.row_tok[r0 + m]) : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = tid + b * blockDim.x;
+      if (i < T * pieces) {
+        const int t = i / pieces, k = i - t * pieces;
+        uint4 o = xv[b];
+        if constexpr (kInt4) {
+          const u32x4_t pp = pair_permute(xv[b]);
+          o = make_uint4(pp.x, pp.y, pp.z, pp.w);
+        }
+        xs_lds[t * xstride + k] = o;
+      }
+    }
+    if (T * pieces > 4 * static_cast<int>(blockDim.x)) {  // the rest of the rows
+      for (int base = tid + 4 * blockDim.x; base < T * pieces; base += blockDim.x) {
+        const int t = base / pieces, k = base - t * pieces;
+        uint4 o = reinterpret_cast<const uint4 *>(a.x)[base];
+        if constexpr (kInt4) {
+          const u32x4_t pp = pair_permute(o);
+          o = make_uint4(pp.x, pp.y, pp.z, pp.w);
+        }
+        xs_lds[t * xstride + k] = o;
+      }
+    }
+  } else if (tid < kGuTable) {
+    // waves 0-1 look up the block's items (unit, rows, tokens; one thread per
+    // item, all in parallel) while the other waves stage the x rows in LDS
     if (tid < my_items) {
       int e, r0, nn, f0;
       gu_item(a, first + tid, tiles_r, tiles_s, e, r0, nn, f0);
@@ -236,28 +333,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
       for (int m = 0; m < 16; ++m) toks[tid][m] = tk[m];
     }
   } else {
-    const int nthr = blockDim.x - kGuTable;
-    for (int base = tid - kGuTable; base < T * pieces; base += nthr * kStageBatch) {
-      uint4 v[kStageBatch];
-#pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
-        const int i = base + b * nthr;
-        v[b] = i < T * pieces ? reinterpret_cast<const uint4 *>(a.x)[i] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
-        const int i = base + b * nthr;
-        if (i < T * pieces) {
-          const int t = i / pieces, k = i - t * pieces;
-          uint4 o = v[b];
-          if constexpr (kInt4) {
-            const u32x4_t pp = pair_permute(v[b]);
-            o = make_uint4(pp.x, pp.y, pp.z, pp.w);
-          }
-          xs_lds[t * xstride + k] = o;
-        }
-      }
-    }
+    stage_x(kGuTable, blockDim.x - kGuTable);
   }
   lds_barrier();
 

@@ -12,7 +12,7 @@
 #include <float.h>
 #include <math.h>
 
-#include "common.h"
+#include "route_common.h"
 
 namespace moe {
 
@@ -124,84 +124,6 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restr
   if (e < E && lane < nt) logits[static_cast<size_t>(t0 + lane) * E + e] = total + (bias ? bias[e] : 0.f);
 }
 
-// Order-preserving map of a float onto uint32 (NaN must be excluded).
-MOE_DEV uint32_t float_key(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-MOE_DEV float key_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-template <int CTRL>
-MOE_DEV uint32_t dpp_u32(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
-}
-
-// Wave-wide maximum (uniform result).
-MOE_DEV uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
-  v = max(v, dpp_u32<0x140>(v));  // row_mirror
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
-}
-
-// Top-k of one token's logits held by a whole wave: lane l holds experts
-// l, l+64, ... in v[] (NaN already replaced by -inf, absent experts -inf).
-// Lane k < K receives round k's expert and routing weight.
-template <int NPL>
-MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t renorm, int &my_e, float &my_w) {
-  const int lane = __lane_id();
-  uint32_t key[NPL];  // 0 = used or absent
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) key[j] = (lane + 64 * j < E) ? float_key(v[j]) : 0u;
-  float top_v = 0.f;
-  float my_v = 0.f;  // lane k keeps round k's value and index
-  my_e = 0;
-  for (int k = 0; k < K; ++k) {
-    // the largest remaining key, then the lowest expert index holding it
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) m = max(m, key[j]);
-    m = wave_max_u32(m);
-    int sel = 0;
-#pragma unroll
-    for (int j = NPL - 1; j >= 0; --j) {
-      const uint64_t hit = __ballot(key[j] == m);
-      if (hit) sel = 64 * j + __builtin_ctzll(hit);
-    }
-    if ((sel & 63) == lane) {
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (j == (sel >> 6)) key[j] = 0u;
-    }
-    const float sel_v = key_float(m);
-    if (k == 0) top_v = sel_v;
-    if (lane == k) {
-      my_v = sel_v;
-      my_e = sel;
-    }
-  }
-  // Softmax over the selected logits (renorm) or over all E, the largest
-  // logit subtracted for range; sums in a fixed order.
-  const float mine = (lane < K) ? expf(my_v - top_v) : 0.f;
-  float denom;
-  if (renorm) {
-    denom = 0.f;
-    for (int k = 0; k < K; ++k) denom += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), k));
-  } else {
-    float part = 0.f;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      if (lane + 64 * j < E) part += expf(v[j] - top_v);
-    denom = sum64(part);
-  }
-  my_w = mine / denom;
-}
-
 // One wave per token.  Lane l holds experts l, l+64, ... (up to 16 each).
 template <int NPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int32_t T, int32_t E,
@@ -259,136 +181,34 @@ __global__ void __launch_bounds__(256) route_partial_kernel(RouteFusedArgs a) {
   if (lane < T && e < E) a.part[(static_cast<size_t>(slice) * T + lane) * E + e] = p;
 }
 
-// Exclusive scan of one value per thread over the block (up to 16 waves);
-// `scratch` holds 16 ints.  Also returns the block total.
-MOE_DEV int block_scan(int v, int *scratch, int &total) {
-  const int lane = __lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
-  if (lane == 63) scratch[wave] = inc;
-  lds_barrier();
-  int before = 0, all = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int x = scratch[w];
-    before += w < wave ? x : 0;
-    all += x;
-  }
-  total = all;
-  lds_barrier();
-  return before + inc - v;
-}
-
-// One block of kSelectThreads: wave t adds token t's partial logits in
-// order and selects its top-k; then the permutation of the T*K pairs
-// (thread = expert for the counts and offsets, thread = pair for the rows).
+// One block of kSelectThreads: the routing of a decode batch (top-k and
+// permutation) from the partial logits, published to global memory.
 constexpr int kSelectThreads = 1024;
 
 template <int NPL>
 __global__ void __launch_bounds__(kSelectThreads) route_select_kernel(RouteFusedArgs a) {
-  extern __shared__ float4 smem_route[];
-  __shared__ int scan_scratch[16];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int T = a.T, E = a.E, S = a.S, K = a.K;
-  const int TK = T * K;
-  int32_t *ids_l = reinterpret_cast<int32_t *>(smem_route);  // [TK]
-  float *w_l = reinterpret_cast<float *>(ids_l + TK);         // [TK]
-  int32_t *cnt = reinterpret_cast<int32_t *>(w_l + TK);       // [E]
-  if (tid < E) cnt[tid] = 0;
-  if (wave < T) {
-    const int t = wave;
-    // the partials of four slices at a time as independent loads, then
-    // their sums in slice order
-    const float *__restrict__ part = a.part;
-    float acc[NPL];
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      float pv[NPL][4];
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ex = lane + 64 * j;
-          pv[j][q] = (ex < E && s0 + q < S) ? part[(static_cast<size_t>(s0 + q) * T + t) * E + ex] : 0.f;
-        }
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (s0 + q < S) acc[j] += pv[j][q];
-    }
-    float v[NPL];
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int ex = lane + 64 * j;
-      const float sum = acc[j] + (a.router_bias && ex < E ? a.router_bias[ex] : 0.f);
-      v[j] = (ex < E && sum == sum) ? sum : -INFINITY;  // NaN never outranks a number
-      if (a.logits && ex < E) a.logits[static_cast<size_t>(t) * E + ex] = sum;
-    }
-    int my_e;
-    float my_w;
-    wave_topk<NPL>(v, E, K, a.renorm, my_e, my_w);
-    if (lane < K) {
-      const size_t p = static_cast<size_t>(t) * K + lane;
-      a.ids[p] = my_e;
-      a.w[p] = my_w;
-      ids_l[p] = my_e;
-      w_l[p] = my_w;
-    }
-  }
-  lds_barrier();
-  if (tid < TK) atomicAdd(&cnt[ids_l[tid]], 1);
-  lds_barrier();
-  const int c = tid < E ? cnt[tid] : 0;
-  int total = 0, n_act = 0;
-  const int base = block_scan(c, scan_scratch, total);
-  const int abase = block_scan(c > 0 ? 1 : 0, scan_scratch, n_act);
-  if (tid < E) {
-    a.counts[tid] = c;
-    a.offsets[tid] = base;
-    if (c > 0) a.active[abase] = tid;
-  }
-  if (tid == 0) {
-    a.offsets[E] = total;
-    *a.n_active = n_act;
-  }
-  lds_barrier();          // every thread has read its count
-  if (tid < E) cnt[tid] = base;  // cnt now holds the offsets
-  lds_barrier();
-  if (tid < TK) {
-    const int ex = ids_l[tid];
-    int r = 0;
-    for (int q = 0; q < tid; ++q) r += ids_l[q] == ex;
-    const int pos = cnt[ex] + r;
-    a.row_tok[pos] = tid / K;
-    a.row_w[pos] = w_l[tid];
-    a.inv_pos[tid] = pos;
-  }
+  __shared__ RouteLds L;
+  route_in_block<NPL>(a, L, true);
+}
+
+hipError_t launch_route_partial(const RouteFusedArgs &a, hipStream_t s) {
+  const int groups = (a.E + 3) / 4;
+  route_partial_kernel<<<groups * a.S, 256, router_slice_lds_bytes(a.Hs, a.T), s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
-  const int groups = (a.E + 3) / 4;
-  route_partial_kernel<<<groups * a.S, 256, router_slice_lds_bytes(a.Hs, a.T), s>>>(a);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_route_partial(a, s);
   if (err != hipSuccess) return err;
-  const size_t lds = static_cast<size_t>(a.T) * a.K * 8 + static_cast<size_t>(a.E) * 4;
   const int npl = (a.E + 63) / 64;
   if (npl <= 1)
-    route_select_kernel<1><<<1, kSelectThreads, lds, s>>>(a);
+    route_select_kernel<1><<<1, kSelectThreads, 0, s>>>(a);
   else if (npl <= 2)
-    route_select_kernel<2><<<1, kSelectThreads, lds, s>>>(a);
+    route_select_kernel<2><<<1, kSelectThreads, 0, s>>>(a);
   else if (npl <= 4)
-    route_select_kernel<4><<<1, kSelectThreads, lds, s>>>(a);
+    route_select_kernel<4><<<1, kSelectThreads, 0, s>>>(a);
   else
-    route_select_kernel<16><<<1, kSelectThreads, lds, s>>>(a);
+    route_select_kernel<16><<<1, kSelectThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,252 @@
+// Device helpers of the routing: the wavefront top-k shared by the router
+// kernels and the decode gate/up kernel (which routes a decode batch itself).
+#pragma once
+
+#include <math.h>
+
+#include "common.h"
+
+namespace moe {
+
+// Order-preserving map of a float onto uint32 (NaN must be excluded).
+MOE_DEV uint32_t float_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+MOE_DEV float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int CTRL>
+MOE_DEV uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
+}
+
+// Wave-wide maximum (uniform result).
+MOE_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Top-k of one token's logits held by a whole wave: lane l holds experts
+// l, l+64, ... in v[] (NaN already replaced by -inf, absent experts -inf).
+// Lane k < K receives round k's expert and routing weight.
+template <int NPL>
+MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t renorm, int &my_e, float &my_w) {
+  const int lane = __lane_id();
+  uint32_t key[NPL];  // 0 = used or absent
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) key[j] = (lane + 64 * j < E) ? float_key(v[j]) : 0u;
+  float top_v = 0.f;
+  float my_v = 0.f;  // lane k keeps round k's value and index
+  my_e = 0;
+  for (int k = 0; k < K; ++k) {
+    // the largest remaining key, then the lowest expert index holding it
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) m = max(m, key[j]);
+    m = wave_max_u32(m);
+    int sel = 0;
+#pragma unroll
+    for (int j = NPL - 1; j >= 0; --j) {
+      const uint64_t hit = __ballot(key[j] == m);
+      if (hit) sel = 64 * j + __builtin_ctzll(hit);
+    }
+    if ((sel & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (j == (sel >> 6)) key[j] = 0u;
+    }
+    const float sel_v = key_float(m);
+    if (k == 0) top_v = sel_v;
+    if (lane == k) {
+      my_v = sel_v;
+      my_e = sel;
+    }
+  }
+  // Softmax over the selected logits (renorm) or over all E, the largest
+  // logit subtracted for range; sums in a fixed order.
+  const float mine = (lane < K) ? expf(my_v - top_v) : 0.f;
+  float denom;
+  if (renorm) {
+    denom = 0.f;
+    for (int k = 0; k < K; ++k) denom += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), k));
+  } else {
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      if (lane + 64 * j < E) part += expf(v[j] - top_v);
+    denom = sum64(part);
+  }
+  my_w = mine / denom;
+}
+
+// ------------------------------------------------------------------------
+// Routing of a decode batch (T <= kFusedTokens) inside one block: logits
+// from the router's partial sums (slices added in order, then the bias),
+// top-k per token (one wave per token), and the permutation, all in LDS.
+// With `publish` the block also writes the routing to global memory (ids,
+// weights, counts, offsets, active list, rows, inverse positions).
+
+constexpr int kRouteMaxPairs = 1024;  // T * K for T <= 16, K <= 64
+constexpr int kRouteMaxExperts = 1024;
+
+struct RouteLds {
+  uint32_t mask[16][kRouteMaxExperts / 32];  // experts chosen by each token
+  int ids[kRouteMaxPairs];
+  float w[kRouteMaxPairs];
+  int row_tok[kRouteMaxPairs];  // token of each permuted row
+  int cnt[kRouteMaxExperts];    // rows per expert
+  int off[kRouteMaxExperts];    // first row per expert
+  int active[kRouteMaxExperts];
+  int scan[16];
+  int n_active;
+};
+
+// Exclusive scan of one value per thread over the block (up to 16 waves);
+// also returns the block total.
+MOE_DEV int block_scan(int v, int *scratch, int &total) {
+  const int lane = __lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  lds_barrier();
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int x = scratch[w];
+    before += w < wave ? x : 0;
+    all += x;
+  }
+  total = all;
+  lds_barrier();
+  return before + inc - v;
+}
+
+template <int NPL>
+MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) {
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int nw = nthr >> 6;
+  const int T = a.T, E = a.E, S = a.S, K = a.K;
+  const int TK = T * K;
+  const int mwords = (E + 31) / 32;
+  for (int i = tid; i < E; i += nthr) L.cnt[i] = 0;
+  for (int i = tid; i < T * mwords; i += nthr) L.mask[i / mwords][i % mwords] = 0u;
+  for (int t = wave; t < T; t += nw) {
+    // the partials of four slices at a time as independent loads, then
+    // their sums in slice order
+    const float *__restrict__ part = a.part;
+    float acc[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float pv[NPL][4];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ex = lane + 64 * j;
+          pv[j][q] = (ex < E && s0 + q < S) ? part[(static_cast<size_t>(s0 + q) * T + t) * E + ex] : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (s0 + q < S) acc[j] += pv[j][q];
+    }
+    float v[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int ex = lane + 64 * j;
+      const float sum = acc[j] + (a.router_bias && ex < E ? a.router_bias[ex] : 0.f);
+      v[j] = (ex < E && sum == sum) ? sum : -INFINITY;  // NaN never outranks a number
+      if (publish && a.logits && ex < E) a.logits[static_cast<size_t>(t) * E + ex] = sum;
+    }
+    int my_e;
+    float my_w;
+    wave_topk<NPL>(v, E, K, a.renorm, my_e, my_w);
+    if (lane < K) {
+      const int p = t * K + lane;
+      L.ids[p] = my_e;
+      L.w[p] = my_w;
+      if (publish) {
+        a.ids[p] = my_e;
+        a.w[p] = my_w;
+      }
+    }
+  }
+  lds_barrier();
+  for (int p = tid; p < TK; p += nthr) {
+    const int ex = L.ids[p];
+    atomicAdd(&L.cnt[ex], 1);
+    atomicOr(&L.mask[p / K][ex >> 5], 1u << (ex & 31));
+  }
+  lds_barrier();
+  // thread tid owns the experts [tid * ept, tid * ept + ept)
+  const int ept = (E + nthr - 1) / nthr;  // <= 4
+  int c4[4], n_here = 0, nz_here = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = tid * ept + i;
+    c4[i] = (i < ept && ex < E) ? L.cnt[ex] : 0;
+    n_here += c4[i];
+    nz_here += c4[i] > 0;
+  }
+  int total = 0, n_act = 0;
+  int base = block_scan(n_here, L.scan, total);
+  int abase = block_scan(nz_here, L.scan, n_act);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = tid * ept + i;
+    if (i < ept && ex < E) {
+      L.off[ex] = base;
+      if (c4[i] > 0) L.active[abase] = ex;
+      if (publish) {
+        a.counts[ex] = c4[i];
+        a.offsets[ex] = base;
+        if (c4[i] > 0) a.active[abase] = ex;
+      }
+      abase += c4[i] > 0;
+    }
+    base += c4[i];
+  }
+  if (tid == 0) {
+    L.n_active = n_act;
+    if (publish) {
+      a.offsets[E] = total;
+      *a.n_active = n_act;
+    }
+  }
+  lds_barrier();
+  for (int p = tid; p < TK; p += nthr) {
+    // a token picks an expert at most once, so the pair's rank inside its
+    // expert is the number of earlier tokens that picked the expert
+    const int ex = L.ids[p];
+    const int t = p / K;
+    int r = 0;
+    for (int q = 0; q < t; ++q) r += (L.mask[q][ex >> 5] >> (ex & 31)) & 1u;
+    const int pos = L.off[ex] + r;
+    L.row_tok[pos] = p / K;
+    if (publish) {
+      a.row_tok[pos] = p / K;
+      a.row_w[pos] = L.w[p];
+      a.inv_pos[p] = pos;
+    }
+  }
+  lds_barrier();
+}
+
+}  // namespace moe
