@@ -425,7 +425,7 @@ static int pf_grid(int items_upper) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
-  const int cap = 4 * cus;  // four resident blocks per compute unit
+  const int cap = 3 * cus;  // the blocks resident at once (three per compute unit)
   return items_upper < 1 ? 1 : (items_upper < cap ? items_upper : cap);
 }
 

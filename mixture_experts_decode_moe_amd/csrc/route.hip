@@ -124,6 +124,90 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restr
   if (e < E && lane < nt) logits[static_cast<size_t>(t0 + lane) * E + e] = total + (bias ? bias[e] : 0.f);
 }
 
+// ---------------------------------------------------------- large batches
+//
+// For more than kFusedTokens tokens the logits are an fp32 GEMM on the
+// matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation):
+// a block owns 32 tokens x 64 experts, wave w the experts 16w..16w+15 of
+// both 16-token halves; the reduction dimension advances 64 at a time with
+// the x rows (bf16, widened exactly) and the router rows staged in LDS.
+// moe_route and the layer use this kernel alike for such batches.
+typedef float rf32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRmTok = 32, kRmExp = 64, kRmK = 64, kRmPad = 68;
+
+__global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restrict__ wr,
+                                                          const float *__restrict__ bias,
+                                                          const uint16_t *__restrict__ x, int32_t T, int32_t H,
+                                                          int32_t E, float *__restrict__ logits) {
+  __shared__ float xs[2][kRmTok][kRmPad];
+  __shared__ float ws[2][kRmExp][kRmPad];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 15, q = lane >> 4;
+  const int t0 = blockIdx.y * kRmTok;
+  const int e0 = blockIdx.x * kRmExp;
+  // staging: x piece (token tid / 8, 8 elements at 8 (tid % 8)); router
+  // rows: 4 float4 per thread (expert tid / 4 + 0, k 16 (tid % 4) + 4 i)
+  const int xt = tid >> 3, xk = (tid & 7) * 8;
+  const int we = tid >> 2, wk = (tid & 3) * 16;
+  const bool xv = t0 + xt < T, wv = e0 + we < E;
+  const uint4 *xp = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(xv ? t0 + xt : 0) * H + xk);
+  const float4 *wp = reinterpret_cast<const float4 *>(wr + static_cast<size_t>(wv ? e0 + we : 0) * H + wk);
+  uint4 xr;
+  float4 wrr[4];
+  auto load = [&](int s) {
+    xr = xv ? xp[s * (kRmK / 8)] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrr[i] = wv ? wp[s * (kRmK / 4) + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto store = [&](int buf) {
+    const uint32_t d[4] = {xr.x, xr.y, xr.z, xr.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xs[buf][xt][xk + 2 * i] = bf16_lo(d[i]);
+      xs[buf][xt][xk + 2 * i + 1] = bf16_hi(d[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4 *>(&ws[buf][we][wk + 4 * i]) = wrr[i];
+  };
+  rf32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const int steps = H / kRmK;
+  load(0);
+  store(0);
+  lds_barrier();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) load(s + 1);
+    // lane group q takes k = 16 r + 4 q + c in MFMA (r, c), for A and B alike
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 b4 = *reinterpret_cast<const float4 *>(&ws[buf][16 * wave + n][16 * r + 4 * q]);
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(&xs[buf][16 * mt + n][16 * r + 4 * q]);
+        const float aa[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[c], bb[c], acc[mt], 0, 0, 0);
+      }
+    }
+    if (s + 1 < steps) store(buf ^ 1);
+    lds_barrier();
+  }
+  const int e = e0 + 16 * wave + n;
+  if (e < E) {
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * mt + 4 * q + i;
+        if (t < T) logits[static_cast<size_t>(t) * E + e] = acc[mt][i] + b;
+      }
+  }
+}
+
 // One wave per token.  Lane l holds experts l, l+64, ... (up to 16 each).
 template <int NPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int32_t T, int32_t E,
@@ -213,6 +297,11 @@ hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s) {
+  if (a.T > kFusedTokens && a.H % kRmK == 0) {
+    dim3 g((a.E + kRmExp - 1) / kRmExp, (a.T + kRmTok - 1) / kRmTok);
+    router_mfma_kernel<<<g, 256, 0, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits);
+    return hipGetLastError();
+  }
   dim3 grid((a.E + 3) / 4, (a.T + kRouterTokens - 1) / kRouterTokens);
   const size_t lds = router_slice_lds_bytes(route_fused_slice(a.H), kRouterTokens);
   router_logits_kernel<<<grid, 256, lds, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits);

@@ -58,7 +58,11 @@ def test_route(mb, cfg):
     tie = pu.check_selection(ids_h, ids_ref, ref, K)
     ok = ~tie
     same = np.all(ids_h == ids_ref, axis=1) & ok
-    assert np.all(np.abs(w_h[same] - w_ref[same]) <= pu.W_TOL)
+    # the weights are the softmax of the GPU's own logits, and differ from
+    # the oracle's by at most what the logits' float32 error allows
+    pu.check_routing_self_consistent(ids_h, w_h, lg_h, K, shape.renorm)
+    w_tol = pu.W_TOL + 2.0 * np.max(np.abs(lg_h - ref), axis=1)
+    assert np.all(np.abs(w_h[same] - w_ref[same]) <= w_tol[same][:, None])
     assert np.all(np.abs(w_h.sum(axis=1) - 1.0) <= 1e-6)
     say(f"route cfg{cfg}: near ties {int(tie.sum())} of {T}")
 
