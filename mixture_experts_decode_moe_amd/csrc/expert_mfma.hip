@@ -129,17 +129,38 @@ struct GuWeights {
   float rs;           // int8: the row scale
 };
 
+// Base pointers of the routed and shared gate/up weights, read once per
+// block into scalar registers.
+struct GuPtrs {
+  gchar_t *gq, *uq, *gs, *us;      // routed
+  gchar_t *sgq, *suq, *sgs, *sus;  // shared
+};
+
+MOE_DEV GuPtrs gu_ptrs(const FfnArgs &a) {
+  GuPtrs p;
+  p.gq = uniform_gptr(a.gq);
+  p.uq = uniform_gptr(a.uq);
+  p.gs = uniform_gptr(a.gs);
+  p.us = uniform_gptr(a.us);
+  p.sgq = uniform_gptr(a.sgq);
+  p.suq = uniform_gptr(a.suq);
+  p.sgs = uniform_gptr(a.sgs);
+  p.sus = uniform_gptr(a.sus);
+  return p;
+}
+
 // Loads this lane's part of item (e, f0): lanes n < 8 the gate row f0 + n,
 // lanes n >= 8 the up row f0 + n - 8 (e < 0: the shared expert).
 template <int FMT, int JW>
-MOE_DEV void gu_load(const FfnArgs &a, int e, int f0, int wave, int n, int g, GuWeights<FMT, JW> &w) {
+MOE_DEV void gu_load(const FfnArgs &a, const GuPtrs &P, int e, int f0, int wave, int n, int g,
+                     GuWeights<FMT, JW> &w) {
   using Fm = MfmaFmt<FMT>;
   const bool shared = e < 0;
   const bool up = n >= 8;
   const int F = shared ? a.Fs : a.F;
   const size_t row = static_cast<size_t>(shared ? 0 : e) * F + f0 + (n & 7);
-  gchar_t *gq = uniform_gptr(shared ? a.sgq : a.gq), *uq = uniform_gptr(shared ? a.suq : a.uq);
-  gchar_t *gs = uniform_gptr(shared ? a.sgs : a.gs), *us = uniform_gptr(shared ? a.sus : a.us);
+  gchar_t *gq = shared ? P.sgq : P.gq, *uq = shared ? P.suq : P.uq;
+  gchar_t *gs = shared ? P.sgs : P.gs, *us = shared ? P.sus : P.us;
   gchar_t *q = up ? uq : gq;
   gchar_t *sc = up ? us : gs;
   const int nblk = a.H / Fm::kBlockK;
@@ -242,11 +263,11 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
     // every block routes the batch (block 0 also publishes it)
     const int npl = (a.route.E + 63) / 64;
     if (npl <= 1)
-      route_in_block<1>(a.route, L, blockIdx.x == 0);
+      route_in_block_small<1>(a.route, L, blockIdx.x == 0);
     else if (npl <= 2)
-      route_in_block<2>(a.route, L, blockIdx.x == 0);
+      route_in_block_small<2>(a.route, L, blockIdx.x == 0);
     else
-      route_in_block<4>(a.route, L, blockIdx.x == 0);  // E <= 256 on this path
+      route_in_block_small<4>(a.route, L, blockIdx.x == 0);  // E <= 256 on this path
     U = L.n_active;
   } else {
     U = routed_units(a);
@@ -341,12 +362,13 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   // is issued first (unconditionally: a missing item re-requests the
   // chunk's first item, already in flight), so the wait before each item
   // leaves the later items' loads in flight.
+  const GuPtrs P = gu_ptrs(a);
   for (int c0 = 0; c0 < my_items; c0 += NI) {
     GuWeights<FMT, JW> w[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int it = c0 + i < my_items ? c0 + i : c0;
-      gu_load<FMT, JW>(a, tab[it][0], tab[it][3], wave, n, g, w[i]);
+      gu_load<FMT, JW>(a, P, tab[it][0], tab[it][3], wave, n, g, w[i]);
     }
     // groups of kGuGroup items: every wave's partial tiles of the group go to
     // LDS, then one pass adds them and applies SwiGLU (two barriers a group)

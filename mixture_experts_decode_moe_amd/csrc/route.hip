@@ -272,7 +272,10 @@ constexpr int kSelectThreads = 1024;
 template <int NPL>
 __global__ void __launch_bounds__(kSelectThreads) route_select_kernel(RouteFusedArgs a) {
   __shared__ RouteLds L;
-  route_in_block<NPL>(a, L, true);
+  if constexpr (NPL <= 4)
+    route_in_block_small<NPL>(a, L, true);
+  else
+    route_in_block<NPL>(a, L, true);
 }
 
 hipError_t launch_route_partial(const RouteFusedArgs &a, hipStream_t s) {

@@ -249,4 +249,135 @@ MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) 
   lds_barrier();
 }
 
+// The same routing for E <= 256 (NPL <= 4) with fewer block-wide steps:
+// each token's wave builds the token's expert bitmask, one wave derives the
+// counts, offsets and active list from the masks, then every thread places
+// pairs.  Results are identical to route_in_block's.
+template <int NPL>
+MOE_DEV void route_in_block_small(const RouteFusedArgs &a, RouteLds &L, bool publish) {
+  static_assert(NPL <= 4, "E <= 256");
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int nw = nthr >> 6;
+  const int T = a.T, E = a.E, S = a.S, K = a.K;
+  const int TK = T * K;
+  const int mwords = (E + 31) / 32;  // <= 8
+  for (int t = wave; t < T; t += nw) {
+    const float *__restrict__ part = a.part;
+    float acc[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float pv[NPL][4];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ex = lane + 64 * j;
+          pv[j][q] = (ex < E && s0 + q < S) ? part[(static_cast<size_t>(s0 + q) * T + t) * E + ex] : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (s0 + q < S) acc[j] += pv[j][q];
+    }
+    float v[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int ex = lane + 64 * j;
+      const float sum = acc[j] + (a.router_bias && ex < E ? a.router_bias[ex] : 0.f);
+      v[j] = (ex < E && sum == sum) ? sum : -INFINITY;  // NaN never outranks a number
+      if (publish && a.logits && ex < E) a.logits[static_cast<size_t>(t) * E + ex] = sum;
+    }
+    int my_e;
+    float my_w;
+    wave_topk<NPL>(v, E, K, a.renorm, my_e, my_w);
+    // the wave's own LDS operations run in order: clear, then set the bits
+    if (lane < mwords) L.mask[t][lane] = 0u;
+    if (lane < K) {
+      const int p = t * K + lane;
+      L.ids[p] = my_e;
+      L.w[p] = my_w;
+      if (publish) {
+        a.ids[p] = my_e;
+        a.w[p] = my_w;
+      }
+      atomicOr(&L.mask[t][my_e >> 5], 1u << (my_e & 31));
+    }
+  }
+  lds_barrier();
+  if (wave == 0) {
+    // lane l owns the experts 4l .. 4l+3 (one mask word)
+    int c[4] = {0, 0, 0, 0};
+    const int word = (4 * lane) >> 5, sh = (4 * lane) & 31;
+    if (4 * lane < E) {
+      for (int t = 0; t < T; ++t) {
+        const uint32_t m = L.mask[t][word] >> sh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] += (m >> i) & 1u;
+      }
+    }
+    int n_here = 0, nz_here = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * lane + i >= E) c[i] = 0;
+      n_here += c[i];
+      nz_here += c[i] > 0;
+    }
+    int inc = n_here, incz = nz_here;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off), oz = __shfl_up(incz, off);
+      if (lane >= off) {
+        inc += o;
+        incz += oz;
+      }
+    }
+    int base = inc - n_here, abase = incz - nz_here;
+    const int total = __shfl(inc, 63), n_act = __shfl(incz, 63);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ex = 4 * lane + i;
+      if (ex < E) {
+        L.cnt[ex] = c[i];
+        L.off[ex] = base;
+        if (c[i] > 0) L.active[abase] = ex;
+        if (publish) {
+          a.counts[ex] = c[i];
+          a.offsets[ex] = base;
+          if (c[i] > 0) a.active[abase] = ex;
+        }
+        abase += c[i] > 0;
+      }
+      base += c[i];
+    }
+    if (lane == 0) {
+      L.n_active = n_act;
+      if (publish) {
+        a.offsets[E] = total;
+        *a.n_active = n_act;
+      }
+    }
+  }
+  lds_barrier();
+  for (int p = tid; p < TK; p += nthr) {
+    // rank inside the expert = earlier tokens that picked it
+    const int ex = L.ids[p];
+    const int t = p / K;
+    int r = 0;
+    for (int q = 0; q < t; ++q) r += (L.mask[q][ex >> 5] >> (ex & 31)) & 1u;
+    const int pos = L.off[ex] + r;
+    L.row_tok[pos] = t;
+    if (publish) {
+      a.row_tok[pos] = t;
+      a.row_w[pos] = L.w[p];
+      a.inv_pos[p] = pos;
+    }
+  }
+  lds_barrier();
+}
+
 }  // namespace moe
