@@ -411,6 +411,380 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
   }
 }
 
+// ------------------------------------------------ pipelined GEMM variants
+// For an even number of k-steps (the model's H = 2048 for gate/up, F = 512
+// for down) the k loop runs over pairs of steps with two register slots and
+// two LDS buffers whose indices are constants: the weight chunks of the next
+// two steps and the A rows of the next one stay in flight, with no copies
+// between iterations (a register ring copied across a loop back-edge makes
+// the compiler wait for every load).  Tiles are wider than the generic
+// kernels' (128 SwiGLU columns for gate/up, 256 output columns for down, 64
+// rows), each wave owning four 16-column weight tiles against the 16-row
+// tiles of A; the -136 sum correction of a block is one MFMA against a
+// constant operand per 16-row tile, shared by the wave's four weight tiles.
+//
+// The k loop is instantiated once per number of 16-row tiles that hold rows
+// (1..4), chosen per item: no matrix-core instruction sits under a branch.
+// (With the tile count as a branch inside the loop, hipcc left an MFMA
+// result read by a VALU instruction right after the branch without the
+// wait states the matrix core needs, and those reads saw stale registers.)
+
+typedef __attribute__((address_space(1))) const u32x2_t gu2_t;
+
+MOE_DEV uint4 load16_g(gchar_t *p) {
+  const u32x4_t v = *reinterpret_cast<gu32x4_t *>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// An empty volatile statement that takes the value in registers: volatile
+// statements keep their order, so each scaled accumulation happens where it
+// is written, instead of every product of a step being computed first and
+// held (which spills).
+MOE_DEV void pin(f32x4_t &v) { __asm__ volatile("" : "+v"(v)); }
+// The same for a 32-bit offset: the addresses derived from it are then
+// computed where they are used rather than hoisted out of the k loop and
+// kept live (which spills, and a spill reload waits for every load).
+MOE_DEV void pin_u32(uint32_t &v) { __asm__ volatile("" : "+v"(v)); }
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+template <class Fn>
+MOE_DEV void with_msub(int msub, Fn &&fn) {
+  switch (msub) {
+    case 1:
+      fn(IntC<1>{});
+      break;
+    case 2:
+      fn(IntC<2>{});
+      break;
+    case 3:
+      fn(IntC<3>{});
+      break;
+    default:
+      fn(IntC<4>{});
+      break;
+  }
+}
+
+template <int KS>
+__global__ void __launch_bounds__(kPfThreads, 2) gateup_gemm_kernel(FfnArgs a) {
+  static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
+  __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted, one k-step
+  __shared__ int pre[kPfMaxUnits + 1];
+  __shared__ int scratch[4];
+  constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int T = a.T;
+  const int H = 128 * KS;
+  const int n_units = pf_tiles(a, pre, scratch);
+  const int col_tiles = a.F / 128;
+  const int n_items = pre[n_units] * col_tiles;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const u32x4_t c136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
+  const int pc = tid & 15;
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int j = item / col_tiles;
+    const int ct = item - j * col_tiles;
+    const int u = pf_find(pre, n_units, j);
+    const PfUnit un = pf_unit(a, u);
+    const int m0 = (j - pre[u]) * kPfRows;
+    const int rows = min(kPfRows, un.n - m0);
+    const bool shared = un.e < 0;
+    const int F = shared ? a.Fs : a.F;
+    // weight rows of this lane: tiles q = 0, 1 gate, q = 2, 3 up, SwiGLU
+    // column cbase + 16 (q & 1); 32-bit offsets from block-uniform bases (an
+    // expert's weights are far below 4 GiB)
+    const int cbase = ct * 128 + 32 * wave + n;
+    gchar_t *gq = uniform_gptr(shared ? a.sgq : a.gq);
+    gchar_t *uq = uniform_gptr(shared ? a.suq : a.uq);
+    gchar_t *gsc = uniform_gptr(shared ? a.sgs : a.gs);
+    gchar_t *usc = uniform_gptr(shared ? a.sus : a.us);
+    const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * F + cbase);
+    uint32_t woff = row0 * (nblk * 16) + 16 * g, soff = row0 * (nblk * 2);
+    constexpr uint32_t kW16 = 16 * nblk * 16, kS16 = 16 * nblk * 2;  // 16 rows further
+
+    // A staging: thread t owns piece t % 16 of rows t / 16 + 16 i
+    gchar_t *xg = uniform_gptr(a.x);
+    uint32_t xoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 4) + 16 * i;
+      int t = 0;
+      if (r < rows) {
+        const int rr = un.r0 + m0 + r;
+        t = shared ? rr : (a.row_tok ? a.row_tok[rr] : rr);
+        t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+      }
+      xoff[i] = static_cast<uint32_t>(t) * (2 * H) + 16 * pc;
+    }
+    // Rows past the tile's end read token 0's row: their products land in
+    // accumulator rows that are never stored (every row of an MFMA result
+    // depends on its own A row only), and the requests stay unconditional.
+    auto load_a = [&](int s, uint4(&v)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = load16_g(xg + (xoff[i] + 256u * s));
+    };
+    auto store_a = [&](int buf, const uint4(&v)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4_t pp = pair_permute(v[i]);
+        as[buf][(tid >> 4) + 16 * i][pc] = make_uint4(pp.x, pp.y, pp.z, pp.w);
+      }
+    };
+    auto load_b = [&](int s, uint4(&w)[4], u32x2_t(&sc)[4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        gchar_t *wb = q < 2 ? gq : uq;
+        gchar_t *sb = q < 2 ? gsc : usc;
+        w[q] = load_stream16_g(wb + (woff + (q & 1) * kW16 + 64u * s));
+        sc[q] = *reinterpret_cast<gu2_t *>(sb + (soff + (q & 1) * kS16 + 8u * s));
+      }
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[q][mt] = zero4;
+    uint4 av[4];        // A rows of the next step
+    uint4 bw[2][4];     // weight chunks, slot s & 1
+    u32x2_t bs[2][4];   // their block scales
+    load_a(0, av);
+    load_b(0, bw[0], bs[0]);
+    load_b(1, bw[1], bs[1]);
+    store_a(0, av);
+    lds_barrier();
+    with_msub((rows + 15) >> 4, [&](auto msc) __attribute__((always_inline)) {
+      constexpr int MS = decltype(msc)::value;
+      auto step = [&](int s, auto slc) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slc)::value;
+        pin_u32(woff);
+        pin_u32(soff);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pin_u32(xoff[i]);
+        // unconditional (clamped) requests keep the register slots out of
+        // scratch memory; past the end they re-read the last step
+        load_a(min(s + 1, KS - 1), av);  // A(s) is in LDS already
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xpose4(bw[sl][q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          // block 4 s + p: the four weight tiles' operands, then one 16-row
+          // tile of A at a time against all four
+          u32x4_t B[4];
+          float scl[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            B[q] = magic_pairs(word(bw[sl][q], p));
+            scl[q] = scale4(bs[sl][q].x, bs[sl][q].y, p);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MS; ++mt) {
+            const uint4 v = as[sl][16 * mt + n][4 * p + g];
+            const u32x4_t A = {v.x, v.y, v.z, v.w};
+            const f32x4_t cc = mfma_bf16(A, c136, zero4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[q][mt] = fma4(scl[q], mfma_bf16(A, B[q], cc), acc[q][mt]);
+              pin(acc[q][mt]);
+            }
+          }
+        }
+        load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);
+        // the weight requests go out before the wait for the A rows below
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(sl ^ 1, av);  // unconditional: no branch inside the step (past the end a harmless rewrite)
+        lds_barrier();
+      };
+      for (int s = 0; s < KS; s += 2) {
+        step(s, IntC<0>{});
+        step(s + 1, IntC<1>{});
+      }
+    });
+    // SwiGLU: lane (n, g) holds rows 16 mt + 4 g + i of columns cbase, cbase + 16
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pos = act_pos<MOE_W_INT4_B32>(cbase + 16 * h);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * g + i;
+          if (r < rows) {
+            const float gv = acc[h][mt][i], uv = acc[2 + h][mt][i];
+            const float v = gv / (1.f + expf(-gv)) * uv;
+            const uint16_t hi = f32_to_bf16_rne(v);
+            const uint16_t lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
+            const int rr = m0 + r;
+            const size_t off = shared ? static_cast<size_t>(a.n_rows) * a.F + static_cast<size_t>(rr) * a.Fs
+                                      : static_cast<size_t>(un.r0 + rr) * a.F;
+            uint16_t *arow = reinterpret_cast<uint16_t *>(a.act + off);
+            arow[pos] = hi;
+            arow[F + pos] = lo;
+          }
+        }
+    }
+    lds_barrier();  // the next item's first A tile reuses buffer 0
+  }
+}
+
+template <int KS>
+__global__ void __launch_bounds__(kPfThreads, 2) down_gemm_kernel(FfnArgs a) {
+  static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
+  __shared__ uint4 as[2][2][kPfRows][17];  // [buffer][hi, lo plane] act rows, one k-step
+  __shared__ int pre[kPfMaxUnits + 1];
+  __shared__ int scratch[4];
+  constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int H = a.H;
+  const int n_units = pf_tiles(a, pre, scratch);
+  const int col_tiles = H / 256;
+  const int n_items = pre[n_units] * col_tiles;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const u32x4_t c136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
+  const int pc = tid & 15;
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int j = item / col_tiles;
+    const int ct = item - j * col_tiles;
+    const int u = pf_find(pre, n_units, j);
+    const PfUnit un = pf_unit(a, u);
+    const int m0 = (j - pre[u]) * kPfRows;
+    const int rows = min(kPfRows, un.n - m0);
+    const bool shared = un.e < 0;
+    const int F = shared ? a.Fs : a.F;  // == 128 KS
+    // output columns of this lane: hbase + 16 q; 32-bit offsets from
+    // block-uniform bases
+    const int hbase = ct * 256 + 64 * wave + n;
+    const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * H + hbase);
+    gchar_t *dq = uniform_gptr(shared ? a.sdq : a.dq);
+    gchar_t *dsc = uniform_gptr(shared ? a.sds : a.ds);
+    uint32_t woff = row0 * (nblk * 16) + 16 * g, soff = row0 * (nblk * 2);
+    constexpr uint32_t kW16 = 16 * nblk * 16, kS16 = 16 * nblk * 2;  // 16 rows further
+
+    // A staging: thread t owns piece t % 16 of rows t / 16 + 16 i, both
+    // planes (byte offsets of the rows inside the act buffer)
+    gchar_t *ag = uniform_gptr(a.act);
+    uint32_t aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 4) + 16 * i;
+      const int rr = m0 + (r < rows ? r : 0);
+      const uint32_t off = shared ? static_cast<uint32_t>(a.n_rows * a.F + rr * a.Fs)
+                                  : static_cast<uint32_t>((un.r0 + rr) * a.F);
+      aoff[i] = 4 * off + 16 * pc;
+    }
+    // rows past the tile's end read its first row (results never stored)
+    auto load_a = [&](int s, uint4(&v)[8]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = load16_g(ag + (aoff[i] + 256u * s));
+        v[4 + i] = load16_g(ag + (aoff[i] + 2u * F + 256u * s));
+      }
+    };
+    auto store_a = [&](int buf, const uint4(&v)[8]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        as[buf][0][(tid >> 4) + 16 * i][pc] = v[i];
+        as[buf][1][(tid >> 4) + 16 * i][pc] = v[4 + i];
+      }
+    };
+    auto load_b = [&](int s, uint4(&w)[4], u32x2_t(&sc)[4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q] = load_stream16_g(dq + (woff + q * kW16 + 64u * s));
+        sc[q] = *reinterpret_cast<gu2_t *>(dsc + (soff + q * kS16 + 8u * s));
+      }
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[q][mt] = zero4;
+    uint4 av[8];
+    uint4 bw[2][4];
+    u32x2_t bs[2][4];
+    load_a(0, av);
+    load_b(0, bw[0], bs[0]);
+    load_b(1, bw[1], bs[1]);
+    store_a(0, av);
+    lds_barrier();
+    with_msub((rows + 15) >> 4, [&](auto msc) __attribute__((always_inline)) {
+      constexpr int MS = decltype(msc)::value;
+      auto step = [&](int s, auto slc) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slc)::value;
+        pin_u32(woff);
+        pin_u32(soff);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pin_u32(aoff[i]);
+        load_a(min(s + 1, KS - 1), av);  // A(s) is in LDS already; clamped, unconditional
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xpose4(bw[sl][q]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          u32x4_t B[4];
+          float scl[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            B[q] = magic_pairs(word(bw[sl][q], p));
+            scl[q] = scale4(bs[sl][q].x, bs[sl][q].y, p);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MS; ++mt) {
+            const uint4 vh = as[sl][0][16 * mt + n][4 * p + g];
+            const uint4 vl = as[sl][1][16 * mt + n][4 * p + g];
+            const u32x4_t Ah = {vh.x, vh.y, vh.z, vh.w}, Al = {vl.x, vl.y, vl.z, vl.w};
+            const f32x4_t cc = mfma_bf16(Al, c136, mfma_bf16(Ah, c136, zero4));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[q][mt] = fma4(scl[q], mfma_bf16(Al, B[q], mfma_bf16(Ah, B[q], cc)), acc[q][mt]);
+              pin(acc[q][mt]);
+            }
+          }
+        }
+        load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);
+        // the weight requests go out before the wait for the A rows below
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(sl ^ 1, av);  // unconditional: no branch inside the step (past the end a harmless rewrite)
+        lds_barrier();
+      };
+      for (int s = 0; s < KS; s += 2) {
+        step(s, IntC<0>{});
+        step(s + 1, IntC<1>{});
+      }
+    });
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int h = hbase + 16 * q;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * g + i;
+          if (r < rows) {
+            const int rr = m0 + r;
+            const int row = un.r0 + rr;
+            const float wgt = shared || !a.row_w ? 1.f : a.row_w[row];
+            const size_t orow = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(row);
+            a.rows_out[orow * H + h] = acc[q][mt][i] * wgt;
+          }
+        }
+    }
+    lds_barrier();
+  }
+}
+
 // ----------------------------------------------------------------- launches
 
 bool prefill_ok(const FfnArgs &a) {
@@ -436,12 +810,30 @@ static int pf_tiles_upper(const FfnArgs &a) {
   return (a.n_rows + kPfRows - 1) / kPfRows + units + (a.Fs > 0 ? (a.T + kPfRows - 1) / kPfRows : 0);
 }
 
+static int gm_grid(int items_upper) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const int cap = 2 * cus;  // two blocks per compute unit
+  return items_upper < 1 ? 1 : (items_upper < cap ? items_upper : cap);
+}
+
 hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
+  if (a.H == 128 * 16 && a.F % 128 == 0) {
+    gateup_gemm_kernel<16><<<gm_grid(pf_tiles_upper(a) * (a.F / 128)), kPfThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   gateup_prefill_kernel<<<pf_grid(pf_tiles_upper(a) * (a.F / kPfCols)), kPfThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
+  if (a.F == 128 * 4 && a.H % 256 == 0) {
+    down_gemm_kernel<4><<<gm_grid(pf_tiles_upper(a) * (a.H / 256)), kPfThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   down_prefill_kernel<<<pf_grid(pf_tiles_upper(a) * (a.H / kPfCols)), kPfThreads, 0, s>>>(a);
   return hipGetLastError();
 }
