@@ -69,10 +69,12 @@ MOE_DEV PfUnit pf_unit(const FfnArgs &a, int u) {
 
 // Fills pre[u] = first row tile of unit u (exclusive prefix of the row
 // tiles), pre[n_units] = total; returns the number of units.
+// NT threads (scratch holds NT / 64 ints).
+template <int NT = kPfThreads>
 MOE_DEV int pf_tiles(const FfnArgs &a, int *pre, int *scratch) {
   const int n_units = (a.Fs > 0 ? 1 : 0) + routed_units(a);
   const int tid = threadIdx.x;
-  constexpr int kPer = (kPfMaxUnits + kPfThreads - 1) / kPfThreads;
+  constexpr int kPer = (kPfMaxUnits + NT - 1) / NT;
   int cnt[kPer];
   int mine = 0;
 #pragma unroll
@@ -469,12 +471,14 @@ MOE_DEV void with_msub(int msub, Fn &&fn) {
   }
 }
 
+constexpr int kGmThreads = 512;  // 8 waves; two blocks per compute unit
+
 template <int KS>
-__global__ void __launch_bounds__(kPfThreads, 2) gateup_gemm_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
   __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted, one k-step
   __shared__ int pre[kPfMaxUnits + 1];
-  __shared__ int scratch[4];
+  __shared__ int scratch[kGmThreads / 64];
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -482,14 +486,22 @@ __global__ void __launch_bounds__(kPfThreads, 2) gateup_gemm_kernel(FfnArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int T = a.T;
   const int H = 128 * KS;
-  const int n_units = pf_tiles(a, pre, scratch);
+  const int n_units = pf_tiles<kGmThreads>(a, pre, scratch);
   const int col_tiles = a.F / 128;
   const int n_items = pre[n_units] * col_tiles;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t c136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
   const int pc = tid & 15;
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // XCD-aware order: the blocks of one XCD (block b runs on XCD b mod 8)
+  // take a contiguous run of items per round, so the column tiles of a row
+  // tile, and consecutive row tiles of a unit, share that XCD's L2 for
+  // their A rows and weights
+  const int per_xcd = gridDim.x >> 3;
+  const int my_off = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  for (int round = 0; round < n_items; round += gridDim.x) {
+    const int item = round + my_off;
+    if (item >= n_items) continue;
     const int j = item / col_tiles;
     const int ct = item - j * col_tiles;
     const int u = pf_find(pre, n_units, j);
@@ -498,24 +510,26 @@ __global__ void __launch_bounds__(kPfThreads, 2) gateup_gemm_kernel(FfnArgs a) {
     const int rows = min(kPfRows, un.n - m0);
     const bool shared = un.e < 0;
     const int F = shared ? a.Fs : a.F;
-    // weight rows of this lane: tiles q = 0, 1 gate, q = 2, 3 up, SwiGLU
-    // column cbase + 16 (q & 1); 32-bit offsets from block-uniform bases (an
-    // expert's weights are far below 4 GiB)
-    const int cbase = ct * 128 + 32 * wave + n;
+    // this lane's weight rows: the gate (q = 0) and up (q = 1) rows of SwiGLU
+    // column col; 32-bit offsets from block-uniform bases (an expert's
+    // weights are far below 4 GiB)
+    const int col = ct * 128 + 16 * wave + n;
     gchar_t *gq = uniform_gptr(shared ? a.sgq : a.gq);
     gchar_t *uq = uniform_gptr(shared ? a.suq : a.uq);
     gchar_t *gsc = uniform_gptr(shared ? a.sgs : a.gs);
     gchar_t *usc = uniform_gptr(shared ? a.sus : a.us);
-    const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * F + cbase);
+    const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * F + col);
     uint32_t woff = row0 * (nblk * 16) + 16 * g, soff = row0 * (nblk * 2);
-    constexpr uint32_t kW16 = 16 * nblk * 16, kS16 = 16 * nblk * 2;  // 16 rows further
 
-    // A staging: thread t owns piece t % 16 of rows t / 16 + 16 i
+    // A staging: thread t owns piece t % 16 of rows t / 16 + 32 i.  Rows
+    // past the tile's end read token 0's row: their products land in
+    // accumulator rows that are never stored (every row of an MFMA result
+    // depends on its own A row only), and the requests stay unconditional.
     gchar_t *xg = uniform_gptr(a.x);
-    uint32_t xoff[4];
+    uint32_t xoff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 4) + 16 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int r = (tid >> 4) + 32 * i;
       int t = 0;
       if (r < rows) {
         const int rr = un.r0 + m0 + r;
@@ -524,38 +538,34 @@ __global__ void __launch_bounds__(kPfThreads, 2) gateup_gemm_kernel(FfnArgs a) {
       }
       xoff[i] = static_cast<uint32_t>(t) * (2 * H) + 16 * pc;
     }
-    // Rows past the tile's end read token 0's row: their products land in
-    // accumulator rows that are never stored (every row of an MFMA result
-    // depends on its own A row only), and the requests stay unconditional.
-    auto load_a = [&](int s, uint4(&v)[4]) {
+    auto load_a = [&](int s, uint4(&v)[2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = load16_g(xg + (xoff[i] + 256u * s));
+      for (int i = 0; i < 2; ++i) v[i] = load16_g(xg + (xoff[i] + 256u * s));
     };
-    auto store_a = [&](int buf, const uint4(&v)[4]) {
+    auto store_a = [&](int buf, const uint4(&v)[2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         const u32x4_t pp = pair_permute(v[i]);
-        as[buf][(tid >> 4) + 16 * i][pc] = make_uint4(pp.x, pp.y, pp.z, pp.w);
+        as[buf][(tid >> 4) + 32 * i][pc] = make_uint4(pp.x, pp.y, pp.z, pp.w);
       }
     };
-    auto load_b = [&](int s, uint4(&w)[4], u32x2_t(&sc)[4]) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        gchar_t *wb = q < 2 ? gq : uq;
-        gchar_t *sb = q < 2 ? gsc : usc;
-        w[q] = load_stream16_g(wb + (woff + (q & 1) * kW16 + 64u * s));
-        sc[q] = *reinterpret_cast<gu2_t *>(sb + (soff + (q & 1) * kS16 + 8u * s));
-      }
+    auto load_b = [&](int s, uint4(&w)[2], u32x2_t(&sc)[2]) {
+      // plain loads: the other half of each 128-byte line is requested one
+      // step later and should still be in the L2
+      w[0] = load16_g(gq + (woff + 64u * s));
+      w[1] = load16_g(uq + (woff + 64u * s));
+      sc[0] = *reinterpret_cast<gu2_t *>(gsc + (soff + 8u * s));
+      sc[1] = *reinterpret_cast<gu2_t *>(usc + (soff + 8u * s));
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[2][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[q][mt] = zero4;
-    uint4 av[4];        // A rows of the next step
-    uint4 bw[2][4];     // weight chunks, slot s & 1
-    u32x2_t bs[2][4];   // their block scales
+    uint4 av[2];        // A rows of the next step
+    uint4 bw[2][2];     // weight chunks, slot s & 1
+    u32x2_t bs[2][2];   // their block scales
     load_a(0, av);
     load_b(0, bw[0], bs[0]);
     load_b(1, bw[1], bs[1]);
@@ -568,39 +578,55 @@ __global__ void __launch_bounds__(kPfThreads, 2) gateup_gemm_kernel(FfnArgs a) {
         pin_u32(woff);
         pin_u32(soff);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pin_u32(xoff[i]);
+        for (int i = 0; i < 2; ++i) pin_u32(xoff[i]);
         // unconditional (clamped) requests keep the register slots out of
         // scratch memory; past the end they re-read the last step
         load_a(min(s + 1, KS - 1), av);  // A(s) is in LDS already
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xpose4(bw[sl][q]);
+        for (int q = 0; q < 2; ++q) xpose4(bw[sl][q]);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          // block 4 s + p: the four weight tiles' operands, then one 16-row
-          // tile of A at a time against all four
-          u32x4_t B[4];
-          float scl[4];
+          // block 4 s + p: both weight tiles' operands, then one 16-row tile
+          // of A at a time against both
+          u32x4_t B[2];
+          float scl[2];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < 2; ++q) {
             B[q] = magic_pairs(word(bw[sl][q], p));
             scl[q] = scale4(bs[sl][q].x, bs[sl][q].y, p);
           }
+          // products of 16-row tile mt are scaled into the accumulators
+          // after the products of tile mt + 1 are issued (the matrix core's
+          // latency overlaps the scaling)
+          f32x4_t prev[2];
 #pragma unroll
           for (int mt = 0; mt < MS; ++mt) {
             const uint4 v = as[sl][16 * mt + n][4 * p + g];
             const u32x4_t A = {v.x, v.y, v.z, v.w};
             const f32x4_t cc = mfma_bf16(A, c136, zero4);
+            f32x4_t prod[2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              acc[q][mt] = fma4(scl[q], mfma_bf16(A, B[q], cc), acc[q][mt]);
-              pin(acc[q][mt]);
+            for (int q = 0; q < 2; ++q) prod[q] = mfma_bf16(A, B[q], cc);
+            if (mt > 0) {
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                acc[q][mt - 1] = fma4(scl[q], prev[q], acc[q][mt - 1]);
+                pin(acc[q][mt - 1]);
+              }
             }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) prev[q] = prod[q];
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            acc[q][MS - 1] = fma4(scl[q], prev[q], acc[q][MS - 1]);
+            pin(acc[q][MS - 1]);
           }
         }
         load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);
         // the weight requests go out before the wait for the A rows below
         __builtin_amdgcn_sched_barrier(0);
-        store_a(sl ^ 1, av);  // unconditional: no branch inside the step (past the end a harmless rewrite)
+        store_a(sl ^ 1, av);  // unconditional: no branch inside the step
         lds_barrier();
       };
       for (int s = 0; s < KS; s += 2) {
@@ -608,53 +634,72 @@ __global__ void __launch_bounds__(kPfThreads, 2) gateup_gemm_kernel(FfnArgs a) {
         step(s + 1, IntC<1>{});
       }
     });
-    // SwiGLU: lane (n, g) holds rows 16 mt + 4 g + i of columns cbase, cbase + 16
+    // SwiGLU into LDS (the A buffers are free now): lane (n, g) holds rows
+    // 16 mt + 4 g + i of column col; rows [64][hi 128 + 8 pad | lo 128 + 8].
+    // Rows past the tile's end hold finite values that are never stored.
+    uint16_t *st = reinterpret_cast<uint16_t *>(&as[0][0][0]);
+    constexpr int kStPlane = 136, kStRow = 2 * kStPlane;
+    static_assert(kPfRows * kStRow * 2 <= sizeof(as), "SwiGLU staging must fit the A buffers");
+    const int cl = act_pos<MOE_W_INT4_B32>(16 * wave + n);  // tiles start at multiples of 8
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int pos = act_pos<MOE_W_INT4_B32>(cbase + 16 * h);
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * g + i;
+        const float gv = acc[0][mt][i], uv = acc[1][mt][i];
+        const float v = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
+        const uint16_t hi = f32_to_bf16_rne(v);
+        const uint16_t lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
+        st[r * kStRow + cl] = hi;
+        st[r * kStRow + kStPlane + cl] = lo;
+      }
+    lds_barrier();
+    // 16-byte stores of whole row segments: piece (row, plane, 16 of them)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * g + i;
-          if (r < rows) {
-            const float gv = acc[h][mt][i], uv = acc[2 + h][mt][i];
-            const float v = gv / (1.f + expf(-gv)) * uv;
-            const uint16_t hi = f32_to_bf16_rne(v);
-            const uint16_t lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
-            const int rr = m0 + r;
-            const size_t off = shared ? static_cast<size_t>(a.n_rows) * a.F + static_cast<size_t>(rr) * a.Fs
-                                      : static_cast<size_t>(un.r0 + rr) * a.F;
-            uint16_t *arow = reinterpret_cast<uint16_t *>(a.act + off);
-            arow[pos] = hi;
-            arow[F + pos] = lo;
-          }
-        }
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int idx = tid + kGmThreads * k2;
+      const int r = idx >> 5, plane = (idx >> 4) & 1, pcs = idx & 15;
+      if (r < rows) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(st + r * kStRow + plane * kStPlane + 8 * pcs);
+        const int rr = m0 + r;
+        const size_t off = shared ? static_cast<size_t>(a.n_rows) * a.F + static_cast<size_t>(rr) * a.Fs
+                                  : static_cast<size_t>(un.r0 + rr) * a.F;
+        uint16_t *arow = reinterpret_cast<uint16_t *>(a.act + off);
+        *reinterpret_cast<uint4 *>(arow + plane * F + ct * 128 + 8 * pcs) = v;
+      }
     }
-    lds_barrier();  // the next item's first A tile reuses buffer 0
+    lds_barrier();  // the next item's first A tile reuses the buffers
   }
 }
 
 template <int KS>
-__global__ void __launch_bounds__(kPfThreads, 2) down_gemm_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
   __shared__ uint4 as[2][2][kPfRows][17];  // [buffer][hi, lo plane] act rows, one k-step
   __shared__ int pre[kPfMaxUnits + 1];
-  __shared__ int scratch[4];
+  __shared__ int scratch[kGmThreads / 64];
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
   const int H = a.H;
-  const int n_units = pf_tiles(a, pre, scratch);
+  const int n_units = pf_tiles<kGmThreads>(a, pre, scratch);
   const int col_tiles = H / 256;
   const int n_items = pre[n_units] * col_tiles;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t c136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
   const int pc = tid & 15;
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // XCD-aware order: the blocks of one XCD (block b runs on XCD b mod 8)
+  // take a contiguous run of items per round, so the column tiles of a row
+  // tile, and consecutive row tiles of a unit, share that XCD's L2 for
+  // their A rows and weights
+  const int per_xcd = gridDim.x >> 3;
+  const int my_off = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  for (int round = 0; round < n_items; round += gridDim.x) {
+    const int item = round + my_off;
+    if (item >= n_items) continue;
     const int j = item / col_tiles;
     const int ct = item - j * col_tiles;
     const int u = pf_find(pre, n_units, j);
@@ -665,56 +710,56 @@ __global__ void __launch_bounds__(kPfThreads, 2) down_gemm_kernel(FfnArgs a) {
     const int F = shared ? a.Fs : a.F;  // == 128 KS
     // output columns of this lane: hbase + 16 q; 32-bit offsets from
     // block-uniform bases
-    const int hbase = ct * 256 + 64 * wave + n;
+    const int hbase = ct * 256 + 32 * wave + n;
     const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * H + hbase);
     gchar_t *dq = uniform_gptr(shared ? a.sdq : a.dq);
     gchar_t *dsc = uniform_gptr(shared ? a.sds : a.ds);
     uint32_t woff = row0 * (nblk * 16) + 16 * g, soff = row0 * (nblk * 2);
     constexpr uint32_t kW16 = 16 * nblk * 16, kS16 = 16 * nblk * 2;  // 16 rows further
 
-    // A staging: thread t owns piece t % 16 of rows t / 16 + 16 i, both
-    // planes (byte offsets of the rows inside the act buffer)
+    // A staging: thread t owns piece t % 16 of rows t / 16 + 32 i, both
+    // planes (byte offsets of the rows inside the act buffer); rows past
+    // the tile's end read its first row (results never stored)
     gchar_t *ag = uniform_gptr(a.act);
-    uint32_t aoff[4];
+    uint32_t aoff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 4) + 16 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int r = (tid >> 4) + 32 * i;
       const int rr = m0 + (r < rows ? r : 0);
       const uint32_t off = shared ? static_cast<uint32_t>(a.n_rows * a.F + rr * a.Fs)
                                   : static_cast<uint32_t>((un.r0 + rr) * a.F);
       aoff[i] = 4 * off + 16 * pc;
     }
-    // rows past the tile's end read its first row (results never stored)
-    auto load_a = [&](int s, uint4(&v)[8]) {
+    auto load_a = [&](int s, uint4(&v)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         v[i] = load16_g(ag + (aoff[i] + 256u * s));
-        v[4 + i] = load16_g(ag + (aoff[i] + 2u * F + 256u * s));
+        v[2 + i] = load16_g(ag + (aoff[i] + 2u * F + 256u * s));
       }
     };
-    auto store_a = [&](int buf, const uint4(&v)[8]) {
+    auto store_a = [&](int buf, const uint4(&v)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        as[buf][0][(tid >> 4) + 16 * i][pc] = v[i];
-        as[buf][1][(tid >> 4) + 16 * i][pc] = v[4 + i];
+      for (int i = 0; i < 2; ++i) {
+        as[buf][0][(tid >> 4) + 32 * i][pc] = v[i];
+        as[buf][1][(tid >> 4) + 32 * i][pc] = v[2 + i];
       }
     };
-    auto load_b = [&](int s, uint4(&w)[4], u32x2_t(&sc)[4]) {
+    auto load_b = [&](int s, uint4(&w)[2], u32x2_t(&sc)[2]) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[q] = load_stream16_g(dq + (woff + q * kW16 + 64u * s));
+      for (int q = 0; q < 2; ++q) {
+        w[q] = load16_g(dq + (woff + q * kW16 + 64u * s));
         sc[q] = *reinterpret_cast<gu2_t *>(dsc + (soff + q * kS16 + 8u * s));
       }
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[2][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[q][mt] = zero4;
-    uint4 av[8];
-    uint4 bw[2][4];
-    u32x2_t bs[2][4];
+    uint4 av[4];
+    uint4 bw[2][2];
+    u32x2_t bs[2][2];
     load_a(0, av);
     load_b(0, bw[0], bs[0]);
     load_b(1, bw[1], bs[1]);
@@ -727,16 +772,16 @@ __global__ void __launch_bounds__(kPfThreads, 2) down_gemm_kernel(FfnArgs a) {
         pin_u32(woff);
         pin_u32(soff);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pin_u32(aoff[i]);
-        load_a(min(s + 1, KS - 1), av);  // A(s) is in LDS already; clamped, unconditional
+        for (int i = 0; i < 2; ++i) pin_u32(aoff[i]);
+        load_a(min(s + 1, KS - 1), av);  // A(s) is in LDS already; clamped
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xpose4(bw[sl][q]);
+        for (int q = 0; q < 2; ++q) xpose4(bw[sl][q]);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          u32x4_t B[4];
-          float scl[4];
+          u32x4_t B[2];
+          float scl[2];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < 2; ++q) {
             B[q] = magic_pairs(word(bw[sl][q], p));
             scl[q] = scale4(bs[sl][q].x, bs[sl][q].y, p);
           }
@@ -747,16 +792,15 @@ __global__ void __launch_bounds__(kPfThreads, 2) down_gemm_kernel(FfnArgs a) {
             const u32x4_t Ah = {vh.x, vh.y, vh.z, vh.w}, Al = {vl.x, vl.y, vl.z, vl.w};
             const f32x4_t cc = mfma_bf16(Al, c136, mfma_bf16(Ah, c136, zero4));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2; ++q) {
               acc[q][mt] = fma4(scl[q], mfma_bf16(Al, B[q], mfma_bf16(Ah, B[q], cc)), acc[q][mt]);
               pin(acc[q][mt]);
             }
           }
         }
         load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);
-        // the weight requests go out before the wait for the A rows below
         __builtin_amdgcn_sched_barrier(0);
-        store_a(sl ^ 1, av);  // unconditional: no branch inside the step (past the end a harmless rewrite)
+        store_a(sl ^ 1, av);  // unconditional: no branch inside the step
         lds_barrier();
       };
       for (int s = 0; s < KS; s += 2) {
@@ -764,22 +808,33 @@ __global__ void __launch_bounds__(kPfThreads, 2) down_gemm_kernel(FfnArgs a) {
         step(s + 1, IntC<1>{});
       }
     });
+    // the tile into LDS (the A buffers are free now), rows of 256 + 4 floats,
+    // then 16-byte stores of whole row segments with the row's weight
+    float *st = reinterpret_cast<float *>(&as[0][0][0][0]);
+    constexpr int kStRow = 260;
+    static_assert(kPfRows * kStRow * 4 <= sizeof(as), "output staging must fit the A buffers");
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int h = hbase + 16 * q;
+    for (int q = 0; q < 2; ++q) {
+      const int c = 32 * wave + 16 * q + n;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * g + i;
-          if (r < rows) {
-            const int rr = m0 + r;
-            const int row = un.r0 + rr;
-            const float wgt = shared || !a.row_w ? 1.f : a.row_w[row];
-            const size_t orow = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(row);
-            a.rows_out[orow * H + h] = acc[q][mt][i] * wgt;
-          }
-        }
+        for (int i = 0; i < 4; ++i) st[(16 * mt + 4 * g + i) * kStRow + c] = acc[q][mt][i];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k2 = 0; k2 < 8; ++k2) {
+      const int idx = tid + kGmThreads * k2;
+      const int r = idx >> 6, pcs = idx & 63;
+      if (r < rows) {
+        const float4 v = *reinterpret_cast<const float4 *>(st + r * kStRow + 4 * pcs);
+        const int rr = m0 + r;
+        const int row = un.r0 + rr;
+        const float wgt = shared || !a.row_w ? 1.f : a.row_w[row];
+        const size_t orow = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(row);
+        *reinterpret_cast<float4 *>(a.rows_out + orow * H + ct * 256 + 4 * pcs) =
+            make_float4(v.x * wgt, v.y * wgt, v.z * wgt, v.w * wgt);
+      }
     }
     lds_barrier();
   }
@@ -817,12 +872,13 @@ static int gm_grid(int items_upper) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
   const int cap = 2 * cus;  // two blocks per compute unit
-  return items_upper < 1 ? 1 : (items_upper < cap ? items_upper : cap);
+  const int g = items_upper < 1 ? 1 : (items_upper < cap ? items_upper : cap);
+  return (g + 7) & ~7;  // a multiple of the 8 XCDs (the item order relies on it)
 }
 
 hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
   if (a.H == 128 * 16 && a.F % 128 == 0) {
-    gateup_gemm_kernel<16><<<gm_grid(pf_tiles_upper(a) * (a.F / 128)), kPfThreads, 0, s>>>(a);
+    gateup_gemm_kernel<16><<<gm_grid(pf_tiles_upper(a) * (a.F / 128)), kGmThreads, 0, s>>>(a);
     return hipGetLastError();
   }
   gateup_prefill_kernel<<<pf_grid(pf_tiles_upper(a) * (a.F / kPfCols)), kPfThreads, 0, s>>>(a);
@@ -831,7 +887,7 @@ hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
 
 hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
   if (a.F == 128 * 4 && a.H % 256 == 0) {
-    down_gemm_kernel<4><<<gm_grid(pf_tiles_upper(a) * (a.H / 256)), kPfThreads, 0, s>>>(a);
+    down_gemm_kernel<4><<<gm_grid(pf_tiles_upper(a) * (a.H / 256)), kGmThreads, 0, s>>>(a);
     return hipGetLastError();
   }
   down_prefill_kernel<<<pf_grid(pf_tiles_upper(a) * (a.H / kPfCols)), kPfThreads, 0, s>>>(a);
