@@ -4,7 +4,7 @@
 // bf16(r' / sqrt(mean(r'^2) + eps)) that feeds the next layer.  One launch
 // sums every expert of the call ("Models and backends", What was tuned); a
 // fixed summation order keeps the bits independent of scheduling.  One
-// 256-thread block owns one token row, so the row's sum of squares is a
+// 512-thread block owns one token row, so the row's sum of squares is a
 // block reduction in a fixed order.
 #include <math.h>
 
@@ -12,7 +12,9 @@
 
 namespace moe {
 
-constexpr int kCombineChunks = 8;  // float4 chunks per thread: H <= 8192
+constexpr int kCombineThreads = 512;
+constexpr int kCombineChunks = 4;  // float4 chunks per thread: H <= 8192
+constexpr int kCombineSlots = 16;  // top-k slots summed from registers (K <= 16)
 
 MOE_DEV void add4(float4 &a, const float4 &b) {
   a.x += b.x;
@@ -21,37 +23,39 @@ MOE_DEV void add4(float4 &a, const float4 &b) {
   a.w += b.w;
 }
 
-__global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
-  __shared__ float wave_sq[4];
-  __shared__ int rows[64];  // this token's K row indices (K <= 64)
+// One block per token row.  With K <= kCombineSlots every row of a chunk is
+// requested at once (the slot rows are block-uniform, read through the
+// scalar cache), then added in slot order.
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
+  __shared__ float wave_sq[kCombineThreads / 64];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int n4 = a.H / 4;
-  if (tid < a.K) rows[tid] = a.inv_pos[static_cast<size_t>(t) * a.K + tid];
-  lds_barrier();
+  const int K = a.K;
+  const int32_t *inv = a.inv_pos + static_cast<size_t>(t) * K;
   float4 r[kCombineChunks];
   float sq = 0.f;
 #pragma unroll
   for (int i = 0; i < kCombineChunks; ++i) {
-    const int c = tid + 256 * i;
+    const int c = tid + kCombineThreads * i;
     if (c >= n4) break;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int k = 0;
-    // groups of four independent row loads, summed in slot order
-    for (; k + 4 <= a.K; k += 4) {
-      float4 v[4];
+    if (K <= kCombineSlots) {
+      float4 v[kCombineSlots];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = rows[k + m];
-        v[m] = row >= 0 ? reinterpret_cast<const float4 *>(a.rows_out + static_cast<size_t>(row) * a.H)[c]
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < kCombineSlots; ++k) {
+        const int row = k < K ? inv[k] : -1;
+        const float4 x = reinterpret_cast<const float4 *>(a.rows_out + static_cast<size_t>(row < 0 ? 0 : row) * a.H)[c];
+        v[k] = row >= 0 ? x : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) add4(acc, v[m]);
-    }
-    for (; k < a.K; ++k) {
-      const int row = rows[k];
-      if (row >= 0) add4(acc, reinterpret_cast<const float4 *>(a.rows_out + static_cast<size_t>(row) * a.H)[c]);
+      for (int k = 0; k < kCombineSlots; ++k)
+        if (k < K) add4(acc, v[k]);
+    } else {
+      for (int k = 0; k < K; ++k) {
+        const int row = inv[k];
+        if (row >= 0) add4(acc, reinterpret_cast<const float4 *>(a.rows_out + static_cast<size_t>(row) * a.H)[c]);
+      }
     }
     const size_t o4 = static_cast<size_t>(t) * n4 + c;
     if (a.shared_out) add4(acc, reinterpret_cast<const float4 *>(a.shared_out)[o4]);
@@ -76,11 +80,13 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
   sq = sum64(sq);
   if ((tid & 63) == 0) wave_sq[tid >> 6] = sq;
   lds_barrier();
-  const float total = ((wave_sq[0] + wave_sq[1]) + wave_sq[2]) + wave_sq[3];
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) total += wave_sq[w];
   const float inv_rms = 1.f / sqrtf(total / static_cast<float>(a.H) + a.eps);
 #pragma unroll
   for (int i = 0; i < kCombineChunks; ++i) {
-    const int c = tid + 256 * i;
+    const int c = tid + kCombineThreads * i;
     if (c >= n4) break;
     const size_t o4 = static_cast<size_t>(t) * n4 + c;
     const uint16_t b0 = f32_to_bf16_rne(r[i].x * inv_rms);
@@ -95,7 +101,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  combine_kernel<<<a.T, 256, 0, s>>>(a);
+  combine_kernel<<<a.T, kCombineThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -260,14 +260,15 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
       const int i = tid + b * blockDim.x;
       xv[b] = i < T * pieces ? reinterpret_cast<const uint4 *>(a.x)[i] : make_uint4(0, 0, 0, 0);
     }
-    // every block routes the batch (block 0 also publishes it)
+    // every block routes the batch (the last block, which has the fewest
+    // items, also publishes it)
     const int npl = (a.route.E + 63) / 64;
     if (npl <= 1)
-      route_in_block_small<1>(a.route, L, blockIdx.x == 0);
+      route_in_block_small<1>(a.route, L, blockIdx.x == gridDim.x - 1);
     else if (npl <= 2)
-      route_in_block_small<2>(a.route, L, blockIdx.x == 0);
+      route_in_block_small<2>(a.route, L, blockIdx.x == gridDim.x - 1);
     else
-      route_in_block_small<4>(a.route, L, blockIdx.x == 0);  // E <= 256 on this path
+      route_in_block_small<4>(a.route, L, blockIdx.x == gridDim.x - 1);  // E <= 256 on this path
     U = L.n_active;
   } else {
     U = routed_units(a);

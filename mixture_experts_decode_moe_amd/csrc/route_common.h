@@ -270,19 +270,21 @@ MOE_DEV void route_in_block_small(const RouteFusedArgs &a, RouteLds &L, bool pub
 #pragma unroll
     for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
     for (int s0 = 0; s0 < S; s0 += 4) {
+      // every request of the batch at once (clamped, unconditional), then
+      // the slices added in order
       float pv[NPL][4];
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int ex = lane + 64 * j;
-          pv[j][q] = (ex < E && s0 + q < S) ? part[(static_cast<size_t>(s0 + q) * T + t) * E + ex] : 0.f;
+          const int ex = min(lane + 64 * j, E - 1);
+          const int sl = min(s0 + q, S - 1);
+          pv[j][q] = part[(static_cast<size_t>(sl) * T + t) * E + ex];
         }
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (s0 + q < S) acc[j] += pv[j][q];
+        for (int q = 0; q < 4; ++q) acc[j] += (s0 + q < S) ? pv[j][q] : 0.f;
     }
     float v[NPL];
 #pragma unroll
