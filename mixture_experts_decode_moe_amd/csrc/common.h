@@ -150,10 +150,9 @@ struct FfnArgs {
   float *rows_out;          // [n_rows + (Fs ? T : 0)][H]
   int32_t max_units;        // upper bound of routed units (grid sizing)
   // decode layer calls (E <= 256): the gate/up kernel routes the batch
-  // itself from the router's partial logits and its block 0 publishes the
-  // routing (the
-  // offsets, active, n_active, row_tok and row_w above point at the same
-  // buffers for the kernels that follow)
+  // itself from the router's partial logits and its last block publishes
+  // the routing (the offsets, active, n_active, row_tok and row_w above
+  // point at the same buffers for the kernels that follow)
   int32_t route_here;
   RouteFusedArgs route;
 };

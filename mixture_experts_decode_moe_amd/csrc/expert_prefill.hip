@@ -433,10 +433,6 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 
 typedef __attribute__((address_space(1))) const u32x2_t gu2_t;
 
-MOE_DEV uint4 load16_g(gchar_t *p) {
-  const u32x4_t v = *reinterpret_cast<gu32x4_t *>(p);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // An empty volatile statement that takes the value in registers: volatile
 // statements keep their order, so each scaled accumulation happens where it

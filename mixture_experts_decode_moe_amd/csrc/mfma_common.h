@@ -157,6 +157,11 @@ MOE_DEV gchar_t *uniform_gptr(const void *p) {
   return reinterpret_cast<gchar_t *>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+MOE_DEV uint4 load16_g(gchar_t *p) {
+  const u32x4_t v = *reinterpret_cast<gu32x4_t *>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 MOE_DEV uint4 load_stream16_g(gchar_t *p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t *>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
