@@ -50,22 +50,24 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload, stage):
-    """HBM bytes per launch of a stage's kernel from the committed counter
-    runs (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a
-    plain copy of known size), or None when there is no such run or the
-    kernel's source has changed since it was taken."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of a kernel from the committed counter runs
+    (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE scaled by a plain
+    copy of known size), or None when there is no such run or a source file
+    the kernel is built from has changed since it was taken."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
-            rec = json.load(f)
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
-                return None
+            rec = json.load(f)["kernels"][kernel]
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sha256"]:
+            return None
+        return rec["bytes_per_launch"].get(workload)
     except (OSError, ValueError, KeyError):
         return None
-    kernel = {"gateup": "gateup_mfma_kernel", "down": "down_mfma_kernel"}[stage]
-    return rec.get("bytes_per_launch", {}).get(workload, {}).get(kernel)
 
 
 def expert_bytes(fmt, H, F):
@@ -293,6 +295,24 @@ def main():
     dom = max(kern, key=lambda k: kern[k][1])
     dom_bytes, dom_us = kern[dom]
     achieved_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    prefill = T > 16
+    kernel_name = {("gateup", False): "gateup_mfma_kernel", ("down", False): "down_mfma_kernel",
+                   ("gateup", True): "gateup_gemm_kernel", ("down", True): "down_gemm_kernel"}[(dom, prefill)]
+    if prefill:
+        # useful matrix-core work of the dominant grouped GEMM: every routed
+        # and shared row through gate+up (2 H F each, 2 flops a product) or
+        # down (H F), padding and the hi/lo split not counted
+        rows = T * K + (T if shape.shared_ffn else 0)
+        flops = {"gateup": 2.0 * rows * 2 * H * F, "down": 2.0 * rows * H * F}[dom]
+        achieved_tf = flops / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved_tf / BF16_PEAK_TFLOPS, "traffic": measured_traffic(args.workload, kernel_name),
+                    "kernel": kernel_name, "kernel_us": dom_us, "kernel_flops": flops, "kernel_bytes": dom_bytes,
+                    "stage_us": stage_us}
+    else:
+        roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload, kernel_name),
+                    "kernel": kernel_name, "kernel_us": dom_us, "kernel_bytes": dom_bytes, "stage_us": stage_us}
     # whole-layer algorithmic bytes (router + unique experts + shared + x + y)
     layer_bytes = E * H * 4 + U * (gu_bytes + dn_bytes) + sh_gu + sh_dn + T * H * 2 + T * H * 4
     tokens_per_s = T * n_calls_per_step / (ms_per_step * 1e-3)
@@ -324,7 +344,7 @@ def main():
         log(f"oracle: {n_tok} tokens in {dt:.1f} s on {threads} threads")
 
     out = {
-        "metric": "MoE-layer tokens/s (+ achieved HBM GB/s of the dominant kernel)",
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA % (prefill), 1 GPU",
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -340,11 +360,7 @@ def main():
                    "ffn": F, "shared_ffn": shape.shared_ffn, "layers_per_step": n_calls_per_step,
                    "distinct_layer_instances": len(dev_layers),
                    "unique_experts_per_call": U, "layer_GBps": layer_bytes / (ms_per_step / n_calls_per_step * 1e-3) / 1e9},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.workload, dom) if T <= 16 else None,
-                     "kernel": dom, "kernel_us": dom_us, "kernel_bytes": dom_bytes,
-                     "stage_us": stage_us},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
