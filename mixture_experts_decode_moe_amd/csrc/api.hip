@@ -9,6 +9,13 @@
 using namespace moe;
 
 namespace {
+thread_local LaunchEvents t_launch_events;
+}  // namespace
+
+// the profiling hook's events for the next expert-kernel launch
+LaunchEvents &moe::launch_events() { return t_launch_events; }
+
+namespace {
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
@@ -56,14 +63,24 @@ constexpr size_t kControlBytes = 256;  // control words kept zero between calls
 constexpr int kStages = MOE_STAGE_COMBINE + 1;
 hipEvent_t g_prof_start[kStages] = {}, g_prof_stop[kStages] = {};
 
+// A stage's events: the stage's expert kernel, when it has one, records
+// them itself at its own start and end (launch_kernel); otherwise they
+// bracket the stage's launches here.
 struct StageMark {
   int32_t stage;
   hipStream_t s;
   StageMark(int32_t st, hipStream_t str) : stage(st), s(str) {
-    if (g_prof_start[stage]) (void)hipEventRecord(g_prof_start[stage], s);
+    if (g_prof_start[stage]) {
+      (void)hipEventRecord(g_prof_start[stage], s);
+      t_launch_events = LaunchEvents{g_prof_start[stage], g_prof_stop[stage]};
+    }
   }
   ~StageMark() {
-    if (g_prof_stop[stage]) (void)hipEventRecord(g_prof_stop[stage], s);
+    if (g_prof_stop[stage] && t_launch_events.stop == g_prof_stop[stage]) {
+      // no expert kernel took the events
+      t_launch_events = LaunchEvents{};
+      (void)hipEventRecord(g_prof_stop[stage], s);
+    }
   }
 };
 

@@ -1,6 +1,7 @@
 // Device helpers shared by the HIP kernels (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -174,5 +175,27 @@ struct CombineArgs {
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+// Events of the profiling hook for the next expert-kernel launch of a stage
+// (both null when nothing is profiled): that launch has the runtime record
+// them at the kernel's own start and end, so the interval is the kernel's
+// execution time without the launch gap.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents &launch_events();
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                         Args... args) {
+  LaunchEvents &ev = launch_events();
+  if (ev.start) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.start, ev.stop, 0u, args...);
+    ev = LaunchEvents{};
+  } else {
+    kernel<<<grid, block, lds, s>>>(args...);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace moe

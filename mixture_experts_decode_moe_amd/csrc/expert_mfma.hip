@@ -634,8 +634,7 @@ static hipError_t launch_gateup_mfma_t(const FfnArgs &a, int ks, hipStream_t s) 
   const int cus = cu_count();
   int grid = (items + kGuTable - 1) / kGuTable;
   if (grid < cus) grid = items < cus ? (items < 1 ? 1 : items) : cus;
-  gateup_mfma_kernel<FMT, JW, D><<<grid, 64 * ks, lds, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(gateup_mfma_kernel<FMT, JW, D>, dim3(grid), dim3(64 * ks), lds, s, a);
 }
 
 template <int FMT>
@@ -654,12 +653,11 @@ static hipError_t launch_down_mfma_f(const FfnArgs &a, hipStream_t s) {
   const int tiles = a.H / 64;
   const int grid = mfma_grid((a.Fs > 0 ? tiles : 0) + a.max_units * tiles);
   if (jw == 1)
-    down_mfma_kernel<FMT, 1><<<grid, 64 * ks, 0, s>>>(a);
+    return launch_kernel(down_mfma_kernel<FMT, 1>, dim3(grid), dim3(64 * ks), 0, s, a);
   else if (jw == 2)
-    down_mfma_kernel<FMT, 2><<<grid, 64 * ks, 0, s>>>(a);
+    return launch_kernel(down_mfma_kernel<FMT, 2>, dim3(grid), dim3(64 * ks), 0, s, a);
   else
-    down_mfma_kernel<FMT, 4><<<grid, 64 * ks, 0, s>>>(a);
-  return hipGetLastError();
+    return launch_kernel(down_mfma_kernel<FMT, 4>, dim3(grid), dim3(64 * ks), 0, s, a);
 }
 
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t s) {

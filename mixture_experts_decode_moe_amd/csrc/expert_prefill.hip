@@ -874,20 +874,20 @@ static int gm_grid(int items_upper) {
 
 hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
   if (a.H == 128 * 16 && a.F % 128 == 0) {
-    gateup_gemm_kernel<16><<<gm_grid(pf_tiles_upper(a) * (a.F / 128)), kGmThreads, 0, s>>>(a);
-    return hipGetLastError();
+    return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128))), dim3(kGmThreads), 0,
+                         s, a);
   }
-  gateup_prefill_kernel<<<pf_grid(pf_tiles_upper(a) * (a.F / kPfCols)), kPfThreads, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(gateup_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.F / kPfCols))), dim3(kPfThreads), 0,
+                       s, a);
 }
 
 hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
   if (a.F == 128 * 4 && a.H % 256 == 0) {
-    down_gemm_kernel<4><<<gm_grid(pf_tiles_upper(a) * (a.H / 256)), kGmThreads, 0, s>>>(a);
-    return hipGetLastError();
+    return launch_kernel(down_gemm_kernel<4>, dim3(gm_grid(pf_tiles_upper(a) * (a.H / 256))), dim3(kGmThreads), 0, s,
+                         a);
   }
-  down_prefill_kernel<<<pf_grid(pf_tiles_upper(a) * (a.H / kPfCols)), kPfThreads, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(down_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.H / kPfCols))), dim3(kPfThreads), 0,
+                       s, a);
 }
 
 }  // namespace moe
