@@ -20,12 +20,13 @@ MOE_DEV float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 MOE_DEV float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// float32 -> bfloat16, round to nearest even (NaN kept quiet).
-MOE_DEV uint16_t f32_to_bf16_rne(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((b >> 16) | 0x40u);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return static_cast<uint16_t>(b >> 16);
+// float32 -> bfloat16, round to nearest even: the chip's own conversion
+// (v_cvt_pk_bf16_f32), two values an instruction when paired.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
+MOE_DEV uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 MOE_DEV float f16_bits_to_f32(uint16_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, h)); }

@@ -468,12 +468,59 @@ MOE_DEV void with_msub(int msub, Fn &&fn) {
 }
 
 constexpr int kGmThreads = 512;  // 8 waves; two blocks per compute unit
+constexpr int kGmMaxUnits = 257;  // the shared expert and up to 256 routed experts
+
+// The call's units in LDS, filled once per block: pre[u] = first row tile of
+// unit u (pre[n] = the total), and each unit's expert (-1: shared), first
+// row and row count, so that an item needs no global lookup before its
+// weight requests.
+struct GmUnits {
+  int pre[kGmMaxUnits + 1];
+  int e[kGmMaxUnits], r0[kGmMaxUnits], n[kGmMaxUnits];
+};
+
+MOE_DEV int gm_units(const FfnArgs &a, GmUnits &G, int *scratch) {
+  static_assert(kGmThreads >= kGmMaxUnits, "one unit per thread");
+  const int n_units = (a.Fs > 0 ? 1 : 0) + routed_units(a);
+  const int tid = threadIdx.x;
+  int c = 0;
+  if (tid < n_units) {
+    const PfUnit x = pf_unit(a, tid);
+    G.e[tid] = x.e;
+    G.r0[tid] = x.r0;
+    G.n[tid] = x.n;
+    c = x.n > 0 ? (x.n + kPfRows - 1) / kPfRows : 0;
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  int inc = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  lds_barrier();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += scratch[w];
+  base += inc - c;
+  if (tid <= n_units) G.pre[tid] = base;
+  lds_barrier();
+  return n_units;
+}
+
+MOE_DEV PfUnit gm_unit(const GmUnits &G, int u) {
+  PfUnit x;
+  x.e = G.e[u];
+  x.r0 = G.r0[u];
+  x.n = G.n[u];
+  return x;
+}
 
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
   __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted, one k-step
-  __shared__ int pre[kPfMaxUnits + 1];
+  __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
   const int tid = threadIdx.x;
@@ -482,9 +529,9 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int T = a.T;
   const int H = 128 * KS;
-  const int n_units = pf_tiles<kGmThreads>(a, pre, scratch);
+  const int n_units = gm_units(a, units, scratch);
   const int col_tiles = a.F / 128;
-  const int n_items = pre[n_units] * col_tiles;
+  const int n_items = units.pre[n_units] * col_tiles;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t c136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
   const int pc = tid & 15;
@@ -500,9 +547,9 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
     if (item >= n_items) continue;
     const int j = item / col_tiles;
     const int ct = item - j * col_tiles;
-    const int u = pf_find(pre, n_units, j);
-    const PfUnit un = pf_unit(a, u);
-    const int m0 = (j - pre[u]) * kPfRows;
+    const int u = pf_find(units.pre, n_units, j);
+    const PfUnit un = gm_unit(units, u);
+    const int m0 = (j - units.pre[u]) * kPfRows;
     const int rows = min(kPfRows, un.n - m0);
     const bool shared = un.e < 0;
     const int F = shared ? a.Fs : a.F;
@@ -640,14 +687,21 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; i += 2) {
+        // rows r and r + 1 converted in pairs
         const int r = 16 * mt + 4 * g + i;
-        const float gv = acc[0][mt][i], uv = acc[1][mt][i];
-        const float v = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
-        const uint16_t hi = f32_to_bf16_rne(v);
-        const uint16_t lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
-        st[r * kStRow + cl] = hi;
-        st[r * kStRow + kStPlane + cl] = lo;
+        float v[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const float gv = acc[0][mt][i + d], uv = acc[1][mt][i + d];
+          v[d] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
+        }
+        const uint32_t hi = f32x2_to_bf16x2_rne(v[0], v[1]);
+        const uint32_t lo = f32x2_to_bf16x2_rne(v[0] - bf16_lo(hi), v[1] - bf16_hi(hi));
+        st[r * kStRow + cl] = static_cast<uint16_t>(hi);
+        st[(r + 1) * kStRow + cl] = static_cast<uint16_t>(hi >> 16);
+        st[r * kStRow + kStPlane + cl] = static_cast<uint16_t>(lo);
+        st[(r + 1) * kStRow + kStPlane + cl] = static_cast<uint16_t>(lo >> 16);
       }
     lds_barrier();
     // 16-byte stores of whole row segments: piece (row, plane, 16 of them)
@@ -672,7 +726,7 @@ template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
   __shared__ uint4 as[2][2][kPfRows][17];  // [buffer][hi, lo plane] act rows, one k-step
-  __shared__ int pre[kPfMaxUnits + 1];
+  __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
   const int tid = threadIdx.x;
@@ -680,9 +734,9 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   const int lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
   const int H = a.H;
-  const int n_units = pf_tiles<kGmThreads>(a, pre, scratch);
+  const int n_units = gm_units(a, units, scratch);
   const int col_tiles = H / 256;
-  const int n_items = pre[n_units] * col_tiles;
+  const int n_items = units.pre[n_units] * col_tiles;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t c136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
   const int pc = tid & 15;
@@ -698,9 +752,9 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
     if (item >= n_items) continue;
     const int j = item / col_tiles;
     const int ct = item - j * col_tiles;
-    const int u = pf_find(pre, n_units, j);
-    const PfUnit un = pf_unit(a, u);
-    const int m0 = (j - pre[u]) * kPfRows;
+    const int u = pf_find(units.pre, n_units, j);
+    const PfUnit un = gm_unit(units, u);
+    const int m0 = (j - units.pre[u]) * kPfRows;
     const int rows = min(kPfRows, un.n - m0);
     const bool shared = un.e < 0;
     const int F = shared ? a.Fs : a.F;  // == 128 KS
@@ -872,8 +926,12 @@ static int gm_grid(int items_upper) {
   return (g + 7) & ~7;  // a multiple of the 8 XCDs (the item order relies on it)
 }
 
+static bool gm_units_fit(const FfnArgs &a) {
+  return (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1) <= kGmMaxUnits;
+}
+
 hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
-  if (a.H == 128 * 16 && a.F % 128 == 0) {
+  if (a.H == 128 * 16 && a.F % 128 == 0 && gm_units_fit(a)) {
     return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128))), dim3(kGmThreads), 0,
                          s, a);
   }
@@ -882,7 +940,7 @@ hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
-  if (a.F == 128 * 4 && a.H % 256 == 0) {
+  if (a.F == 128 * 4 && a.H % 256 == 0 && gm_units_fit(a)) {
     return launch_kernel(down_gemm_kernel<4>, dim3(gm_grid(pf_tiles_upper(a) * (a.H / 256))), dim3(kGmThreads), 0, s,
                          a);
   }
