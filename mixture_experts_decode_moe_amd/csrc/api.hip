@@ -91,6 +91,7 @@ struct LayerWs {
   int32_t *ids;
   float *w;
   int32_t *counts, *offsets, *active, *n_active, *row_tok, *inv_pos, *rank, *tile_hist;
+  int32_t *units;  // [E][4]: expert, first row, rows, 0 of each active unit
   float *row_w;
   float *act, *rows_out;
   size_t bytes;
@@ -118,6 +119,7 @@ LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
   w.inv_pos = c.take<int32_t>(TK);
   w.rank = c.take<int32_t>(TK);
   w.tile_hist = c.take<int32_t>(n_tiles * E);
+  w.units = c.take<int32_t>(4 * E);
   // SwiGLU rows and expert output rows: the routed rows, then (with a shared
   // expert) its T rows
   const size_t Fs = L->shared.n_experts == 1 ? L->shared.ffn : 0;
@@ -373,6 +375,7 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
     fa.active = w.active;
     fa.n_active = w.n_active;
     fa.row_w = w.row_w;
+    fa.units = w.units;
     xa.route_here = (mfma_decode_ok(xa) && E <= 256) ? 1 : 0;
     xa.route = fa;
     StageMark m(MOE_STAGE_ROUTE, s);
@@ -410,6 +413,17 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
     e = launch_gateup(xa, s);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (xa.route_here && (!res || !res->normed_out) && down_combine_ok(xa, K)) {
+    // a few tokens: down projection and combine in one launch
+    DownCombineArgs d{xa, w.units, w.inv_pos, K, E, y, res ? res->residual_in : nullptr,
+                      res ? res->residual_out : nullptr};
+    {
+      StageMark m(MOE_STAGE_DOWN, s);
+      e = launch_down_combine(d, s);
+    }
+    StageMark m(MOE_STAGE_COMBINE, s);  // no launch of its own
+    return hip_status(e);
+  }
   {
     StageMark m(MOE_STAGE_DOWN, s);
     e = launch_down(xa, s);

@@ -115,6 +115,7 @@ struct RouteFusedArgs {
   float *part;        // [S][T][E] partial logits
   int32_t *counts, *offsets, *row_tok, *inv_pos, *active, *n_active;
   float *row_w;
+  int32_t *units;     // [E] int4 (expert, first row, rows, 0) per active unit, or NULL
 };
 hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s);    // partials + selection
 hipError_t launch_route_partial(const RouteFusedArgs &a, hipStream_t s);  // partials only
@@ -161,6 +162,20 @@ struct FfnArgs {
 hipError_t launch_gateup(const FfnArgs &a, hipStream_t s);
 bool mfma_decode_ok(const FfnArgs &a);  // the decode matrix-core kernels take this call
 hipError_t launch_down(const FfnArgs &a, hipStream_t s);
+
+// Down projection and combine in one launch (decode layer calls of a few
+// tokens after the matrix-core gate/up kernel has published the routing).
+struct DownCombineArgs {
+  FfnArgs f;
+  const int32_t *units;    // [max_units] int4 records (expert, first row, rows, 0)
+  const int32_t *inv_pos;  // [T][K] permuted row of each slot
+  int32_t K, E;
+  float *y;                     // [T][H]
+  const uint16_t *residual_in;  // with residual_out
+  uint16_t *residual_out;       // NULL: no residual epilogue
+};
+bool down_combine_ok(const FfnArgs &a, int K);
+hipError_t launch_down_combine(const DownCombineArgs &d, hipStream_t s);
 
 struct CombineArgs {
   const float *rows_out;

@@ -249,20 +249,32 @@ MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) 
   lds_barrier();
 }
 
-// The same routing for E <= 256 (NPL <= 4) with fewer block-wide steps:
-// each token's wave builds the token's expert bitmask, one wave derives the
-// counts, offsets and active list from the masks, then every thread places
-// pairs.  Results are identical to route_in_block's.
+// Inclusive sum over the wave: four row shifts give each 16-lane row's
+// running sum, two row broadcasts carry the sums of the earlier rows.
+MOE_DEV int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// The same routing for E <= 256 (NPL <= 4) in three phases with fewer
+// block-wide steps: each token's wave takes the token's top-k and builds
+// its expert bitmask (route_small_topk); wave 0 derives the counts,
+// offsets and active list from the masks (route_small_scan); every thread
+// then places pairs (route_small_rows).  The phases are separated by block
+// barriers, so a caller can start work that needs only the active list
+// before the rows are placed.  Results are identical to route_in_block's.
 template <int NPL>
-MOE_DEV void route_in_block_small(const RouteFusedArgs &a, RouteLds &L, bool publish) {
+MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish) {
   static_assert(NPL <= 4, "E <= 256");
-  const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int nw = nthr >> 6;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
   const int T = a.T, E = a.E, S = a.S, K = a.K;
-  const int TK = T * K;
   const int mwords = (E + 31) / 32;  // <= 8
   for (int t = wave; t < T; t += nw) {
     const float *__restrict__ part = a.part;
@@ -310,62 +322,64 @@ MOE_DEV void route_in_block_small(const RouteFusedArgs &a, RouteLds &L, bool pub
       atomicOr(&L.mask[t][my_e >> 5], 1u << (my_e & 31));
     }
   }
-  lds_barrier();
-  if (wave == 0) {
-    // lane l owns the experts 4l .. 4l+3 (one mask word)
-    int c[4] = {0, 0, 0, 0};
-    const int word = (4 * lane) >> 5, sh = (4 * lane) & 31;
-    if (4 * lane < E) {
-      for (int t = 0; t < T; ++t) {
-        const uint32_t m = L.mask[t][word] >> sh;
+}
+
+// Wave 0 only, after route_small_topk and a block barrier.
+MOE_DEV void route_small_scan(const RouteFusedArgs &a, RouteLds &L, bool publish) {
+  const int lane = threadIdx.x & 63;
+  const int T = a.T, E = a.E;
+  // lane l owns the experts 4l .. 4l+3 (one mask word)
+  int c[4] = {0, 0, 0, 0};
+  const int word = (4 * lane) >> 5, sh = (4 * lane) & 31;
+  if (4 * lane < E) {
+    for (int t = 0; t < T; ++t) {
+      const uint32_t m = L.mask[t][word] >> sh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] += (m >> i) & 1u;
-      }
-    }
-    int n_here = 0, nz_here = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (4 * lane + i >= E) c[i] = 0;
-      n_here += c[i];
-      nz_here += c[i] > 0;
-    }
-    int inc = n_here, incz = nz_here;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(inc, off), oz = __shfl_up(incz, off);
-      if (lane >= off) {
-        inc += o;
-        incz += oz;
-      }
-    }
-    int base = inc - n_here, abase = incz - nz_here;
-    const int total = __shfl(inc, 63), n_act = __shfl(incz, 63);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ex = 4 * lane + i;
-      if (ex < E) {
-        L.cnt[ex] = c[i];
-        L.off[ex] = base;
-        if (c[i] > 0) L.active[abase] = ex;
-        if (publish) {
-          a.counts[ex] = c[i];
-          a.offsets[ex] = base;
-          if (c[i] > 0) a.active[abase] = ex;
-        }
-        abase += c[i] > 0;
-      }
-      base += c[i];
-    }
-    if (lane == 0) {
-      L.n_active = n_act;
-      if (publish) {
-        a.offsets[E] = total;
-        *a.n_active = n_act;
-      }
+      for (int i = 0; i < 4; ++i) c[i] += (m >> i) & 1u;
     }
   }
-  lds_barrier();
-  for (int p = tid; p < TK; p += nthr) {
+  int n_here = 0, nz_here = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * lane + i >= E) c[i] = 0;
+    n_here += c[i];
+    nz_here += c[i] > 0;
+  }
+  const int inc = wave_incl_sum(n_here), incz = wave_incl_sum(nz_here);
+  int base = inc - n_here, abase = incz - nz_here;
+  const int total = __builtin_amdgcn_readlane(inc, 63), n_act = __builtin_amdgcn_readlane(incz, 63);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = 4 * lane + i;
+    if (ex < E) {
+      L.cnt[ex] = c[i];
+      L.off[ex] = base;
+      if (c[i] > 0) L.active[abase] = ex;
+      if (publish) {
+        a.counts[ex] = c[i];
+        a.offsets[ex] = base;
+        if (c[i] > 0) {
+          a.active[abase] = ex;
+          if (a.units) reinterpret_cast<int4 *>(a.units)[abase] = make_int4(ex, base, c[i], 0);
+        }
+      }
+      abase += c[i] > 0;
+    }
+    base += c[i];
+  }
+  if (lane == 0) {
+    L.n_active = n_act;
+    if (publish) {
+      a.offsets[E] = total;
+      *a.n_active = n_act;
+    }
+  }
+}
+
+// Every thread, after route_small_scan and a block barrier.
+MOE_DEV void route_small_rows(const RouteFusedArgs &a, RouteLds &L, bool publish) {
+  const int K = a.K, TK = a.T * a.K;
+  for (int p = threadIdx.x; p < TK; p += blockDim.x) {
     // rank inside the expert = earlier tokens that picked it
     const int ex = L.ids[p];
     const int t = p / K;
@@ -379,6 +393,15 @@ MOE_DEV void route_in_block_small(const RouteFusedArgs &a, RouteLds &L, bool pub
       a.inv_pos[p] = pos;
     }
   }
+}
+
+template <int NPL>
+MOE_DEV void route_in_block_small(const RouteFusedArgs &a, RouteLds &L, bool publish) {
+  route_small_topk<NPL>(a, L, publish);
+  lds_barrier();
+  if ((threadIdx.x >> 6) == 0) route_small_scan(a, L, publish);
+  lds_barrier();
+  route_small_rows(a, L, publish);
   lds_barrier();
 }
 

@@ -58,7 +58,7 @@ def rel_max_err(y, ref):
     return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
-def run_layer(dlayer, x_dev, T, ws=None, residual=None, with_logits=True):
+def run_layer(dlayer, x_dev, T, ws=None, residual=None, with_logits=True, normed=True):
     """Runs moe_layer_forward; also runs moe_route on the same input (same
     kernels) to read the GPU's fp32 logits."""
     from mixture_experts_decode_moe_amd import binding as mb
@@ -72,8 +72,8 @@ def run_layer(dlayer, x_dev, T, ws=None, residual=None, with_logits=True):
     if residual is not None:
         # residual: the bf16 residual stream entering the layer (device)
         r_out = torch.empty((T, H), dtype=torch.int16, device="cuda")
-        normed = torch.empty((T, H), dtype=torch.int16, device="cuda")
-        res = mb.residual(residual, r_out, normed)
+        n_out = torch.empty((T, H), dtype=torch.int16, device="cuda") if normed else None
+        res = mb.residual(residual, r_out, n_out)
     mb.layer_forward(dlayer, x_dev, y, ws, res=res, topk_ids=ids, topk_w=w)
     out = {}
     if with_logits:
@@ -90,7 +90,8 @@ def run_layer(dlayer, x_dev, T, ws=None, residual=None, with_logits=True):
         assert np.array_equal(w2.cpu().numpy().astype(np.float64), out["w"])
     if residual is not None:
         out["residual_out"] = host_u16(r_out)
-        out["normed_out"] = host_u16(normed)
+        if normed:
+            out["normed_out"] = host_u16(n_out)
     return out
 
 

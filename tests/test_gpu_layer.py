@@ -62,6 +62,47 @@ def test_layer_parity_token_counts(mb, T):
     say(f"T={T}: rel err {err:.2e}, near ties {ties}")
 
 
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_small_batch_one_launch_down_combine(mb, cfg):
+    """Batches of up to eight tokens run the down projection and the combine
+    as one launch, larger ones as two; a token's output must carry the same
+    bits either way (int8 and int4), and match the oracle."""
+    import parity_util as pu
+    shape = _shape(cfg, tokens=12, correlated_sigma=0.0, seed=70 + cfg)
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    dl = mb.layer_to_device(layer)
+    say(f"one-launch down+combine cfg{cfg}: T=12 reference")
+    full = pu.run_layer(dl, pu.dev_u16(x), 12, with_logits=False)
+    for T in (1, 2, 5, 8):
+        say(f"  T={T}")
+        part = pu.run_layer(dl, pu.dev_u16(x[:T]), T)
+        assert np.array_equal(part["ids"], full["ids"][:T])
+        assert np.array_equal(part["y"], full["y"][:T]), f"T={T}: bits differ from the two-launch path"
+        if T == 5:
+            err, ties = pu.check_layer_against_oracle(layer, x[:T], part)
+            say(f"  T=5: rel err {err:.2e}, near ties {ties}")
+
+
+def test_small_batch_residual_without_norm(mb):
+    """The one-launch path's residual epilogue: bf16(r + y), no normalised
+    copy."""
+    import parity_util as pu
+    import oracle
+    shape = _shape(2, tokens=3, correlated_sigma=0.0, seed=77)
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    r = synth.make_x(_shape(2, tokens=3, correlated_sigma=0.0, seed=78))
+    dl = mb.layer_to_device(layer)
+    say("residual without norm, T=3")
+    gpu = pu.run_layer(dl, pu.dev_u16(x), 3, residual=pu.dev_u16(r), normed=False)
+    err, ties = pu.check_layer_against_oracle(layer, x, gpu)
+    r_ref = oracle.residual(r, gpu["y"].astype(np.float32).astype(np.float64))
+    d_r = np.abs(r_ref.astype(np.int32) - gpu["residual_out"].astype(np.int32))
+    assert d_r.max() <= 1, "residual_out differs from bf16(r + y) by more than one bf16 step"
+    say(f"  rel err {err:.2e}, near ties {ties}")
+
+
 def test_prefill_chunk_sampled(mb):
     """Config 4 at full size (2048 tokens), oracle on 64 sampled tokens."""
     import parity_util as pu
