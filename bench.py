@@ -289,14 +289,20 @@ def main():
     # experts' (+ shared expert's) weights and scales, the activations read
     # and the results written
     Fs = shape.shared_ffn
+    # decode calls of up to eight tokens without the normalised residual copy
+    # take the one-launch down projection + combine (it writes y, not the
+    # expert rows)
+    fused_down = T <= 8 and not stack
     gateup_bytes = U * gu_bytes + sh_gu + T * H * 2 + (T * K * F + T * Fs) * 4
-    down_bytes = U * dn_bytes + sh_dn + (T * K * F + T * Fs) * 4 + (T * K + (T if Fs else 0)) * H * 4
+    down_out = T * H * 4 if fused_down else (T * K + (T if Fs else 0)) * H * 4
+    down_bytes = U * dn_bytes + sh_dn + (T * K * F + T * Fs) * 4 + down_out
     kern = {"gateup": (gateup_bytes, stage_us["gateup"]), "down": (down_bytes, stage_us["down"])}
     dom = max(kern, key=lambda k: kern[k][1])
     dom_bytes, dom_us = kern[dom]
     achieved_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
     prefill = T > 16
-    kernel_name = {("gateup", False): "gateup_mfma_kernel", ("down", False): "down_mfma_kernel",
+    kernel_name = {("gateup", False): "gateup_mfma_kernel",
+                   ("down", False): "down_combine_kernel" if fused_down else "down_mfma_kernel",
                    ("gateup", True): "gateup_gemm_kernel", ("down", True): "down_gemm_kernel"}[(dom, prefill)]
     if prefill:
         # useful matrix-core work of the dominant grouped GEMM: every routed
