@@ -421,9 +421,13 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 // between iterations (a register ring copied across a loop back-edge makes
 // the compiler wait for every load).  Tiles are wider than the generic
 // kernels' (128 SwiGLU columns for gate/up, 256 output columns for down, 64
-// rows), each wave owning four 16-column weight tiles against the 16-row
-// tiles of A; the -136 sum correction of a block is one MFMA against a
-// constant operand per 16-row tile, shared by the wave's four weight tiles.
+// rows), each wave owning two 16-column weight tiles against the 16-row
+// tiles of A.  Unlike the generic kernels, these multiply in fp16: each
+// weight is dequantized once per item to the fp16 value q s (rounded once,
+// relative error at most 2^-11) and the A rows are staged in fp16 (x, and
+// the hi and lo parts of the SwiGLU rows, are bf16 values, exact in fp16
+// within its normal range), so the products accumulate in the matrix core
+// with no sum correction and no per-block scaling on the vector unit.
 //
 // The k loop is instantiated once per number of 16-row tiles that hold rows
 // (1..4), chosen per item: no matrix-core instruction sits under a branch.
@@ -519,7 +523,7 @@ MOE_DEV PfUnit gm_unit(const GmUnits &G, int u) {
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
-  __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted, one k-step
+  __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted fp16, one k-step
   __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
@@ -533,7 +537,6 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
   const int col_tiles = a.F / 128;
   const int n_items = units.pre[n_units] * col_tiles;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const u32x4_t c136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
   const int pc = tid & 15;
 
   // XCD-aware order: the blocks of one XCD (block b runs on XCD b mod 8)
@@ -586,10 +589,12 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
       for (int i = 0; i < 2; ++i) v[i] = load16_g(xg + (xoff[i] + 256u * s));
     };
     auto store_a = [&](int buf, const uint4(&v)[2]) {
+      // pair-permuted, in fp16
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const u32x4_t pp = pair_permute(v[i]);
-        as[buf][(tid >> 4) + 32 * i][pc] = make_uint4(pp.x, pp.y, pp.z, pp.w);
+        as[buf][(tid >> 4) + 32 * i][pc] = make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y),
+                                                      bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
       }
     };
     auto load_b = [&](int s, uint4(&w)[2], u32x2_t(&sc)[2]) {
@@ -629,41 +634,18 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
         for (int q = 0; q < 2; ++q) xpose4(bw[sl][q]);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          // block 4 s + p: both weight tiles' operands, then one 16-row tile
-          // of A at a time against both
+          // block 4 s + p: both weight tiles' operands (scaled, fp16), then
+          // each 16-row tile of A against both
           u32x4_t B[2];
-          float scl[2];
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            B[q] = magic_pairs(word(bw[sl][q], p));
-            scl[q] = scale4(bs[sl][q].x, bs[sl][q].y, p);
-          }
-          // products of 16-row tile mt are scaled into the accumulators
-          // after the products of tile mt + 1 are issued (the matrix core's
-          // latency overlaps the scaling)
-          f32x4_t prev[2];
+          for (int q = 0; q < 2; ++q)
+            B[q] = dequant_f16_pairs(word(bw[sl][q], p), scale_pair(bs[sl][q].x, bs[sl][q].y, p));
 #pragma unroll
           for (int mt = 0; mt < MS; ++mt) {
             const uint4 v = as[sl][16 * mt + n][4 * p + g];
             const u32x4_t A = {v.x, v.y, v.z, v.w};
-            const f32x4_t cc = mfma_bf16(A, c136, zero4);
-            f32x4_t prod[2];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) prod[q] = mfma_bf16(A, B[q], cc);
-            if (mt > 0) {
-#pragma unroll
-              for (int q = 0; q < 2; ++q) {
-                acc[q][mt - 1] = fma4(scl[q], prev[q], acc[q][mt - 1]);
-                pin(acc[q][mt - 1]);
-              }
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q) prev[q] = prod[q];
-          }
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            acc[q][MS - 1] = fma4(scl[q], prev[q], acc[q][MS - 1]);
-            pin(acc[q][MS - 1]);
+            for (int q = 0; q < 2; ++q) acc[q][mt] = mfma_f16(A, B[q], acc[q][mt]);
           }
         }
         load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);
@@ -725,7 +707,7 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
-  __shared__ uint4 as[2][2][kPfRows][17];  // [buffer][hi, lo plane] act rows, one k-step
+  __shared__ uint4 as[2][2][kPfRows][17];  // [buffer][hi, lo plane] act rows in fp16, one k-step
   __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
@@ -738,7 +720,6 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   const int col_tiles = H / 256;
   const int n_items = units.pre[n_units] * col_tiles;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const u32x4_t c136 = {kMinus136Pair, kMinus136Pair, kMinus136Pair, kMinus136Pair};
   const int pc = tid & 15;
 
   // XCD-aware order: the blocks of one XCD (block b runs on XCD b mod 8)
@@ -787,11 +768,15 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
         v[2 + i] = load16_g(ag + (aoff[i] + 2u * F + 256u * s));
       }
     };
+    auto f16x8 = [](const uint4 &v) {
+      return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
+    };
     auto store_a = [&](int buf, const uint4(&v)[4]) {
+      // both planes in fp16
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        as[buf][0][(tid >> 4) + 32 * i][pc] = v[i];
-        as[buf][1][(tid >> 4) + 32 * i][pc] = v[2 + i];
+        as[buf][0][(tid >> 4) + 32 * i][pc] = f16x8(v[i]);
+        as[buf][1][(tid >> 4) + 32 * i][pc] = f16x8(v[2 + i]);
       }
     };
     auto load_b = [&](int s, uint4(&w)[2], u32x2_t(&sc)[2]) {
@@ -829,23 +814,16 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           u32x4_t B[2];
-          float scl[2];
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            B[q] = magic_pairs(word(bw[sl][q], p));
-            scl[q] = scale4(bs[sl][q].x, bs[sl][q].y, p);
-          }
+          for (int q = 0; q < 2; ++q)
+            B[q] = dequant_f16_pairs(word(bw[sl][q], p), scale_pair(bs[sl][q].x, bs[sl][q].y, p));
 #pragma unroll
           for (int mt = 0; mt < MS; ++mt) {
             const uint4 vh = as[sl][0][16 * mt + n][4 * p + g];
             const uint4 vl = as[sl][1][16 * mt + n][4 * p + g];
             const u32x4_t Ah = {vh.x, vh.y, vh.z, vh.w}, Al = {vl.x, vl.y, vl.z, vl.w};
-            const f32x4_t cc = mfma_bf16(Al, c136, mfma_bf16(Ah, c136, zero4));
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              acc[q][mt] = fma4(scl[q], mfma_bf16(Al, B[q], mfma_bf16(Ah, B[q], cc)), acc[q][mt]);
-              pin(acc[q][mt]);
-            }
+            for (int q = 0; q < 2; ++q) acc[q][mt] = mfma_f16(Al, B[q], mfma_f16(Ah, B[q], acc[q][mt]));
           }
         }
         load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);

@@ -24,6 +24,51 @@ MOE_DEV f32x4_t mfma_bf16(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) 
                                                  c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+
+MOE_DEV f32x4_t mfma_f16(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+// A pair of bf16 (one word) -> the same pair in fp16: exact for magnitudes
+// in fp16's normal range [2^-14, 65504], rounded to nearest below it.
+MOE_DEV uint32_t bf16x2_to_f16x2(uint32_t u) {
+  const f32x2v_t f = {__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+}
+
+// Eight nibbles (one k-group of a 32-element block, stored as q + 8) and the
+// block's fp16 scale s as the pair (s, s) -> four fp16 pairs (q_i s,
+// q_{i+4} s), i = 0..3, in the pair order of magic_pairs: 0x6400 | n is
+// 1024 + n exactly, minus 1032 gives q exactly, and the product with s is
+// rounded once to fp16 (relative error at most 2^-11).
+MOE_DEV u32x4_t dequant_f16_pairs(uint32_t w, uint32_t s2) {
+  const uint32_t ev = w & 0x0F0F0F0Fu;
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t hi = 0x64646464u;
+  const uint32_t r[4] = {__builtin_amdgcn_perm(hi, ev, 0x04020400u), __builtin_amdgcn_perm(hi, od, 0x04020400u),
+                         __builtin_amdgcn_perm(hi, ev, 0x04030401u), __builtin_amdgcn_perm(hi, od, 0x04030401u)};
+  const f16x2_t off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+  const f16x2_t sc = __builtin_bit_cast(f16x2_t, s2);
+  u32x4_t out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2_t q = __builtin_bit_cast(f16x2_t, r[i]) + off;  // exact
+    out[i] = __builtin_bit_cast(uint32_t, q * sc);
+  }
+  return out;
+}
+
+// fp16 scale p (0..3) of a pair of words holding four consecutive scales,
+// as the pair (s, s)
+MOE_DEV uint32_t scale_pair(uint32_t s01, uint32_t s23, int p) {
+  const uint32_t w = p < 2 ? s01 : s23;
+  return __builtin_amdgcn_perm(w, w, (p & 1) ? 0x03020302u : 0x01000100u);
+}
+
 MOE_DEV f32x4_t mfma_bf16_k16(const u32x2_t &a, const u32x2_t &b, const f32x4_t &c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
                                                    0, 0, 0);
