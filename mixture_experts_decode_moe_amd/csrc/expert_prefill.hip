@@ -414,12 +414,17 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 }
 
 // ------------------------------------------------ pipelined GEMM variants
-// For an even number of k-steps (the model's H = 2048 for gate/up, F = 512
-// for down) the k loop runs over pairs of steps with two register slots and
-// two LDS buffers whose indices are constants: the weight chunks of the next
-// two steps and the A rows of the next one stay in flight, with no copies
-// between iterations (a register ring copied across a loop back-edge makes
-// the compiler wait for every load).  Tiles are wider than the generic
+// The k loop runs over groups of steps whose register slots and LDS buffers
+// have constant indices, with no copies between iterations (a register ring
+// copied across a loop back-edge makes the compiler wait for every load).
+// Down (F = 512: four steps) keeps the weights of the next two steps and the
+// A rows of the next one in flight, two blocks per compute unit.  Gate/up
+// (H = 2048: sixteen steps) runs one block per compute unit with 256
+// registers a lane and keeps the weights of the next four steps and the A
+// rows of the next two in flight, and reads a block's A fragments from LDS
+// together before its MFMAs (with 128 registers hipcc read and waited for
+// each fragment right before its MFMA; measured: 202 against 216 us for the
+// prefill chunk).  Tiles are wider than the generic
 // kernels' (128 SwiGLU columns for gate/up, 256 output columns for down, 64
 // rows), each wave owning two 16-column weight tiles against the 16-row
 // tiles of A.  Unlike the generic kernels, these multiply in fp16: each
@@ -521,7 +526,7 @@ MOE_DEV PfUnit gm_unit(const GmUnits &G, int u) {
 }
 
 template <int KS>
-__global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
   __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted fp16, one k-step
   __shared__ GmUnits units;
@@ -611,13 +616,19 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[q][mt] = zero4;
-    uint4 av[2];        // A rows of the next step
-    uint4 bw[2][2];     // weight chunks, slot s & 1
-    u32x2_t bs[2][2];   // their block scales
-    load_a(0, av);
+    uint4 av[2][2];     // A rows of the next two steps, slot s & 1
+    uint4 bw[4][2];     // weight chunks, slot s & 3
+    u32x2_t bs[4][2];   // their block scales
+    // B(0), A(0), B(1): once A(0) has arrived, B(0) has too (the counter of
+    // outstanding loads drains in order) and only B(1) is pending, as at the
+    // top of every later pair of steps
     load_b(0, bw[0], bs[0]);
+    load_a(0, av[0]);
     load_b(1, bw[1], bs[1]);
-    store_a(0, av);
+    load_b(2, bw[2], bs[2]);
+    load_b(3, bw[3], bs[3]);
+    load_a(1, av[1]);
+    store_a(0, av[0]);
     lds_barrier();
     with_msub((rows + 15) >> 4, [&](auto msc) __attribute__((always_inline)) {
       constexpr int MS = decltype(msc)::value;
@@ -629,7 +640,7 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
         for (int i = 0; i < 2; ++i) pin_u32(xoff[i]);
         // unconditional (clamped) requests keep the register slots out of
         // scratch memory; past the end they re-read the last step
-        load_a(min(s + 1, KS - 1), av);  // A(s) is in LDS already
+        load_a(min(s + 2, KS - 1), av[sl & 1]);
 #pragma unroll
         for (int q = 0; q < 2; ++q) xpose4(bw[sl][q]);
 #pragma unroll
@@ -640,23 +651,27 @@ __global__ void __launch_bounds__(kGmThreads, 4) gateup_gemm_kernel(FfnArgs a) {
 #pragma unroll
           for (int q = 0; q < 2; ++q)
             B[q] = dequant_f16_pairs(word(bw[sl][q], p), scale_pair(bs[sl][q].x, bs[sl][q].y, p));
+          uint4 Av[MS];
+#pragma unroll
+          for (int mt = 0; mt < MS; ++mt) Av[mt] = as[sl & 1][16 * mt + n][4 * p + g];
 #pragma unroll
           for (int mt = 0; mt < MS; ++mt) {
-            const uint4 v = as[sl][16 * mt + n][4 * p + g];
-            const u32x4_t A = {v.x, v.y, v.z, v.w};
+            const u32x4_t A = {Av[mt].x, Av[mt].y, Av[mt].z, Av[mt].w};
 #pragma unroll
             for (int q = 0; q < 2; ++q) acc[q][mt] = mfma_f16(A, B[q], acc[q][mt]);
           }
         }
-        load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);
+        load_b(min(s + 4, KS - 1), bw[sl], bs[sl]);
         // the weight requests go out before the wait for the A rows below
         __builtin_amdgcn_sched_barrier(0);
-        store_a(sl ^ 1, av);  // unconditional: no branch inside the step
+        store_a((sl & 1) ^ 1, av[(sl & 1) ^ 1]);  // unconditional: no branch inside the step
         lds_barrier();
       };
-      for (int s = 0; s < KS; s += 2) {
+      for (int s = 0; s < KS; s += 4) {
         step(s, IntC<0>{});
         step(s + 1, IntC<1>{});
+        step(s + 2, IntC<2>{});
+        step(s + 3, IntC<3>{});
       }
     });
     // SwiGLU into LDS (the A buffers are free now): lane (n, g) holds rows
@@ -795,8 +810,11 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
     uint4 av[4];
     uint4 bw[2][2];
     u32x2_t bs[2][2];
-    load_a(0, av);
+    // B(0), A(0), B(1): once A(0) has arrived, B(0) has too (the counter of
+    // outstanding loads drains in order) and only B(1) is pending, as at the
+    // top of every later pair of steps
     load_b(0, bw[0], bs[0]);
+    load_a(0, av);
     load_b(1, bw[1], bs[1]);
     store_a(0, av);
     lds_barrier();
@@ -893,15 +911,17 @@ static int pf_tiles_upper(const FfnArgs &a) {
   return (a.n_rows + kPfRows - 1) / kPfRows + units + (a.Fs > 0 ? (a.T + kPfRows - 1) / kPfRows : 0);
 }
 
-static int gm_grid(int items_upper) {
+// Blocks of a GEMM launch: per_cu per compute unit (fewer when there are
+// fewer items), a multiple of the 8 XCDs (the item order relies on it).
+static int gm_grid(int items_upper, int per_cu) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
-  const int cap = 2 * cus;  // two blocks per compute unit
+  const int cap = per_cu * cus;
   const int g = items_upper < 1 ? 1 : (items_upper < cap ? items_upper : cap);
-  return (g + 7) & ~7;  // a multiple of the 8 XCDs (the item order relies on it)
+  return (g + 7) & ~7;
 }
 
 static bool gm_units_fit(const FfnArgs &a) {
@@ -910,7 +930,7 @@ static bool gm_units_fit(const FfnArgs &a) {
 
 hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
   if (a.H == 128 * 16 && a.F % 128 == 0 && gm_units_fit(a)) {
-    return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128))), dim3(kGmThreads), 0,
+    return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128), 1)), dim3(kGmThreads), 0,
                          s, a);
   }
   return launch_kernel(gateup_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.F / kPfCols))), dim3(kPfThreads), 0,
@@ -919,7 +939,7 @@ hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
 
 hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
   if (a.F == 128 * 4 && a.H % 256 == 0 && gm_units_fit(a)) {
-    return launch_kernel(down_gemm_kernel<4>, dim3(gm_grid(pf_tiles_upper(a) * (a.H / 256))), dim3(kGmThreads), 0, s,
+    return launch_kernel(down_gemm_kernel<4>, dim3(gm_grid(pf_tiles_upper(a) * (a.H / 256), 2)), dim3(kGmThreads), 0, s,
                          a);
   }
   return launch_kernel(down_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.H / kPfCols))), dim3(kPfThreads), 0,
