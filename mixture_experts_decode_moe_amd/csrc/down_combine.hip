@@ -19,8 +19,7 @@
 // integer products and the per-block scales are those of the decode down
 // kernel: bf16 hi + lo parts of the SwiGLU rows, weights as magic bf16 pairs
 // (int4: q + 136, -136 sum(x) per block through one more MFMA, fp16 block
-// scale in fp32; int8: q + 128 with the -128 sum(x) correction and the row
-// scale).  Each block-quad of the SwiGLU dimension gives one partial,
+// scale in fp32; int8: q itself and the row scale).  Each block-quad of the SwiGLU dimension gives one partial,
 // summed from zero over its four blocks exactly as one wave of the down
 // kernel sums it; the partials are added in quad order, multiplied by the
 // routing weight and summed in slot order as the combine kernel does, so a
@@ -159,7 +158,7 @@ __global__ void __launch_bounds__(kDcMaxThreads) down_combine_kernel(DownCombine
       // blocks, the same partials the down kernel's waves form
 #pragma unroll
       for (int jj = 0; jj < NQ; ++jj) {
-        f32x4_t acc = zero4, corr = zero4;
+        f32x4_t acc = zero4;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int b = ha * NBh + 4 * jj + p;  // block of this lane's A row
@@ -173,13 +172,11 @@ __global__ void __launch_bounds__(kDcMaxThreads) down_combine_kernel(DownCombine
             c = Fm::mfma(al, bw, c);
             acc = fma4(scale4(w[j].s[jj][0], w[j].s[jj][1], p), c, acc);
           } else {
-            corr = Fm::mfma(ah, cvec, corr);
-            corr = Fm::mfma(al, cvec, corr);
             acc = Fm::mfma(ah, bw, acc);
             acc = Fm::mfma(al, bw, acc);
           }
         }
-        if constexpr (!kInt4) acc = (acc + corr) * w[j].rs;
+        if constexpr (!kInt4) acc = acc * w[j].rs;
         // lane (n, g) holds tile rows 4g..4g+3 of column n: kept where the
         // row's half (g >> 1) is the column's half
         if ((g >> 1) == hb) {

@@ -23,11 +23,10 @@
 // both parts go through the matrix core.
 //
 // int8 weights (q stored as a two's-complement byte, fp32 scale per row):
-// byte ^ 0x80 = q + 128 in [1, 255] is exact in bfloat16 (converted through
-// fp32), the 16x16x16 MFMA takes four consecutive k per lane, the sums run
-// over the whole row in the MFMA accumulator, a second accumulator collects
-// -128 * sum(x), and the row scale is applied once at the end.  The
-// operands keep their natural element order.
+// q itself is exact in bfloat16 (|q| <= 127; converted through fp32), the
+// 16x16x16 MFMA takes four consecutive k per lane, the sums run over the
+// whole row in the MFMA accumulator with no correction, and the row scale is
+// applied once at the end.  The operands keep their natural element order.
 //
 // Operand layout (v_mfma_f32_16x16x32_bf16, wave64): lane l supplies A row
 // l % 16 and B column l % 16, k-group l / 16 (8 consecutive k of the 32);
@@ -385,7 +384,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
           for (int jj = 0; jj < JW; ++jj) xpose4(w[i].w[jj]);
           const bool mv = n < nrows;
           const uint16_t *xrow = reinterpret_cast<const uint16_t *>(xs_lds + toks[it][n] * xstride);
-          f32x4_t acc = zero4, corr = zero4;
+          f32x4_t acc = zero4;
 #pragma unroll
           for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
@@ -399,10 +398,9 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
                 acc = fma4(scale4(w[i].s[jj][0], w[i].s[jj][1], p), c, acc);
               } else {
                 acc = Fm::mfma(xa, Fm::b_w(word(w[i].w[jj], p)), acc);
-                corr = Fm::mfma(xa, cvec, corr);
               }
             }
-          if constexpr (!kInt4) acc = (acc + corr) * w[i].rs;
+          if constexpr (!kInt4) acc = acc * w[i].rs;
           red[j][wave][lane] = acc;
         }
       }
@@ -523,7 +521,6 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
     for (int m0 = 0; m0 < u.n; m0 += 16) {
       if (m0 > 0) load_a(m0);
       f32x4_t acc[4] = {zero4, zero4, zero4, zero4};
-      f32x4_t corr = zero4;
 #pragma unroll
       for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
@@ -539,8 +536,6 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
               acc[nt] = fma4(scale4(sd[jj][nt][0], sd[jj][nt][1], p), c, acc[nt]);
             }
           } else {
-            corr = Fm::mfma(ah[jj][p], cvec, corr);
-            corr = Fm::mfma(al[jj][p], cvec, corr);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
               const Vec bw = Fm::b_w(word(wd[jj][nt], p));
@@ -551,7 +546,7 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
         }
       if constexpr (!kInt4) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[nt] = (acc[nt] + corr) * rs[nt];
+        for (int nt = 0; nt < 4; ++nt) acc[nt] = acc[nt] * rs[nt];
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) red[wave][nt][lane] = acc[nt];

@@ -15,7 +15,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kMagicPair = 0x43004300u;     // bf16 pair (128, 128)
 constexpr uint32_t kMinus136Pair = 0xC308C308u;  // bf16 pair (-136, -136)
-constexpr uint32_t kMinus128Pair = 0xC300C300u;  // bf16 pair (-128, -128)
 constexpr int kGuMaxWaves = 16;  // gate/up: waves splitting the hidden dimension
 constexpr int kDnMaxWaves = 8;   // down: waves splitting the SwiGLU dimension
 
@@ -74,11 +73,14 @@ MOE_DEV f32x4_t mfma_bf16_k16(const u32x2_t &a, const u32x2_t &b, const f32x4_t 
                                                    0, 0, 0);
 }
 
-// Four int8 weights (one k-group) -> two bf16 pairs of q + 128 (exact).
+// Four int8 weights (one k-group) -> two bf16 pairs of q (exact: |q| <= 127
+// needs 7 bits).  Each byte goes through fp32 as its unsigned value of
+// byte ^ 0x80 = q + 128 minus 128 (both steps exact; a float conversion of a
+// sign-extended field has been miscompiled).
 MOE_DEV u32x2_t byte_pairs(uint32_t w) {
   const uint32_t v = w ^ 0x80808080u;
-  const float f0 = static_cast<float>(v & 0xFFu), f1 = static_cast<float>((v >> 8) & 0xFFu);
-  const float f2 = static_cast<float>((v >> 16) & 0xFFu), f3 = static_cast<float>(v >> 24);
+  const float f0 = static_cast<float>(v & 0xFFu) - 128.f, f1 = static_cast<float>((v >> 8) & 0xFFu) - 128.f;
+  const float f2 = static_cast<float>((v >> 16) & 0xFFu) - 128.f, f3 = static_cast<float>(v >> 24) - 128.f;
   u32x2_t r;
   r.x = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);  // high halves
   r.y = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
@@ -181,7 +183,7 @@ struct MfmaFmt<MOE_W_INT8_ROW> {
   static MOE_DEV Vec a_plane(const uint16_t *plane, int b, int g) { return a_x(plane, b, g); }
   static MOE_DEV Vec zero() { return Vec{0u, 0u}; }
   static MOE_DEV Vec b_w(uint32_t w) { return byte_pairs(w); }
-  static MOE_DEV Vec corr() { return Vec{kMinus128Pair, kMinus128Pair}; }
+  static MOE_DEV Vec corr() { return zero(); }  // unused: q itself needs no correction
   static MOE_DEV f32x4_t mfma(const Vec &a, const Vec &b, const f32x4_t &c) { return mfma_bf16_k16(a, b, c); }
 };
 
