@@ -377,6 +377,7 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
     fa.row_w = w.row_w;
     fa.units = w.units;
     xa.route_here = (mfma_decode_ok(xa) && E <= 256) ? 1 : 0;
+    if (xa.route_here) xa.units = w.units;  // published by the gate/up kernel's routing
     xa.route = fa;
     StageMark m(MOE_STAGE_ROUTE, s);
     e = xa.route_here ? launch_route_partial(fa, s) : launch_route_fused(fa, s);

@@ -152,6 +152,7 @@ struct FfnArgs {
   float *act;               // [n_rows*F + T*Fs]
   float *rows_out;          // [n_rows + (Fs ? T : 0)][H]
   int32_t max_units;        // upper bound of routed units (grid sizing)
+  const int32_t *units;     // [max_units] int4 (expert, first row, rows, 0) or NULL
   // decode layer calls (E <= 256): the gate/up kernel routes the batch
   // itself from the router's partial logits and its last block publishes
   // the routing (the offsets, active, n_active, row_tok and row_w above

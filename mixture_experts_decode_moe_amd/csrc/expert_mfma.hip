@@ -58,7 +58,10 @@ struct MUnit {
   bool shared;
 };
 
-MOE_DEV bool mfma_unit(const FfnArgs &a, int item, int tiles_r, int tiles_s, int U, MUnit &u) {
+// rec: the unit's (expert, first row, rows) record from the routing's unit
+// table, when the caller has read it already (nullptr: look it up)
+MOE_DEV bool mfma_unit(const FfnArgs &a, int item, int tiles_r, int tiles_s, int U, MUnit &u,
+                       const int4 *rec = nullptr) {
   if (item < tiles_s) {
     u.shared = true;
     u.gq = a.sgq;
@@ -86,7 +89,11 @@ MOE_DEV bool mfma_unit(const FfnArgs &a, int item, int tiles_r, int tiles_s, int
   u.ds = a.ds;
   u.F = a.F;
   u.tile = i - k * tiles_r;
-  if (a.offsets) {
+  if (rec) {
+    u.e = rec->x;
+    u.r0 = rec->y;
+    u.n = rec->z;
+  } else if (a.offsets) {
     u.e = a.active[k];
     u.r0 = a.offsets[u.e];
     u.n = a.offsets[u.e + 1] - u.r0;
@@ -463,15 +470,29 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
   const int n = lane & 15;
   const int g = lane >> 4;
   const int H = a.H;
-  const int U = routed_units(a);
   const int tiles = H / 64;
-  const int n_items = (a.Fs > 0 ? tiles : 0) + U * tiles;
+  const int tiles_s = a.Fs > 0 ? tiles : 0;
+  // With the routing's unit table, the first item's record is requested
+  // together with the unit count (one round trip instead of three
+  // dependent reads: count, active list, offsets).
+  int4 rec0 = make_int4(0, 0, 0, 0);
+  if (a.units) {
+    const int k0 = blockIdx.x >= tiles_s ? (blockIdx.x - tiles_s) / tiles : 0;
+    rec0 = reinterpret_cast<const int4 *>(a.units)[min(k0, a.max_units - 1)];
+  }
+  const int U = routed_units(a);
+  const int n_items = tiles_s + U * tiles;
   const Vec cvec = Fm::corr();
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     MUnit u;
-    if (!mfma_unit(a, item, tiles, a.Fs > 0 ? tiles : 0, U, u) || u.n <= 0) continue;
+    int4 rec;
+    if (a.units && item != static_cast<int>(blockIdx.x) && item >= tiles_s)
+      rec = reinterpret_cast<const int4 *>(a.units)[min((item - tiles_s) / tiles, a.max_units - 1)];
+    else
+      rec = rec0;
+    if (!mfma_unit(a, item, tiles, tiles_s, U, u, a.units ? &rec : nullptr) || u.n <= 0) continue;
     const int h0 = u.tile * 64;
     const int F = u.F;
     const int nblk = F / Fm::kBlockK;
