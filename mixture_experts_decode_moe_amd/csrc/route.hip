@@ -128,48 +128,57 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restr
 //
 // For more than kFusedTokens tokens the logits are an fp32 GEMM on the
 // matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation):
-// a block owns 32 tokens x 64 experts, wave w the experts 16w..16w+15 of
-// both 16-token halves; the reduction dimension advances 64 at a time with
-// the x rows (bf16, widened exactly) and the router rows staged in LDS.
-// moe_route and the layer use this kernel alike for such batches.
+// a block owns 32 tokens x 64 experts, with 8 waves: wave w takes the
+// experts 16 (w % 4)..+15 of both 16-token halves over one half of each
+// 64-wide step of the reduction dimension (w / 4), and the two halves'
+// sums are added in LDS at the end (lower half first).  The x rows (bf16,
+// widened exactly) and the router rows are staged in LDS.  Two waves a SIMD
+// hide each other's operand reads.  moe_route and the layer use this
+// kernel alike for such batches.
 typedef float rf32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kRmTok = 32, kRmExp = 64, kRmK = 64, kRmPad = 68;
+constexpr int kRmThreads = 512;
 
-__global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restrict__ wr,
-                                                          const float *__restrict__ bias,
-                                                          const uint16_t *__restrict__ x, int32_t T, int32_t H,
-                                                          int32_t E, float *__restrict__ logits) {
+__global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__restrict__ wr,
+                                                                 const float *__restrict__ bias,
+                                                                 const uint16_t *__restrict__ x, int32_t T,
+                                                                 int32_t H, int32_t E, float *__restrict__ logits) {
   __shared__ float xs[2][kRmTok][kRmPad];
   __shared__ float ws[2][kRmExp][kRmPad];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int n = lane & 15, q = lane >> 4;
+  const int et = wave & 3, kh = wave >> 2;  // expert tile, half of each step
   const int t0 = blockIdx.y * kRmTok;
   const int e0 = blockIdx.x * kRmExp;
-  // staging: x piece (token tid / 8, 8 elements at 8 (tid % 8)); router
-  // rows: 4 float4 per thread (expert tid / 4 + 0, k 16 (tid % 4) + 4 i)
-  const int xt = tid >> 3, xk = (tid & 7) * 8;
-  const int we = tid >> 2, wk = (tid & 3) * 16;
-  const bool xv = t0 + xt < T, wv = e0 + we < E;
+  // staging: threads 0-255 one x piece (token tid / 8, 8 elements at
+  // 8 (tid % 8)); every thread two float4 of the router rows (expert
+  // tid / 8, k 8 (tid % 8) + 4 i)
+  const int xt = (tid & 255) >> 3, xk = (tid & 7) * 8;
+  const int we = tid >> 3, wk = (tid & 7) * 8;
+  const bool xthr = tid < 256;
+  const bool xv = xthr && t0 + xt < T, wv = e0 + we < E;
   const uint4 *xp = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(xv ? t0 + xt : 0) * H + xk);
   const float4 *wp = reinterpret_cast<const float4 *>(wr + static_cast<size_t>(wv ? e0 + we : 0) * H + wk);
   uint4 xr;
-  float4 wrr[4];
+  float4 wrr[2];
   auto load = [&](int s) {
     xr = xv ? xp[s * (kRmK / 8)] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wrr[i] = wv ? wp[s * (kRmK / 4) + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < 2; ++i) wrr[i] = wv ? wp[s * (kRmK / 4) + i] : make_float4(0.f, 0.f, 0.f, 0.f);
   };
   auto store = [&](int buf) {
-    const uint32_t d[4] = {xr.x, xr.y, xr.z, xr.w};
+    if (xthr) {
+      const uint32_t d[4] = {xr.x, xr.y, xr.z, xr.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xs[buf][xt][xk + 2 * i] = bf16_lo(d[i]);
-      xs[buf][xt][xk + 2 * i + 1] = bf16_hi(d[i]);
+      for (int i = 0; i < 4; ++i) {
+        xs[buf][xt][xk + 2 * i] = bf16_lo(d[i]);
+        xs[buf][xt][xk + 2 * i + 1] = bf16_hi(d[i]);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4 *>(&ws[buf][we][wk + 4 * i]) = wrr[i];
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<float4 *>(&ws[buf][we][wk + 4 * i]) = wrr[i];
   };
   rf32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const int steps = H / kRmK;
@@ -179,10 +188,12 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restric
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
     if (s + 1 < steps) load(s + 1);
-    // lane group q takes k = 16 r + 4 q + c in MFMA (r, c), for A and B alike
+    // lane group q takes k = 16 r + 4 q + c in MFMA (r, c), for A and B
+    // alike; this wave's half of the step is r = 2 kh, 2 kh + 1
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float4 b4 = *reinterpret_cast<const float4 *>(&ws[buf][16 * wave + n][16 * r + 4 * q]);
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = 2 * kh + rr;
+      const float4 b4 = *reinterpret_cast<const float4 *>(&ws[buf][16 * et + n][16 * r + 4 * q]);
       const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -195,16 +206,29 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restric
     if (s + 1 < steps) store(buf ^ 1);
     lds_barrier();
   }
-  const int e = e0 + 16 * wave + n;
-  if (e < E) {
-    const float b = bias ? bias[e] : 0.f;
+  // the upper half's sums to LDS (the x buffers are free), added to the
+  // lower half's
+  rf32x4_t *part = reinterpret_cast<rf32x4_t *>(&xs[0][0][0]);
+  static_assert(4 * 2 * 64 * sizeof(rf32x4_t) <= sizeof(xs), "partial sums must fit the x buffers");
+  if (kh == 1) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) part[(et * 2 + mt) * 64 + lane] = acc[mt];
+  }
+  lds_barrier();
+  if (kh == 0) {
+    const int e = e0 + 16 * et + n;
+    if (e < E) {
+      const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * mt + 4 * q + i;
-        if (t < T) logits[static_cast<size_t>(t) * E + e] = acc[mt][i] + b;
+      for (int mt = 0; mt < 2; ++mt) {
+        const rf32x4_t v = acc[mt] + part[(et * 2 + mt) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * mt + 4 * q + i;
+          if (t < T) logits[static_cast<size_t>(t) * E + e] = v[i] + b;
+        }
       }
+    }
   }
 }
 
@@ -302,7 +326,7 @@ hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s) {
   if (a.T > kFusedTokens && a.H % kRmK == 0) {
     dim3 g((a.E + kRmExp - 1) / kRmExp, (a.T + kRmTok - 1) / kRmTok);
-    router_mfma_kernel<<<g, 256, 0, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits);
+    router_mfma_kernel<<<g, kRmThreads, 0, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits);
     return hipGetLastError();
   }
   dim3 grid((a.E + 3) / 4, (a.T + kRouterTokens - 1) / kRouterTokens);
