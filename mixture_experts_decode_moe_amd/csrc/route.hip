@@ -4,11 +4,11 @@
 // The pages fold "router top-k and grouping" into one launch on their card
 // ("Qwen3.6-35B-A3B: pictures, several requests at once and speed", Speed
 // (0.1.45)) after a one-thread walk over the 256 experts proved slow; here a
-// whole wavefront holds a token's E logits (E/64 per lane) and each of the K
-// rounds is one wave-wide arg-max done with DPP row steps and four lane
-// reads.  Equal logits go to the lower expert index, the rule the pages
-// apply to their own arg-max ("Models and backends", What was tuned): the
-// arg-max runs on 64-bit keys (order-preserving float bits, inverted index).
+// whole wavefront holds a token's E logits (E/64 per lane, each lane's
+// sorted once) and each of the K rounds is one wave-wide maximum of the
+// lanes' leading logits, done with DPP row steps and four lane reads.  Equal
+// logits go to the lower expert index, the rule the pages apply to their own
+// arg-max ("Models and backends", What was tuned).
 #include <float.h>
 #include <math.h>
 

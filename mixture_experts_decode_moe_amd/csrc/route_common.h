@@ -33,12 +33,107 @@ MOE_DEV uint32_t wave_max_u32(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
+// Wave-wide minimum (uniform result).
+MOE_DEV uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+// Softmax of the K selected logits (renorm) or over all E, the largest
+// logit subtracted for range; sums in a fixed order.  Lane k < K holds
+// round k's logit in my_v.
+template <int NPL>
+MOE_DEV float topk_weight(const float (&v)[NPL], int32_t E, int32_t K, int32_t renorm, float my_v, float top_v) {
+  const int lane = __lane_id();
+  const float mine = (lane < K) ? expf(my_v - top_v) : 0.f;
+  float denom;
+  if (renorm) {
+    denom = 0.f;
+    for (int k = 0; k < K; ++k) denom += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), k));
+  } else {
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      if (lane + 64 * j < E) part += expf(v[j] - top_v);
+    denom = sum64(part);
+  }
+  return mine / denom;
+}
+
 // Top-k of one token's logits held by a whole wave: lane l holds experts
 // l, l+64, ... in v[] (NaN already replaced by -inf, absent experts -inf).
 // Lane k < K receives round k's expert and routing weight.
+//
+// NPL <= 4: each lane first sorts its NPL (key, expert) pairs, larger key
+// first and the lower expert on equal keys.  A round is then one wave-wide
+// maximum of the lanes' first keys; when one lane holds it (the usual case)
+// its first pair wins, else the lowest expert among the lanes holding it
+// (each lane's first pair is its lowest expert of that key).  The winning
+// lane drops its first pair.  Results are those of the rule "largest
+// logit, lower index on equal logits", round by round.
 template <int NPL>
 MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t renorm, int &my_e, float &my_w) {
   const int lane = __lane_id();
+  if constexpr (NPL <= 4) {
+    uint32_t key[NPL];  // 0 = used or absent
+    int idx[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      key[j] = (lane + 64 * j < E) ? float_key(v[j]) : 0u;
+      idx[j] = lane + 64 * j;
+    }
+    // sorting network, comparing (key desc, expert asc)
+    auto cswap = [&](int a, int b) {
+      const bool sw = key[b] > key[a] || (key[b] == key[a] && idx[b] < idx[a]);
+      const uint32_t ka = key[a], kb = key[b];
+      const int ia = idx[a], ib = idx[b];
+      key[a] = sw ? kb : ka;
+      key[b] = sw ? ka : kb;
+      idx[a] = sw ? ib : ia;
+      idx[b] = sw ? ia : ib;
+    };
+    if constexpr (NPL >= 2) cswap(0, 1);
+    if constexpr (NPL == 4) {
+      cswap(2, 3);
+      cswap(0, 2);
+      cswap(1, 3);
+      cswap(1, 2);
+    }
+    float top_v = 0.f;
+    float my_v = 0.f;  // lane k keeps round k's value and index
+    my_e = 0;
+    for (int k = 0; k < K; ++k) {
+      const uint32_t m = wave_max_u32(key[0]);
+      const uint64_t hit = __ballot(key[0] == m);
+      int sel;
+      if (__popcll(hit) == 1) {
+        sel = __builtin_amdgcn_readlane(idx[0], __builtin_ctzll(hit));
+      } else {
+        sel = static_cast<int>(wave_min_u32(key[0] == m ? static_cast<uint32_t>(idx[0]) : 0xFFFFFFFFu));
+      }
+      if ((sel & 63) == lane) {  // the winner drops its first pair
+#pragma unroll
+        for (int j = 0; j + 1 < NPL; ++j) {
+          key[j] = key[j + 1];
+          idx[j] = idx[j + 1];
+        }
+        key[NPL - 1] = 0u;
+      }
+      const float sel_v = key_float(m);
+      if (k == 0) top_v = sel_v;
+      if (lane == k) {
+        my_v = sel_v;
+        my_e = sel;
+      }
+    }
+    my_w = topk_weight<NPL>(v, E, K, renorm, my_v, top_v);
+    return;
+  }
   uint32_t key[NPL];  // 0 = used or absent
 #pragma unroll
   for (int j = 0; j < NPL; ++j) key[j] = (lane + 64 * j < E) ? float_key(v[j]) : 0u;
@@ -69,21 +164,7 @@ MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t reno
       my_e = sel;
     }
   }
-  // Softmax over the selected logits (renorm) or over all E, the largest
-  // logit subtracted for range; sums in a fixed order.
-  const float mine = (lane < K) ? expf(my_v - top_v) : 0.f;
-  float denom;
-  if (renorm) {
-    denom = 0.f;
-    for (int k = 0; k < K; ++k) denom += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), k));
-  } else {
-    float part = 0.f;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      if (lane + 64 * j < E) part += expf(v[j] - top_v);
-    denom = sum64(part);
-  }
-  my_w = mine / denom;
+  my_w = topk_weight<NPL>(v, E, K, renorm, my_v, top_v);
 }
 
 // ------------------------------------------------------------------------

@@ -67,6 +67,40 @@ def test_route(mb, cfg):
     say(f"route cfg{cfg}: near ties {int(tie.sum())} of {T}")
 
 
+@pytest.mark.parametrize("T", [1, 4, 16, 40])
+def test_route_exact_ties(mb, T):
+    """Equal logits: every router row appears eight times (experts e, e + 32,
+    ..., e + 224 share one row, so equal logits sit both in one lane and in
+    different lanes of the top-k wave).  The selection must be the lowest
+    indices among equal logits, round by round: exactly the oracle's
+    selection run on the GPU's own logits (T <= 16: the decode routing; T >
+    16: the top-k kernel), and each token's experts are the eight copies of
+    one row, ascending, with equal weights."""
+    import torch
+    import parity_util as pu
+    E, H, K = 256, 1024, 8
+    base = synth.normal_f32(7, synth.S_ROUTER_W, 32 * H, 0.0, 0.02).reshape(32, H)
+    wr = np.ascontiguousarray(base[np.arange(E) % 32])
+    x = synth.normal_bf16(8, synth.S_X, T * H).reshape(T, H)
+    say(f"route exact ties T={T}")
+    dummy = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    routed = mb.Experts(synth.FMT_INT4_B32, E, 512, dummy, dummy, dummy, dummy, dummy, dummy)
+    dl = mb.Layer(H, E, K, 1, torch.from_numpy(wr).cuda(), None, routed, None)
+    ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    mb.route(dl, pu.dev_u16(x), ids, w, lg)
+    torch.cuda.synchronize()
+    ids_h, w_h, lg_h = ids.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy().astype(np.float64)
+    # duplicate rows give bit-equal logits
+    assert np.array_equal(lg_h, lg_h[:, np.arange(E) % 32])
+    exp_ids, _ = oracle.select(lg_h, K, 1)
+    assert np.array_equal(ids_h, exp_ids)
+    best = np.argmax(lg_h[:, :32], axis=1)
+    assert np.array_equal(ids_h, best[:, None] + 32 * np.arange(K)[None, :])
+    assert np.allclose(w_h, 1.0 / K, rtol=0, atol=1e-7)
+
+
 @pytest.mark.parametrize("T,K,E,mode", [(1, 8, 256, "rand"), (16, 8, 256, "rand"), (2048, 8, 256, "rand"),
                                         (700, 4, 64, "rand"), (300, 8, 256, "one"), (5, 2, 1024, "rand"),
                                         (3000, 1, 16, "skew")])
