@@ -8,14 +8,16 @@
 // 64 on average), enough to tile each expert's rows as the M dimension of a
 // GEMM and reuse every weight tile across them.
 //
-// Arithmetic as in the decode kernels (expert_mfma.hip): the int4 weights
+// Two sets of kernels: pipelined GEMMs for the layer's shape (H = 2048,
+// F = 512; further below) and generic ones for any other shape.  The
+// generic kernels compute as the decode kernels do (expert_mfma.hip): the int4 weights
 // enter the MFMA as the exact bfloat16 values 128 + nibble = q + 136, the
 // other operand is exact (x in bf16; the SwiGLU output as bf16 hi + lo), the
 // fp32 accumulator input of each 32-element block is -136 * sum(other
 // operand over the block) (computed while the operand tile is staged), and
 // the block's fp16 scale is applied with an fp32 FMA.
 //
-// Tiles.  An item is (unit, 64 rows, 64 output columns); a block of 4 waves
+// Generic tiles.  An item is (unit, 64 rows, 64 output columns); a block of 4 waves
 // works on it, wave w owning the 16 columns 16w..16w+15 of all 64 rows (four
 // 16x16 MFMA tiles along M).  Gate/up items hold 64 SwiGLU columns, i.e. 64
 // gate and the matching 64 up columns, so wave w has both halves of its
@@ -421,21 +423,26 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 // A rows of the next one in flight, two blocks per compute unit.  Gate/up
 // (H = 2048: sixteen steps) runs one block per compute unit with 256
 // registers a lane and keeps the weights of the next four steps and the A
-// rows of the next two in flight, and reads a block's A fragments from LDS
-// together before its MFMAs (with 128 registers hipcc read and waited for
-// each fragment right before its MFMA; measured: 202 against 216 us for the
-// prefill chunk).  Tiles are wider than the generic
-// kernels' (128 SwiGLU columns for gate/up, 256 output columns for down, 64
-// rows), each wave owning two 16-column weight tiles against the 16-row
-// tiles of A.  Unlike the generic kernels, these multiply in fp16: each
-// weight is dequantized once per item to the fp16 value q s (rounded once,
-// relative error at most 2^-11) and the A rows are staged in fp16 (x, and
-// the hi and lo parts of the SwiGLU rows, are bf16 values, exact in fp16
-// within its normal range), so the products accumulate in the matrix core
-// with no sum correction and no per-block scaling on the vector unit.
+// rows of the next two in flight.  Items are 64 rows by 128 SwiGLU columns
+// (gate/up) or 256 output columns (down); each wave owns one 32-column
+// weight tile against the 32-row tiles of A, on the 32x32x16 fp16 matrix
+// instruction (measured on this chip: about 2.1 PFLOP/s against 1.2-1.3 for
+// the 16x16x32 shape).  A gate/up wave's 32 columns are the gate and up
+// rows of 16 SwiGLU columns, paired across lanes in the epilogue.
 //
-// The k loop is instantiated once per number of 16-row tiles that hold rows
-// (1..4), chosen per item: no matrix-core instruction sits under a branch.
+// Unlike the generic kernels, these multiply in fp16: each weight is
+// dequantized once per item to the fp16 value q s (rounded once, relative
+// error at most 2^-11), the x rows are staged in fp16 (bf16 values, exact
+// in fp16 within its normal range), and the SwiGLU rows are handed from
+// gate/up to down rounded once to fp16 (one plane), so the products
+// accumulate in the matrix core with no sum correction and no per-block
+// scaling on the vector unit.  Measured against the oracle: 3.6e-4 to
+// 4.3e-4 of max|ref| on prefill calls (T = 37 to 2048).  The vector unit
+// (the int4 dequantization, about 15 operations per 8 weights) is the limit
+// of the gate/up loop at 64 rows per item.
+//
+// The k loop is instantiated once per number of 32-row tiles that hold rows
+// (1, 2), chosen per item: no matrix-core instruction sits under a branch.
 // (With the tile count as a branch inside the loop, hipcc left an MFMA
 // result read by a VALU instruction right after the branch without the
 // wait states the matrix core needs, and those reads saw stale registers.)
@@ -474,6 +481,42 @@ MOE_DEV void with_msub(int msub, Fn &&fn) {
       fn(IntC<4>{});
       break;
   }
+}
+
+template <class Fn>
+MOE_DEV void with_msub2(int msub, Fn &&fn) {
+  if (msub <= 1)
+    fn(IntC<1>{});
+  else
+    fn(IntC<2>{});
+}
+
+// 32x32 output tiles (v_mfma_f32_32x32x16_f16, twice the rate of the 16x16
+// shape on this chip): lane l holds row l % 32 of A and column l % 32 of B
+// with k-group l / 32 (8 consecutive k, pair-permuted) of each 16-k step,
+// and accumulator j of column l % 32, row (j & 3) + 8 (j >> 2) + 4 (l / 32).
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+MOE_DEV f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+MOE_DEV f32x16_t mfma32_f16(const u32x4_t &a, const u32x4_t &b, const f32x16_t &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+// A 16-byte weight chunk (one 32-element block, its four k-group words)
+// per lane, block b0 in lanes 0-31 and block b1 in lanes 32-63 (same
+// column) -> lane half h holds words h and 2 + h of b0, then of b1: the
+// k-groups it multiplies in the two 16-k steps of each block.
+MOE_DEV void half_exchange(uint4 &v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v.x, v.y, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v.z, v.w, false, false);
+  v = make_uint4(a[0], b[0], a[1], b[1]);
 }
 
 constexpr int kGmThreads = 512;  // 8 waves; two blocks per compute unit
@@ -527,7 +570,7 @@ MOE_DEV PfUnit gm_unit(const GmUnits &G, int u) {
 
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
-  static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
+  static_assert(KS % 4 == 0, "the k loop runs over groups of four steps");
   __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted fp16, one k-step
   __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
@@ -535,13 +578,13 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int n = lane & 15, g = lane >> 4;
+  const int c = lane & 31, h = lane >> 5;
+  const bool up_lane = c >= 16;
   const int T = a.T;
   const int H = 128 * KS;
   const int n_units = gm_units(a, units, scratch);
   const int col_tiles = a.F / 128;
   const int n_items = units.pre[n_units] * col_tiles;
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const int pc = tid & 15;
 
   // XCD-aware order: the blocks of one XCD (block b runs on XCD b mod 8)
@@ -561,16 +604,18 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
     const int rows = min(kPfRows, un.n - m0);
     const bool shared = un.e < 0;
     const int F = shared ? a.Fs : a.F;
-    // this lane's weight rows: the gate (q = 0) and up (q = 1) rows of SwiGLU
-    // column col; 32-bit offsets from block-uniform bases (an expert's
+    // this lane's weight row: the gate (lanes c < 16) or up (c >= 16) row of
+    // SwiGLU column col; 32-bit offsets from per-lane bases (an expert's
     // weights are far below 4 GiB)
-    const int col = ct * 128 + 16 * wave + n;
+    const int col = ct * 128 + 16 * wave + (c & 15);
     gchar_t *gq = uniform_gptr(shared ? a.sgq : a.gq);
     gchar_t *uq = uniform_gptr(shared ? a.suq : a.uq);
     gchar_t *gsc = uniform_gptr(shared ? a.sgs : a.gs);
     gchar_t *usc = uniform_gptr(shared ? a.sus : a.us);
+    gchar_t *wq = up_lane ? uq : gq;
+    gchar_t *wsc = up_lane ? usc : gsc;
     const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * F + col);
-    uint32_t woff = row0 * (nblk * 16) + 16 * g, soff = row0 * (nblk * 2);
+    uint32_t woff = row0 * (nblk * 16) + 16 * h, soff = row0 * (nblk * 2);
 
     // A staging: thread t owns piece t % 16 of rows t / 16 + 32 i.  Rows
     // past the tile's end read token 0's row: their products land in
@@ -602,26 +647,21 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
                                                       bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
       }
     };
-    auto load_b = [&](int s, uint4(&w)[2], u32x2_t(&sc)[2]) {
-      // plain loads: the other half of each 128-byte line is requested one
-      // step later and should still be in the L2
-      w[0] = load16_g(gq + (woff + 64u * s));
-      w[1] = load16_g(uq + (woff + 64u * s));
-      sc[0] = *reinterpret_cast<gu2_t *>(gsc + (soff + 8u * s));
-      sc[1] = *reinterpret_cast<gu2_t *>(usc + (soff + 8u * s));
+    auto load_b = [&](int s, uint4(&w)[2], u32x2_t &sc) {
+      // blocks 4 s + 2 i + h; the four block scales of the step
+#pragma unroll
+      for (int i = 0; i < 2; ++i) w[i] = load16_g(wq + (woff + 64u * s + 32u * i));
+      sc = *reinterpret_cast<gu2_t *>(wsc + (soff + 8u * s));
     };
 
-    f32x4_t acc[2][4];
+    f32x16_t acc[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[q][mt] = zero4;
-    uint4 av[2][2];     // A rows of the next two steps, slot s & 1
-    uint4 bw[4][2];     // weight chunks, slot s & 3
-    u32x2_t bs[4][2];   // their block scales
-    // B(0), A(0), B(1): once A(0) has arrived, B(0) has too (the counter of
-    // outstanding loads drains in order) and only B(1) is pending, as at the
-    // top of every later pair of steps
+    for (int mt = 0; mt < 2; ++mt) acc[mt] = zero16();
+    uint4 av[2][2];  // A rows of the next two steps, slot s & 1
+    uint4 bw[4][2];  // weight chunks, slot s & 3
+    u32x2_t bs[4];   // their block scales
+    // B(0), A(0), B(1..3), A(1): once A(0) has arrived, B(0) has too (the
+    // counter of outstanding loads drains in order)
     load_b(0, bw[0], bs[0]);
     load_a(0, av[0]);
     load_b(1, bw[1], bs[1]);
@@ -630,7 +670,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
     load_a(1, av[1]);
     store_a(0, av[0]);
     lds_barrier();
-    with_msub((rows + 15) >> 4, [&](auto msc) __attribute__((always_inline)) {
+    with_msub2((rows + 31) >> 5, [&](auto msc) __attribute__((always_inline)) {
       constexpr int MS = decltype(msc)::value;
       auto step = [&](int s, auto slc) __attribute__((always_inline)) {
         constexpr int sl = decltype(slc)::value;
@@ -641,24 +681,23 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
         // unconditional (clamped) requests keep the register slots out of
         // scratch memory; past the end they re-read the last step
         load_a(min(s + 2, KS - 1), av[sl & 1]);
+        // kept at the top of the step: two steps of latency for the gather
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) xpose4(bw[sl][q]);
+        for (int i = 0; i < 2; ++i) half_exchange(bw[sl][i]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          // block 4 s + p: both weight tiles' operands (scaled, fp16), then
-          // each 16-row tile of A against both
-          u32x4_t B[2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-            B[q] = dequant_f16_pairs(word(bw[sl][q], p), scale_pair(bs[sl][q].x, bs[sl][q].y, p));
+        for (int t8 = 0; t8 < 8; ++t8) {
+          // k 16 t8 .. 16 t8 + 15 of the step: block 2 i + (t >> 1)
+          const int i = t8 >> 2, t = t8 & 3;
+          const u32x4_t B =
+              dequant_f16_pairs(word(bw[sl][i], t), bs[sl].x, bs[sl].y, 2 * i + (t >> 1));
           uint4 Av[MS];
 #pragma unroll
-          for (int mt = 0; mt < MS; ++mt) Av[mt] = as[sl & 1][16 * mt + n][4 * p + g];
+          for (int mt = 0; mt < MS; ++mt) Av[mt] = as[sl & 1][32 * mt + c][2 * t8 + h];
 #pragma unroll
           for (int mt = 0; mt < MS; ++mt) {
             const u32x4_t A = {Av[mt].x, Av[mt].y, Av[mt].z, Av[mt].w};
-#pragma unroll
-            for (int q = 0; q < 2; ++q) acc[q][mt] = mfma_f16(A, B[q], acc[q][mt]);
+            acc[mt] = mfma32_f16(A, B, acc[mt]);
           }
         }
         load_b(min(s + 4, KS - 1), bw[sl], bs[sl]);
@@ -674,45 +713,51 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
         step(s + 3, IntC<3>{});
       }
     });
-    // SwiGLU into LDS (the A buffers are free now): lane (n, g) holds rows
-    // 16 mt + 4 g + i of column col; rows [64][hi 128 + 8 pad | lo 128 + 8].
-    // Rows past the tile's end hold finite values that are never stored.
+    // SwiGLU into LDS (the A buffers are free now).  Lane (c, h) holds
+    // accumulator j of rows 32 mt + (j & 3) + 8 (j >> 2) + 4 h, gate (c < 16)
+    // or up (c >= 16) of SwiGLU column c & 15; swapping register j with
+    // j + 8 between the two 16-lane halves of each 32-lane row gives lanes
+    // c < 16 gate and up of value j and lanes c >= 16 those of value j + 8.
+    // The values are rounded once to fp16 (one plane: the down GEMM's A
+    // operand as it is).  Rows [64][128 + 8 pad]; rows past the tile's end
+    // hold finite values that are never stored.
     uint16_t *st = reinterpret_cast<uint16_t *>(&as[0][0][0]);
-    constexpr int kStPlane = 136, kStRow = 2 * kStPlane;
+    constexpr int kStRow = 136;
     static_assert(kPfRows * kStRow * 2 <= sizeof(as), "SwiGLU staging must fit the A buffers");
-    const int cl = act_pos<MOE_W_INT4_B32>(16 * wave + n);  // tiles start at multiples of 8
+    const int cl = act_pos<MOE_W_INT4_B32>(16 * wave + (c & 15));  // tiles start at multiples of 8
+    const int rbase = (up_lane ? 16 : 0) + 4 * h;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; i += 2) {
+      for (int jj = 0; jj < 8; jj += 2) {
         // rows r and r + 1 converted in pairs
-        const int r = 16 * mt + 4 * g + i;
+        const int r = 32 * mt + (jj & 3) + 8 * (jj >> 2) + rbase;
         float v[2];
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
-          const float gv = acc[0][mt][i + d], uv = acc[1][mt][i + d];
+          const auto gu = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[mt][jj + d]),
+                                                           __float_as_uint(acc[mt][jj + d + 8]), false, false);
+          const float gv = __uint_as_float(gu[0]), uv = __uint_as_float(gu[1]);
           v[d] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
         }
-        const uint32_t hi = f32x2_to_bf16x2_rne(v[0], v[1]);
-        const uint32_t lo = f32x2_to_bf16x2_rne(v[0] - bf16_lo(hi), v[1] - bf16_hi(hi));
-        st[r * kStRow + cl] = static_cast<uint16_t>(hi);
-        st[(r + 1) * kStRow + cl] = static_cast<uint16_t>(hi >> 16);
-        st[r * kStRow + kStPlane + cl] = static_cast<uint16_t>(lo);
-        st[(r + 1) * kStRow + kStPlane + cl] = static_cast<uint16_t>(lo >> 16);
+        const f32x2v_t vv = {v[0], v[1]};
+        const uint32_t hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(vv, f16x2_t));
+        st[r * kStRow + cl] = static_cast<uint16_t>(hv);
+        st[(r + 1) * kStRow + cl] = static_cast<uint16_t>(hv >> 16);
       }
     lds_barrier();
-    // 16-byte stores of whole row segments: piece (row, plane, 16 of them)
+    // 16-byte stores of whole row segments: piece (row, 16 of them)
 #pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
+    for (int k2 = 0; k2 < 2; ++k2) {
       const int idx = tid + kGmThreads * k2;
-      const int r = idx >> 5, plane = (idx >> 4) & 1, pcs = idx & 15;
+      const int r = idx >> 4, pcs = idx & 15;
       if (r < rows) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(st + r * kStRow + plane * kStPlane + 8 * pcs);
+        const uint4 v = *reinterpret_cast<const uint4 *>(st + r * kStRow + 8 * pcs);
         const int rr = m0 + r;
         const size_t off = shared ? static_cast<size_t>(a.n_rows) * a.F + static_cast<size_t>(rr) * a.Fs
                                   : static_cast<size_t>(un.r0 + rr) * a.F;
         uint16_t *arow = reinterpret_cast<uint16_t *>(a.act + off);
-        *reinterpret_cast<uint4 *>(arow + plane * F + ct * 128 + 8 * pcs) = v;
+        *reinterpret_cast<uint4 *>(arow + ct * 128 + 8 * pcs) = v;
       }
     }
     lds_barrier();  // the next item's first A tile reuses the buffers
@@ -722,19 +767,20 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
-  __shared__ uint4 as[2][2][kPfRows][17];  // [buffer][hi, lo plane] act rows in fp16, one k-step
+  // act rows in fp16, one k-step, in [buffer][0]; the whole array holds the
+  // output tile in the epilogue
+  __shared__ uint4 as[2][2][kPfRows][17];
   __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int n = lane & 15, g = lane >> 4;
+  const int c = lane & 31, h = lane >> 5;
   const int H = a.H;
   const int n_units = gm_units(a, units, scratch);
   const int col_tiles = H / 256;
   const int n_items = units.pre[n_units] * col_tiles;
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const int pc = tid & 15;
 
   // XCD-aware order: the blocks of one XCD (block b runs on XCD b mod 8)
@@ -754,18 +800,18 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
     const int rows = min(kPfRows, un.n - m0);
     const bool shared = un.e < 0;
     const int F = shared ? a.Fs : a.F;  // == 128 KS
-    // output columns of this lane: hbase + 16 q; 32-bit offsets from
+    // output column (weight row) of this lane: hbase; 32-bit offsets from
     // block-uniform bases
-    const int hbase = ct * 256 + 32 * wave + n;
+    const int hbase = ct * 256 + 32 * wave + c;
     const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * H + hbase);
     gchar_t *dq = uniform_gptr(shared ? a.sdq : a.dq);
     gchar_t *dsc = uniform_gptr(shared ? a.sds : a.ds);
-    uint32_t woff = row0 * (nblk * 16) + 16 * g, soff = row0 * (nblk * 2);
-    constexpr uint32_t kW16 = 16 * nblk * 16, kS16 = 16 * nblk * 2;  // 16 rows further
+    uint32_t woff = row0 * (nblk * 16) + 16 * h, soff = row0 * (nblk * 2);
 
-    // A staging: thread t owns piece t % 16 of rows t / 16 + 32 i, both
-    // planes (byte offsets of the rows inside the act buffer); rows past
-    // the tile's end read its first row (results never stored)
+    // A staging: thread t owns piece t % 16 of rows t / 16 + 32 i (byte
+    // offsets of the rows inside the act buffer, which holds one fp16 plane
+    // per row here); rows past the tile's end read its first row (results
+    // never stored)
     gchar_t *ag = uniform_gptr(a.act);
     uint32_t aoff[2];
 #pragma unroll
@@ -774,42 +820,29 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
       const int rr = m0 + (r < rows ? r : 0);
       const uint32_t off = shared ? static_cast<uint32_t>(a.n_rows * a.F + rr * a.Fs)
                                   : static_cast<uint32_t>((un.r0 + rr) * a.F);
-      aoff[i] = 4 * off + 16 * pc;
+      aoff[i] = 4 * off + 16 * pc;  // the row's slot holds 4 bytes per element; its first half is used
     }
-    auto load_a = [&](int s, uint4(&v)[4]) {
+    auto load_a = [&](int s, uint4(&v)[2]) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        v[i] = load16_g(ag + (aoff[i] + 256u * s));
-        v[2 + i] = load16_g(ag + (aoff[i] + 2u * F + 256u * s));
-      }
+      for (int i = 0; i < 2; ++i) v[i] = load16_g(ag + (aoff[i] + 256u * s));
     };
-    auto f16x8 = [](const uint4 &v) {
-      return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
-    };
-    auto store_a = [&](int buf, const uint4(&v)[4]) {
-      // both planes in fp16
+    auto store_a = [&](int buf, const uint4(&v)[2]) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        as[buf][0][(tid >> 4) + 32 * i][pc] = f16x8(v[i]);
-        as[buf][1][(tid >> 4) + 32 * i][pc] = f16x8(v[2 + i]);
-      }
+      for (int i = 0; i < 2; ++i) as[buf][0][(tid >> 4) + 32 * i][pc] = v[i];
     };
-    auto load_b = [&](int s, uint4(&w)[2], u32x2_t(&sc)[2]) {
+    auto load_b = [&](int s, uint4(&w)[2], u32x2_t &sc) {
+      // blocks 4 s + 2 i + h; the four block scales of the step
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        w[q] = load16_g(dq + (woff + q * kW16 + 64u * s));
-        sc[q] = *reinterpret_cast<gu2_t *>(dsc + (soff + q * kS16 + 8u * s));
-      }
+      for (int i = 0; i < 2; ++i) w[i] = load16_g(dq + (woff + 64u * s + 32u * i));
+      sc = *reinterpret_cast<gu2_t *>(dsc + (soff + 8u * s));
     };
 
-    f32x4_t acc[2][4];
+    f32x16_t acc[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[q][mt] = zero4;
-    uint4 av[4];
+    for (int mt = 0; mt < 2; ++mt) acc[mt] = zero16();
+    uint4 av[2];
     uint4 bw[2][2];
-    u32x2_t bs[2][2];
+    u32x2_t bs[2];
     // B(0), A(0), B(1): once A(0) has arrived, B(0) has too (the counter of
     // outstanding loads drains in order) and only B(1) is pending, as at the
     // top of every later pair of steps
@@ -818,7 +851,7 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
     load_b(1, bw[1], bs[1]);
     store_a(0, av);
     lds_barrier();
-    with_msub((rows + 15) >> 4, [&](auto msc) __attribute__((always_inline)) {
+    with_msub2((rows + 31) >> 5, [&](auto msc) __attribute__((always_inline)) {
       constexpr int MS = decltype(msc)::value;
       auto step = [&](int s, auto slc) __attribute__((always_inline)) {
         constexpr int sl = decltype(slc)::value;
@@ -828,20 +861,18 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
         for (int i = 0; i < 2; ++i) pin_u32(aoff[i]);
         load_a(min(s + 1, KS - 1), av);  // A(s) is in LDS already; clamped
 #pragma unroll
-        for (int q = 0; q < 2; ++q) xpose4(bw[sl][q]);
+        for (int i = 0; i < 2; ++i) half_exchange(bw[sl][i]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          u32x4_t B[2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-            B[q] = dequant_f16_pairs(word(bw[sl][q], p), scale_pair(bs[sl][q].x, bs[sl][q].y, p));
+        for (int t8 = 0; t8 < 8; ++t8) {
+          // k 16 t8 .. 16 t8 + 15 of the step: block 2 i + (t >> 1)
+          const int i = t8 >> 2, t = t8 & 3;
+          const u32x4_t B =
+              dequant_f16_pairs(word(bw[sl][i], t), bs[sl].x, bs[sl].y, 2 * i + (t >> 1));
 #pragma unroll
           for (int mt = 0; mt < MS; ++mt) {
-            const uint4 vh = as[sl][0][16 * mt + n][4 * p + g];
-            const uint4 vl = as[sl][1][16 * mt + n][4 * p + g];
-            const u32x4_t Ah = {vh.x, vh.y, vh.z, vh.w}, Al = {vl.x, vl.y, vl.z, vl.w};
-#pragma unroll
-            for (int q = 0; q < 2; ++q) acc[q][mt] = mfma_f16(Al, B[q], mfma_f16(Ah, B[q], acc[q][mt]));
+            const uint4 v = as[sl][0][32 * mt + c][2 * t8 + h];
+            const u32x4_t A = {v.x, v.y, v.z, v.w};
+            acc[mt] = mfma32_f16(A, B, acc[mt]);
           }
         }
         load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);
@@ -860,13 +891,10 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
     constexpr int kStRow = 260;
     static_assert(kPfRows * kStRow * 4 <= sizeof(as), "output staging must fit the A buffers");
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int c = 32 * wave + 16 * q + n;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[(16 * mt + 4 * g + i) * kStRow + c] = acc[q][mt][i];
-    }
+      for (int jj = 0; jj < 16; ++jj)
+        st[(32 * mt + (jj & 3) + 8 * (jj >> 2) + 4 * h) * kStRow + 32 * wave + c] = acc[mt][jj];
     lds_barrier();
 #pragma unroll
     for (int k2 = 0; k2 < 8; ++k2) {
@@ -928,8 +956,12 @@ static bool gm_units_fit(const FfnArgs &a) {
   return (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1) <= kGmMaxUnits;
 }
 
+// The pipelined GEMMs run as a pair (the gate/up one hands the down one its
+// SwiGLU rows as one fp16 plane; the generic kernels use bf16 hi and lo).
+static bool gm_pair_ok(const FfnArgs &a) { return a.H == 128 * 16 && a.F == 128 * 4 && gm_units_fit(a); }
+
 hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
-  if (a.H == 128 * 16 && a.F % 128 == 0 && gm_units_fit(a)) {
+  if (gm_pair_ok(a)) {
     return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128), 1)), dim3(kGmThreads), 0,
                          s, a);
   }
@@ -938,7 +970,7 @@ hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
-  if (a.F == 128 * 4 && a.H % 256 == 0 && gm_units_fit(a)) {
+  if (gm_pair_ok(a)) {
     return launch_kernel(down_gemm_kernel<4>, dim3(gm_grid(pf_tiles_upper(a) * (a.H / 256), 2)), dim3(kGmThreads), 0, s,
                          a);
   }

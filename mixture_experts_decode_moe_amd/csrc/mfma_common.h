@@ -40,18 +40,22 @@ MOE_DEV uint32_t bf16x2_to_f16x2(uint32_t u) {
 }
 
 // Eight nibbles (one k-group of a 32-element block, stored as q + 8) and the
-// block's fp16 scale s as the pair (s, s) -> four fp16 pairs (q_i s,
-// q_{i+4} s), i = 0..3, in the pair order of magic_pairs: 0x6400 | n is
-// 1024 + n exactly, minus 1032 gives q exactly, and the product with s is
-// rounded once to fp16 (relative error at most 2^-11).
-MOE_DEV u32x4_t dequant_f16_pairs(uint32_t w, uint32_t s2) {
+// block's fp16 scale s -> four fp16 pairs (q_i s, q_{i+4} s), i = 0..3, in
+// the pair order of magic_pairs: 0x6400 | n is 1024 + n exactly, minus 1032
+// gives q exactly, and the product with s is rounded once to fp16 (relative
+// error at most 2^-11).  s is scale p (0..3) of a pair of words holding four
+// consecutive scales; the packed multiply reads it from its half of the word
+// for both lanes of the pair (no separate splat).
+MOE_DEV u32x4_t dequant_f16_pairs(uint32_t w, uint32_t s01, uint32_t s23, int p) {
   const uint32_t ev = w & 0x0F0F0F0Fu;
   const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;
   const uint32_t hi = 0x64646464u;
   const uint32_t r[4] = {__builtin_amdgcn_perm(hi, ev, 0x04020400u), __builtin_amdgcn_perm(hi, od, 0x04020400u),
                          __builtin_amdgcn_perm(hi, ev, 0x04030401u), __builtin_amdgcn_perm(hi, od, 0x04030401u)};
   const f16x2_t off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
-  const f16x2_t sc = __builtin_bit_cast(f16x2_t, s2);
+  const f16x2_t sw = __builtin_bit_cast(f16x2_t, p < 2 ? s01 : s23);
+  const _Float16 sv = (p & 1) ? sw[1] : sw[0];
+  const f16x2_t sc = {sv, sv};
   u32x4_t out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -59,13 +63,6 @@ MOE_DEV u32x4_t dequant_f16_pairs(uint32_t w, uint32_t s2) {
     out[i] = __builtin_bit_cast(uint32_t, q * sc);
   }
   return out;
-}
-
-// fp16 scale p (0..3) of a pair of words holding four consecutive scales,
-// as the pair (s, s)
-MOE_DEV uint32_t scale_pair(uint32_t s01, uint32_t s23, int p) {
-  const uint32_t w = p < 2 ? s01 : s23;
-  return __builtin_amdgcn_perm(w, w, (p & 1) ? 0x03020302u : 0x01000100u);
 }
 
 MOE_DEV f32x4_t mfma_bf16_k16(const u32x2_t &a, const u32x2_t &b, const f32x4_t &c) {
