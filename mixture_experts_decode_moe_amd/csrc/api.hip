@@ -85,7 +85,7 @@ struct StageMark {
 };
 
 struct LayerWs {
-  uint32_t *control;  // kControlBytes of words kept zero between calls; [0]: routing counter
+  uint32_t *control;  // kControlBytes of words kept zero between calls; [0..1]: prefill gate/up item queue
   float *part;        // fused routing: partial logits [S][T][E]
   float *logits;
   int32_t *ids;
@@ -94,6 +94,7 @@ struct LayerWs {
   int32_t *units;  // [E][4]: expert, first row, rows, 0 of each active unit
   float *row_w;
   float *act, *rows_out;
+  uint16_t *x16;  // x in fp16 for the prefill GEMMs, written by the router GEMM
   size_t bytes;
 };
 
@@ -125,6 +126,7 @@ LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
   const size_t Fs = L->shared.n_experts == 1 ? L->shared.ffn : 0;
   w.act = c.take<float>(TK * L->routed.ffn + static_cast<size_t>(T) * Fs);
   w.rows_out = c.take<float>((TK + (Fs ? T : 0)) * L->hidden);
+  w.x16 = c.take<uint16_t>(static_cast<size_t>(T) * L->hidden);
   w.bytes = align_up(c.off, 256);
   return w;
 }
@@ -382,7 +384,11 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
     StageMark m(MOE_STAGE_ROUTE, s);
     e = xa.route_here ? launch_route_partial(fa, s) : launch_route_fused(fa, s);
   } else {
-    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw};
+    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw, w.x16};
+    if (router_writes_x16(ra)) {
+      xa.x16 = w.x16;
+      xa.queue = w.control;
+    }
     {
       StageMark m(MOE_STAGE_ROUTE, s);
       e = launch_router_logits(ra, s);

@@ -95,8 +95,11 @@ struct RouteArgs {
   float *logits;
   int32_t *ids;
   float *w;
+  uint16_t *x16;  // optional [T][H]: x in fp16, pair-permuted 8-element pieces
 };
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s);
+// whether launch_router_logits writes x16 (when given) for this call
+bool router_writes_x16(const RouteArgs &a);
 hipError_t launch_topk(const RouteArgs &a, hipStream_t s);
 
 // Router partial logits, then top-k + permutation in one block, for a decode
@@ -142,6 +145,7 @@ struct FfnArgs {
   const void *gq, *gs, *uq, *us, *dq, *ds;        // routed [E][..]
   const void *sgq, *sgs, *suq, *sus, *sdq, *sds;  // shared [1][..]
   const uint16_t *x;
+  const uint16_t *x16;      // NULL, or x in fp16 as RouteArgs::x16 (prefill GEMMs read it)
   int32_t T;
   int32_t n_rows;           // routed rows
   const int32_t *offsets;   // [E+1] or NULL
@@ -153,6 +157,7 @@ struct FfnArgs {
   float *rows_out;          // [n_rows + (Fs ? T : 0)][H]
   int32_t max_units;        // upper bound of routed units (grid sizing)
   const int32_t *units;     // [max_units] int4 (expert, first row, rows, 0) or NULL
+  uint32_t *queue;          // NULL, or two words, zero between calls: the prefill gate/up item queue
   // decode layer calls (E <= 256): the gate/up kernel routes the batch
   // itself from the router's partial logits and its last block publishes
   // the routing (the offsets, active, n_active, row_tok and row_w above

@@ -491,6 +491,11 @@ MOE_DEV void with_msub2(int msub, Fn &&fn) {
     fn(IntC<2>{});
 }
 
+// s_waitcnt immediate that waits until at most n (< 64) vector memory
+// requests are outstanding and leaves the other counters alone (GFX9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // 32x32 output tiles (v_mfma_f32_32x32x16_f16, twice the rate of the 16x16
 // shape on this chip): lane l holds row l % 32 of A and column l % 32 of B
 // with k-group l / 32 (8 consecutive k, pair-permuted) of each 16-k step,
@@ -531,6 +536,7 @@ struct GmUnits {
   int e[kGmMaxUnits], r0[kGmMaxUnits], n[kGmMaxUnits];
 };
 
+template <int ROWS = kPfRows>
 MOE_DEV int gm_units(const FfnArgs &a, GmUnits &G, int *scratch) {
   static_assert(kGmThreads >= kGmMaxUnits, "one unit per thread");
   const int n_units = (a.Fs > 0 ? 1 : 0) + routed_units(a);
@@ -541,7 +547,7 @@ MOE_DEV int gm_units(const FfnArgs &a, GmUnits &G, int *scratch) {
     G.e[tid] = x.e;
     G.r0[tid] = x.r0;
     G.n[tid] = x.n;
-    c = x.n > 0 ? (x.n + kPfRows - 1) / kPfRows : 0;
+    c = x.n > 0 ? (x.n + ROWS - 1) / ROWS : 0;
   }
   const int lane = tid & 63, wave = tid >> 6;
   int inc = c;
@@ -568,7 +574,9 @@ MOE_DEV PfUnit gm_unit(const GmUnits &G, int u) {
   return x;
 }
 
-template <int KS>
+// X16: the x rows come already in fp16, pair-permuted (a.x16), and are
+// staged as they are.
+template <int KS, bool X16>
 __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
   static_assert(KS % 4 == 0, "the k loop runs over groups of four steps");
   __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted fp16, one k-step
@@ -621,7 +629,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
     // past the tile's end read token 0's row: their products land in
     // accumulator rows that are never stored (every row of an MFMA result
     // depends on its own A row only), and the requests stay unconditional.
-    gchar_t *xg = uniform_gptr(a.x);
+    gchar_t *xg = uniform_gptr(X16 ? static_cast<const void *>(a.x16) : static_cast<const void *>(a.x));
     uint32_t xoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -642,9 +650,13 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
       // pair-permuted, in fp16
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const u32x4_t pp = pair_permute(v[i]);
-        as[buf][(tid >> 4) + 32 * i][pc] = make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y),
-                                                      bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
+        if constexpr (X16) {
+          as[buf][(tid >> 4) + 32 * i][pc] = v[i];
+        } else {
+          const u32x4_t pp = pair_permute(v[i]);
+          as[buf][(tid >> 4) + 32 * i][pc] = make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y),
+                                                        bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
+        }
       }
     };
     auto load_b = [&](int s, uint4(&w)[2], u32x2_t &sc) {
@@ -764,6 +776,231 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
   }
 }
 
+// ------------------------------------------------ gate/up, 128-row items
+// The layer's gate/up GEMM once its router GEMM has written x in fp16
+// operand form (a.x16), with the workspace's item queue (a.queue: two words
+// that are zero between calls).  An item is (unit, up to 128 rows, 128
+// SwiGLU columns), so that an expert's rows (64 on average for a prefill
+// chunk, rarely above 128) share one pass over its weights: each weight is
+// dequantized once per expert instead of once per 64 rows, and a step
+// carries up to four 32-row tiles of matrix work per dequantized chunk.
+// Blocks take items from the queue (the shared expert's, the largest,
+// first), so that they finish together although items differ in size.
+// The x rows go from global memory straight into LDS (no registers), three
+// steps ahead, into four buffers; each row's sixteen 16-byte pieces are
+// stored at slot piece ^ (row & 15), so that the MFMA operand reads, 16
+// rows at one piece, meet every LDS bank once.
+constexpr int kG2Rows = 128;
+constexpr int kG2Bufs = 4;
+
+template <int KS>
+__global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a) {
+  static_assert(KS % 4 == 0, "the k loop runs over groups of four steps");
+  // the A buffers, [kG2Rows][16] pieces each: separate arrays, so that the
+  // compiler sees that the LDS reads of a step do not touch the buffer its
+  // direct loads are filling
+  __shared__ uint4 g2_a0[kG2Rows * 16], g2_a1[kG2Rows * 16], g2_a2[kG2Rows * 16], g2_a3[kG2Rows * 16];
+  __shared__ GmUnits units;
+  __shared__ int scratch[kGmThreads / 64];
+  __shared__ int next_item;
+  constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const bool up_lane = c >= 16;
+  const int T = a.T;
+  const int H = 128 * KS;
+  const int n_units = gm_units<kG2Rows>(a, units, scratch);
+  const int col_tiles = a.F / 128;
+  const int n_items = units.pre[n_units] * col_tiles;
+  auto abuf = [&](int b, int r) __attribute__((always_inline)) {
+    return (b == 0 ? g2_a0 : b == 1 ? g2_a1 : b == 2 ? g2_a2 : g2_a3) + r * 16;
+  };
+
+  for (;;) {
+    if (tid == 0) next_item = static_cast<int>(atomicAdd(&a.queue[0], 1u));
+    lds_barrier();
+    const int item = next_item;
+    if (item >= n_items) break;
+    const int j = item / col_tiles;
+    const int ct = item - j * col_tiles;
+    const int u = pf_find(units.pre, n_units, j);
+    const PfUnit un = gm_unit(units, u);
+    const int m0 = (j - units.pre[u]) * kG2Rows;
+    const int rows = min(kG2Rows, un.n - m0);
+    const bool shared = un.e < 0;
+    const int F = shared ? a.Fs : a.F;
+    // this lane's weight row: the gate (lanes c < 16) or up (c >= 16) row of
+    // SwiGLU column col
+    const int col = ct * 128 + 16 * wave + (c & 15);
+    gchar_t *gq = uniform_gptr(shared ? a.sgq : a.gq);
+    gchar_t *uq = uniform_gptr(shared ? a.suq : a.uq);
+    gchar_t *gsc = uniform_gptr(shared ? a.sgs : a.gs);
+    gchar_t *usc = uniform_gptr(shared ? a.sus : a.us);
+    gchar_t *wq = up_lane ? uq : gq;
+    gchar_t *wsc = up_lane ? usc : gsc;
+    const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * F + col);
+    uint32_t woff = row0 * (nblk * 16) + 16 * h, soff = row0 * (nblk * 2);
+
+    // A: instruction i of this wave fills rows 4 (wave + 8 i) .. + 3 of a
+    // buffer, lane l row 4 (wave + 8 i) + l / 16, slot l % 16 (piece
+    // (l % 16) ^ row % 16).  Rows past the tile's end read token 0's row:
+    // their products land in accumulator rows that are never stored.
+    gchar_t *xg = uniform_gptr(a.x16);
+    uint32_t xoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * (wave + 8 * i) + (lane >> 4);
+      int t = 0;
+      if (r < rows) {
+        const int rr = un.r0 + m0 + r;
+        t = shared ? rr : (a.row_tok ? a.row_tok[rr] : rr);
+        t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+      }
+      xoff[i] = static_cast<uint32_t>(t) * (2 * H) + 16 * ((lane & 15) ^ (r & 15));
+    }
+    // only the 32-row tiles that hold rows: instruction i covers rows of
+    // tiles < i + 1, so an item of MS tiles issues its first MS
+    auto load_a = [&](int s, int b, auto msc) __attribute__((always_inline)) {
+      constexpr int MS = decltype(msc)::value;
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+        __builtin_amdgcn_global_load_lds(xg + (xoff[i] + 256u * s),
+                                         (__attribute__((address_space(3))) void *)(abuf(b, 4 * (wave + 8 * i))), 16,
+                                         0, 0);
+    };
+    auto load_b = [&](int s, uint4(&w)[2], u32x2_t &sc) __attribute__((always_inline)) {
+      // blocks 4 s + 2 i + h; the four block scales of the step
+#pragma unroll
+      for (int i = 0; i < 2; ++i) w[i] = load16_g(wq + (woff + 64u * s + 32u * i));
+      sc = *reinterpret_cast<gu2_t *>(wsc + (soff + 8u * s));
+    };
+
+    f32x16_t acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = zero16();
+    uint4 bw[4][2];  // weight chunks, slot s & 3
+    u32x2_t bs[4];   // their block scales
+    with_msub((rows + 31) >> 5, [&](auto msc) __attribute__((always_inline)) {
+      constexpr int MS = decltype(msc)::value;
+      // A(0), B(0), A(1), B(1), A(2), B(2), B(3): the wait before the first
+      // step leaves the requests after A(0) pending (B(0) 3, A(1) MS,
+      // B(1) 3, A(2) MS, B(2) 3, B(3) 3)
+      load_a(0, 0, msc);
+      load_b(0, bw[0], bs[0]);
+      load_a(1, 1, msc);
+      load_b(1, bw[1], bs[1]);
+      load_a(2, 2, msc);
+      load_b(2, bw[2], bs[2]);
+      load_b(3, bw[3], bs[3]);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(12 + 2 * MS));
+      lds_barrier();
+      auto step = [&](int s, auto slc) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slc)::value;
+        pin_u32(woff);
+        pin_u32(soff);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pin_u32(xoff[i]);
+        // A three steps ahead (clamped: past the end it re-reads the last
+        // step into a buffer no later step reads)
+        load_a(min(s + 3, KS - 1), (sl + 3) & 3, msc);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) half_exchange(bw[sl][i]);
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) {
+          // k 16 t8 .. 16 t8 + 15 of the step: block 2 i + (t >> 1)
+          const int i = t8 >> 2, t = t8 & 3;
+          const u32x4_t B = dequant_f16_pairs(word(bw[sl][i], t), bs[sl].x, bs[sl].y, 2 * i + (t >> 1));
+          const int slot = (2 * t8 + h) ^ (c & 15);
+          uint4 Av[MS];
+#pragma unroll
+          for (int mt = 0; mt < MS; ++mt) Av[mt] = abuf(sl, 32 * mt + c)[slot];
+#pragma unroll
+          for (int mt = 0; mt < MS; ++mt) {
+            const u32x4_t A = {Av[mt].x, Av[mt].y, Av[mt].z, Av[mt].w};
+            acc[mt] = mfma32_f16(A, B, acc[mt]);
+          }
+        }
+        load_b(min(s + 4, KS - 1), bw[sl], bs[sl]);
+        __builtin_amdgcn_sched_barrier(0);
+        // A(s + 1) has landed once at most the requests issued after it are
+        // pending: B(s + 2), A(s + 2), B(s + 3), A(s + 3), B(s + 4)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(9 + 2 * MS));
+        lds_barrier();
+      };
+      // fully unrolled: no loop back-edge, so the compiler can tell which
+      // direct loads each step's LDS reads wait for
+#pragma unroll
+      for (int s = 0; s < KS; s += 4) {
+        step(s, IntC<0>{});
+        step(s + 1, IntC<1>{});
+        step(s + 2, IntC<2>{});
+        step(s + 3, IntC<3>{});
+      }
+    });
+    // the clamped A requests still in flight write into the buffers: let
+    // them land before the staging below reuses the memory
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    // SwiGLU into LDS, rounded once to fp16 (as in gateup_gemm_kernel):
+    // swapping register j with j + 8 between the 16-lane halves of each
+    // 32-lane row gives lanes c < 16 gate and up of value j and lanes
+    // c >= 16 those of value j + 8.  Rows [128][128 + 8 pad], rows 0-63 in
+    // the first A buffer and 64-127 in the second.
+    uint16_t *st0 = reinterpret_cast<uint16_t *>(g2_a0), *st1 = reinterpret_cast<uint16_t *>(g2_a1);
+    constexpr int kStRow = 136;
+    static_assert(64 * kStRow * 2 <= sizeof(g2_a0), "SwiGLU staging must fit the A buffers");
+    const int cl = act_pos<MOE_W_INT4_B32>(16 * wave + (c & 15));  // tiles start at multiples of 8
+    const int rbase = (up_lane ? 16 : 0) + 4 * h;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int jj = 0; jj < 8; jj += 2) {
+        const int r = 32 * mt + (jj & 3) + 8 * (jj >> 2) + rbase;
+        float v[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto gu = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[mt][jj + d]),
+                                                           __float_as_uint(acc[mt][jj + d + 8]), false, false);
+          const float gv = __uint_as_float(gu[0]), uv = __uint_as_float(gu[1]);
+          v[d] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
+        }
+        const f32x2v_t vv = {v[0], v[1]};
+        const uint32_t hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(vv, f16x2_t));
+        uint16_t *st = mt < 2 ? st0 : st1;
+        const int rl = r & 63;
+        st[rl * kStRow + cl] = static_cast<uint16_t>(hv);
+        st[(rl + 1) * kStRow + cl] = static_cast<uint16_t>(hv >> 16);
+      }
+    lds_barrier();
+    // 16-byte stores of whole row segments: piece (row, 16 of them)
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int idx = tid + kGmThreads * k2;
+      const int r = idx >> 4, pcs = idx & 15;
+      if (r < rows) {
+        const uint4 v = *reinterpret_cast<const uint4 *>((k2 < 2 ? st0 : st1) + (r & 63) * kStRow + 8 * pcs);
+        const int rr = m0 + r;
+        const size_t off = shared ? static_cast<size_t>(a.n_rows) * a.F + static_cast<size_t>(rr) * a.Fs
+                                  : static_cast<size_t>(un.r0 + rr) * a.F;
+        uint16_t *arow = reinterpret_cast<uint16_t *>(a.act + off);
+        *reinterpret_cast<uint4 *>(arow + ct * 128 + 8 * pcs) = v;
+      }
+    }
+    lds_barrier();  // the next item's first A tiles reuse the memory
+  }
+  // the last block out leaves the queue words zero for the next call
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(&a.queue[1], 1u) == gridDim.x - 1) {
+      atomicExch(&a.queue[0], 0u);
+      atomicExch(&a.queue[1], 0u);
+    }
+  }
+}
+
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
@@ -799,7 +1036,6 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
     const int m0 = (j - units.pre[u]) * kPfRows;
     const int rows = min(kPfRows, un.n - m0);
     const bool shared = un.e < 0;
-    const int F = shared ? a.Fs : a.F;  // == 128 KS
     // output column (weight row) of this lane: hbase; 32-bit offsets from
     // block-uniform bases
     const int hbase = ct * 256 + 32 * wave + c;
@@ -961,9 +1197,18 @@ static bool gm_units_fit(const FfnArgs &a) {
 static bool gm_pair_ok(const FfnArgs &a) { return a.H == 128 * 16 && a.F == 128 * 4 && gm_units_fit(a); }
 
 hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
+  if (gm_pair_ok(a) && a.x16 && a.queue) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return launch_kernel(gateup_gemm128_kernel<16>, dim3(cus), dim3(kGmThreads), 0, s, a);
+  }
   if (gm_pair_ok(a)) {
-    return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128), 1)), dim3(kGmThreads), 0,
-                         s, a);
+    const dim3 grid(gm_grid(pf_tiles_upper(a) * (a.F / 128), 1));
+    if (a.x16) return launch_kernel(gateup_gemm_kernel<16, true>, grid, dim3(kGmThreads), 0, s, a);
+    return launch_kernel(gateup_gemm_kernel<16, false>, grid, dim3(kGmThreads), 0, s, a);
   }
   return launch_kernel(gateup_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.F / kPfCols))), dim3(kPfThreads), 0,
                        s, a);

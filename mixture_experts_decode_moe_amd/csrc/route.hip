@@ -12,6 +12,7 @@
 #include <float.h>
 #include <math.h>
 
+#include "mfma_common.h"
 #include "route_common.h"
 
 namespace moe {
@@ -142,7 +143,8 @@ constexpr int kRmThreads = 512;
 __global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__restrict__ wr,
                                                                  const float *__restrict__ bias,
                                                                  const uint16_t *__restrict__ x, int32_t T,
-                                                                 int32_t H, int32_t E, float *__restrict__ logits) {
+                                                                 int32_t H, int32_t E, float *__restrict__ logits,
+                                                                 uint16_t *__restrict__ x16) {
   __shared__ float xs[2][kRmTok][kRmPad];
   __shared__ float ws[2][kRmExp][kRmPad];
   const int tid = threadIdx.x;
@@ -168,7 +170,15 @@ __global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__
 #pragma unroll
     for (int i = 0; i < 2; ++i) wrr[i] = wv ? wp[s * (kRmK / 4) + i] : make_float4(0.f, 0.f, 0.f, 0.f);
   };
-  auto store = [&](int buf) {
+  // the first expert tile's blocks also write x in fp16, pair-permuted (the
+  // prefill expert GEMMs' operand form)
+  const bool x16w = x16 && blockIdx.x == 0 && xv;
+  auto store = [&](int buf, int s) {
+    if (x16w) {
+      const u32x4_t pp = pair_permute(xr);
+      *reinterpret_cast<uint4 *>(x16 + static_cast<size_t>(t0 + xt) * H + s * kRmK + xk) =
+          make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y), bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
+    }
     if (xthr) {
       const uint32_t d[4] = {xr.x, xr.y, xr.z, xr.w};
 #pragma unroll
@@ -183,7 +193,7 @@ __global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__
   rf32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const int steps = H / kRmK;
   load(0);
-  store(0);
+  store(0, 0);
   lds_barrier();
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
@@ -203,7 +213,7 @@ __global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__
         for (int c = 0; c < 4; ++c) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[c], bb[c], acc[mt], 0, 0, 0);
       }
     }
-    if (s + 1 < steps) store(buf ^ 1);
+    if (s + 1 < steps) store(buf ^ 1, s + 1);
     lds_barrier();
   }
   // the upper half's sums to LDS (the x buffers are free), added to the
@@ -323,10 +333,14 @@ hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+static bool router_mfma_ok(const RouteArgs &a) { return a.T > kFusedTokens && a.H % kRmK == 0; }
+
+bool router_writes_x16(const RouteArgs &a) { return a.x16 != nullptr && router_mfma_ok(a); }
+
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s) {
-  if (a.T > kFusedTokens && a.H % kRmK == 0) {
+  if (router_mfma_ok(a)) {
     dim3 g((a.E + kRmExp - 1) / kRmExp, (a.T + kRmTok - 1) / kRmTok);
-    router_mfma_kernel<<<g, kRmThreads, 0, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits);
+    router_mfma_kernel<<<g, kRmThreads, 0, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits, a.x16);
     return hipGetLastError();
   }
   dim3 grid((a.E + 3) / 4, (a.T + kRouterTokens - 1) / kRouterTokens);

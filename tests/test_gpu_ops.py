@@ -135,16 +135,18 @@ def test_permute_exact(mb, T, K, E, mode):
     assert np.array_equal(out["active"].cpu().numpy()[:na], ref["active"])
 
 
-@pytest.mark.parametrize("cfg", [0, 2])
-def test_expert_ffn_and_combine(mb, cfg):
+@pytest.mark.parametrize("cfg,tokens", [(0, None), (2, None), (4, 48)])
+def test_expert_ffn_and_combine(mb, cfg, tokens):
     """moe_expert_ffn on the oracle's permutation, then moe_combine, each
-    compared with the oracle's rows and layer output."""
+    compared with the oracle's rows and layer output.  The 48-token case of
+    the prefill layer runs the grouped GEMMs on x as given (bf16; the layer
+    call hands them x already in fp16)."""
     import torch
     import parity_util as pu
     shape = synth.CONFIGS[cfg]
-    say(f"expert_ffn+combine cfg{cfg}")
+    say(f"expert_ffn+combine cfg{cfg} tokens {tokens}")
     layer = synth.make_layer(shape)
-    x = synth.make_x(shape)
+    x = synth.make_x(shape, tokens=tokens)
     T, K, E, H = x.shape[0], shape.top_k, shape.n_experts, shape.hidden
     y_ref, ids, w, _ = oracle.layer_forward(layer, x)
     p = oracle.permute(ids, w.astype(np.float32), E)
