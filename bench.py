@@ -293,21 +293,24 @@ def main():
     # take the one-launch down projection + combine (it writes y, not the
     # expert rows)
     fused_down = T <= 8 and not stack
-    gateup_bytes = U * gu_bytes + sh_gu + T * H * 2 + (T * K * F + T * Fs) * 4
+    prefill = T > 16
+    # the SwiGLU rows between the two kernels: bf16 hi + lo (4 bytes an
+    # element) for decode calls, one fp16 plane (2 bytes) for prefill
+    act_b = 2 if prefill else 4
+    gateup_bytes = U * gu_bytes + sh_gu + T * H * 2 + (T * K * F + T * Fs) * act_b
     down_out = T * H * 4 if fused_down else (T * K + (T if Fs else 0)) * H * 4
-    down_bytes = U * dn_bytes + sh_dn + (T * K * F + T * Fs) * 4 + down_out
+    down_bytes = U * dn_bytes + sh_dn + (T * K * F + T * Fs) * act_b + down_out
     kern = {"gateup": (gateup_bytes, stage_us["gateup"]), "down": (down_bytes, stage_us["down"])}
     dom = max(kern, key=lambda k: kern[k][1])
     dom_bytes, dom_us = kern[dom]
     achieved_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
-    prefill = T > 16
     kernel_name = {("gateup", False): "gateup_mfma_kernel",
                    ("down", False): "down_combine_kernel" if fused_down else "down_mfma_kernel",
-                   ("gateup", True): "gateup_gemm_kernel", ("down", True): "down_gemm_kernel"}[(dom, prefill)]
+                   ("gateup", True): "gateup_gemm128_kernel", ("down", True): "down_gemm_kernel"}[(dom, prefill)]
     if prefill:
         # useful matrix-core work of the dominant grouped GEMM: every routed
         # and shared row through gate+up (2 H F each, 2 flops a product) or
-        # down (H F), padding and the hi/lo split not counted
+        # down (H F), padding not counted
         rows = T * K + (T if shape.shared_ffn else 0)
         flops = {"gateup": 2.0 * rows * 2 * H * F, "down": 2.0 * rows * H * F}[dom]
         achieved_tf = flops / (dom_us * 1e-6) / 1e12

@@ -908,11 +908,18 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 2; ++i) half_exchange(bw[sl][i]);
+        // k 16 t8 .. 16 t8 + 15 of the step: block 2 i + (t >> 1), t8 = 4 i + t;
+        // the operand of t8 + 1 is dequantized before the products of t8
+        // are issued, so the vector unit has work while they run
+        auto dq = [&](int t8) __attribute__((always_inline)) {
+          const int i = t8 >> 2, t = t8 & 3;
+          return dequant_f16_pairs(word(bw[sl][i], t), bs[sl].x, bs[sl].y, 2 * i + (t >> 1));
+        };
+        u32x4_t Bn = dq(0);
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) {
-          // k 16 t8 .. 16 t8 + 15 of the step: block 2 i + (t >> 1)
-          const int i = t8 >> 2, t = t8 & 3;
-          const u32x4_t B = dequant_f16_pairs(word(bw[sl][i], t), bs[sl].x, bs[sl].y, 2 * i + (t >> 1));
+          const u32x4_t B = Bn;
+          if (t8 < 7) Bn = dq(t8 + 1);
           const int slot = (2 * t8 + h) ^ (c & 15);
           uint4 Av[MS];
 #pragma unroll
