@@ -155,6 +155,7 @@ FfnArgs ffn_args(const moe_experts &W, const moe_experts *S, int32_t H, const ui
   a.x = x;
   a.T = T;
   a.n_rows = n_rows;
+  a.n_experts = W.n_experts;
   return a;
 }
 

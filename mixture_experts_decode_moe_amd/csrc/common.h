@@ -148,6 +148,7 @@ struct FfnArgs {
   const uint16_t *x16;      // NULL, or x in fp16 as RouteArgs::x16 (prefill GEMMs read it)
   int32_t T;
   int32_t n_rows;           // routed rows
+  int32_t n_experts;        // routed experts (offsets has n_experts + 1 entries)
   const int32_t *offsets;   // [E+1] or NULL
   const int32_t *active;    // [E]
   const int32_t *n_active;  // [1]

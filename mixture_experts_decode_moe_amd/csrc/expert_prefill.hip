@@ -793,6 +793,74 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
 constexpr int kG2Rows = 128;
 constexpr int kG2Bufs = 4;
 
+// The unit table of a layer call for the 128-row gate/up kernel, in the
+// order its items are taken: the shared expert first, then the routed
+// experts by the number of 32-row tiles of their first item (4 down to 1),
+// ties by expert index, so that the items left for the last round are the
+// smallest.  The routed units are the experts with rows (offsets[e + 1] >
+// offsets[e]): one read of the offsets, no dependent reads.  Needs
+// n_experts <= kGmMaxUnits - 1.
+MOE_DEV int gm_units_by_size(const FfnArgs &a, GmUnits &G, int *scratch, int (*cnt)[4]) {
+  static_assert(kGmThreads >= kGmMaxUnits, "one unit per thread");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int E = a.n_experts;
+  const int sh = a.Fs > 0 ? 1 : 0;
+  int r0 = 0, n = 0;
+  if (tid < E) {
+    r0 = a.offsets[tid];
+    n = a.offsets[tid + 1] - r0;
+  }
+  // class 0: four tiles ... 3: one tile; 4: no rows
+  const int cls = (tid < E && n > 0) ? 4 - (min(n, kG2Rows) + 31) / 32 : 4;
+  uint64_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint64_t m = __ballot(cls == k);
+    if (k == cls) mine = m;
+    if (lane == 0) cnt[wave][k] = __popcll(m);
+  }
+  lds_barrier();
+  int n_routed = 0, pos = 0;
+#pragma unroll
+  for (int w = 0; w < kGmThreads / 64; ++w)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int v = cnt[w][k];
+      n_routed += v;
+      pos += (k < cls || (k == cls && w < wave)) ? v : 0;
+    }
+  if (cls < 4) {
+    pos += __popcll(mine & ((1ull << lane) - 1));
+    G.e[sh + pos] = tid;
+    G.r0[sh + pos] = r0;
+    G.n[sh + pos] = n;
+  }
+  if (sh && tid == 0) {
+    G.e[0] = -1;
+    G.r0[0] = 0;
+    G.n[0] = a.T;
+  }
+  const int n_units = sh + n_routed;
+  lds_barrier();
+  int c = 0;
+  if (tid < n_units) c = (G.n[tid] + kG2Rows - 1) / kG2Rows;
+  int inc = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  lds_barrier();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += scratch[w];
+  base += inc - c;
+  if (tid <= n_units) G.pre[tid] = base;
+  lds_barrier();
+  return n_units;
+}
+
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a) {
   static_assert(KS % 4 == 0, "the k loop runs over groups of four steps");
@@ -802,6 +870,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
   __shared__ uint4 g2_a0[kG2Rows * 16], g2_a1[kG2Rows * 16], g2_a2[kG2Rows * 16], g2_a3[kG2Rows * 16];
   __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
+  __shared__ int class_cnt[kGmThreads / 64][4];
   __shared__ int next_item;
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
   const int tid = threadIdx.x;
@@ -811,7 +880,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
   const bool up_lane = c >= 16;
   const int T = a.T;
   const int H = 128 * KS;
-  const int n_units = gm_units<kG2Rows>(a, units, scratch);
+  const int n_units = gm_units_by_size(a, units, scratch, class_cnt);
   const int col_tiles = a.F / 128;
   const int n_items = units.pre[n_units] * col_tiles;
   auto abuf = [&](int b, int r) __attribute__((always_inline)) {
@@ -1204,7 +1273,7 @@ static bool gm_units_fit(const FfnArgs &a) {
 static bool gm_pair_ok(const FfnArgs &a) { return a.H == 128 * 16 && a.F == 128 * 4 && gm_units_fit(a); }
 
 hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
-  if (gm_pair_ok(a) && a.x16 && a.queue) {
+  if (gm_pair_ok(a) && a.x16 && a.queue && a.offsets && a.n_experts < kGmMaxUnits) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
       int v = 0;

@@ -127,117 +127,136 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restr
 
 // ---------------------------------------------------------- large batches
 //
-// For more than kFusedTokens tokens the logits are an fp32 GEMM on the
-// matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation):
-// a block owns 32 tokens x 64 experts, with 8 waves: wave w takes the
-// experts 16 (w % 4)..+15 of both 16-token halves over one half of each
-// 64-wide step of the reduction dimension (w / 4), and the two halves'
-// sums are added in LDS at the end (lower half first).  The x rows (bf16,
-// widened exactly) and the router rows are staged in LDS.  Two waves a SIMD
-// hide each other's operand reads.  moe_route and the layer use this
-// kernel alike for such batches.
-typedef float rf32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kRmTok = 32, kRmExp = 64, kRmK = 64, kRmPad = 68;
+// For more than kFusedTokens tokens the logits are a GEMM on the bf16 matrix
+// cores with fp32 accuracy: x is exact in bf16, and each fp32 router weight
+// w is split exactly into three bf16 parts, w = hi + mid + lo (hi: w cut to
+// 8 significant bits, mid: the remainder cut likewise, lo: the last 8 bits),
+// so three v_mfma_f32_32x32x16_bf16 per 16-wide k-step form every product
+// exactly and accumulate it in fp32, as an fp32 dot product does (in another
+// order).  A block owns 32 tokens x 64 experts with 8 waves: wave w takes
+// expert tile w & 1 over the quarter w >> 1 of the reduction dimension, its
+// operands straight from global memory (lane l: token / expert l % 32, the
+// 8 consecutive k of group l / 32), and the four quarters' sums are added in
+// LDS in quarter order.  moe_route and the layer use this kernel alike for
+// such batches.
+constexpr int kRmTok = 32, kRmExp = 64, kRmK = 64;
 constexpr int kRmThreads = 512;
+
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x16_t __attribute__((ext_vector_type(16)));
+
+// eight fp32 weights -> their hi, mid and lo bf16 parts, pairs in k order
+MOE_DEV void split3(const float4 &w0, const float4 &w1, u32x4_t &hi, u32x4_t &mid, u32x4_t &lo) {
+  const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  uint32_t ph[8], pm[8], pl[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h = __float_as_uint(w[i]) & 0xFFFF0000u;
+    const float r1 = w[i] - __uint_as_float(h);  // exact
+    const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(m);  // exact, at most 8 significant bits
+    ph[i] = h;
+    pm[i] = m;
+    pl[i] = __float_as_uint(r2);  // its low 16 bits are zero
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // (element 2i in the low half, 2i + 1 in the high half)
+    hi[i] = __builtin_amdgcn_perm(ph[2 * i + 1], ph[2 * i], 0x07060302u);
+    mid[i] = __builtin_amdgcn_perm(pm[2 * i + 1], pm[2 * i], 0x07060302u);
+    lo[i] = __builtin_amdgcn_perm(pl[2 * i + 1], pl[2 * i], 0x07060302u);
+  }
+}
+
+MOE_DEV rf32x16_t mfma32_bf16(const u32x4_t &a, const u32x4_t &b, const rf32x16_t &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(rbf16x8_t, a), __builtin_bit_cast(rbf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
 
 __global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__restrict__ wr,
                                                                  const float *__restrict__ bias,
                                                                  const uint16_t *__restrict__ x, int32_t T,
                                                                  int32_t H, int32_t E, float *__restrict__ logits,
                                                                  uint16_t *__restrict__ x16) {
-  __shared__ float xs[2][kRmTok][kRmPad];
-  __shared__ float ws[2][kRmExp][kRmPad];
+  __shared__ rf32x16_t part[8][64];  // each wave's sums: [wave][lane]
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int n = lane & 15, q = lane >> 4;
-  const int et = wave & 3, kh = wave >> 2;  // expert tile, half of each step
+  const int c = lane & 31, g = lane >> 5;
+  const int et = wave & 1, kq = wave >> 1;  // expert tile, quarter of the reduction
   const int t0 = blockIdx.y * kRmTok;
-  const int e0 = blockIdx.x * kRmExp;
-  // staging: threads 0-255 one x piece (token tid / 8, 8 elements at
-  // 8 (tid % 8)); every thread two float4 of the router rows (expert
-  // tid / 8, k 8 (tid % 8) + 4 i)
-  const int xt = (tid & 255) >> 3, xk = (tid & 7) * 8;
-  const int we = tid >> 3, wk = (tid & 7) * 8;
-  const bool xthr = tid < 256;
-  const bool xv = xthr && t0 + xt < T, wv = e0 + we < E;
-  const uint4 *xp = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(xv ? t0 + xt : 0) * H + xk);
-  const float4 *wp = reinterpret_cast<const float4 *>(wr + static_cast<size_t>(wv ? e0 + we : 0) * H + wk);
-  uint4 xr;
-  float4 wrr[2];
-  auto load = [&](int s) {
-    xr = xv ? xp[s * (kRmK / 8)] : make_uint4(0, 0, 0, 0);
+  const int e0 = blockIdx.x * kRmExp + 32 * et;
+  const int t = t0 + c, e = e0 + c;
+  const bool tv = t < T, ev = e < E;
+  const int Hq = H >> 2;  // a multiple of 16
+  const int k0 = kq * Hq + 8 * g;
+  // rows past T or E read row 0: their sums land in outputs never stored
+  const uint4 *xp = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(tv ? t : 0) * H + k0);
+  const float4 *wp = reinterpret_cast<const float4 *>(wr + static_cast<size_t>(ev ? e : 0) * H + k0);
+  // the first expert tile's waves of the first column of blocks also write
+  // x in fp16, pair-permuted (the prefill expert GEMMs' operand form)
+  uint16_t *x16p = (x16 && blockIdx.x == 0 && et == 0 && tv) ? x16 + static_cast<size_t>(t) * H + k0 : nullptr;
+  rf32x16_t acc;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wrr[i] = wv ? wp[s * (kRmK / 4) + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const int steps = Hq / 16;
+  // two 16-wide steps per round, the next three rounds' operands in flight
+  uint4 xa[4][2];
+  float4 wa[4][2][2];
+  auto load = [&](int r, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int s = min(2 * r + u, steps - 1);  // clamped: past the end it re-reads the last step
+      xa[slot][u] = xp[2 * s];
+      wa[slot][u][0] = wp[4 * s];
+      wa[slot][u][1] = wp[4 * s + 1];
+    }
   };
-  // the first expert tile's blocks also write x in fp16, pair-permuted (the
-  // prefill expert GEMMs' operand form)
-  const bool x16w = x16 && blockIdx.x == 0 && xv;
-  auto store = [&](int buf, int s) {
-    if (x16w) {
-      const u32x4_t pp = pair_permute(xr);
-      *reinterpret_cast<uint4 *>(x16 + static_cast<size_t>(t0 + xt) * H + s * kRmK + xk) =
-          make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y), bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
-    }
-    if (xthr) {
-      const uint32_t d[4] = {xr.x, xr.y, xr.z, xr.w};
+  auto compute = [&](int r, int slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xs[buf][xt][xk + 2 * i] = bf16_lo(d[i]);
-        xs[buf][xt][xk + 2 * i + 1] = bf16_hi(d[i]);
+    for (int u = 0; u < 2; ++u) {
+      const uint4 xv = xa[slot][u];
+      const u32x4_t A = {xv.x, xv.y, xv.z, xv.w};
+      if (x16p) {
+        const u32x4_t pp = pair_permute(xv);
+        *reinterpret_cast<uint4 *>(x16p + 16 * (2 * r + u)) =
+            make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y), bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
       }
+      u32x4_t bh, bm, bl;
+      split3(wa[slot][u][0], wa[slot][u][1], bh, bm, bl);
+      acc = mfma32_bf16(A, bh, acc);
+      acc = mfma32_bf16(A, bm, acc);
+      acc = mfma32_bf16(A, bl, acc);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<float4 *>(&ws[buf][we][wk + 4 * i]) = wrr[i];
   };
-  rf32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  const int steps = H / kRmK;
-  load(0);
-  store(0, 0);
-  lds_barrier();
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < steps) load(s + 1);
-    // lane group q takes k = 16 r + 4 q + c in MFMA (r, c), for A and B
-    // alike; this wave's half of the step is r = 2 kh, 2 kh + 1
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r = 2 * kh + rr;
-      const float4 b4 = *reinterpret_cast<const float4 *>(&ws[buf][16 * et + n][16 * r + 4 * q]);
-      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const float4 a4 = *reinterpret_cast<const float4 *>(&xs[buf][16 * mt + n][16 * r + 4 * q]);
-        const float aa[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[c], bb[c], acc[mt], 0, 0, 0);
-      }
-    }
-    if (s + 1 < steps) store(buf ^ 1, s + 1);
-    lds_barrier();
+  // steps is a multiple of 8 (H % 512 == 0): whole groups of four rounds,
+  // no matrix-core instruction under a branch
+  const int rounds = steps >> 1;
+  load(0, 0);
+  load(1, 1);
+  load(2, 2);
+  for (int r = 0; r < rounds; r += 4) {
+    load(r + 3, 3);
+    compute(r, 0);
+    load(r + 4, 0);
+    compute(r + 1, 1);
+    load(r + 5, 1);
+    compute(r + 2, 2);
+    load(r + 6, 2);
+    compute(r + 3, 3);
   }
-  // the upper half's sums to LDS (the x buffers are free), added to the
-  // lower half's
-  rf32x4_t *part = reinterpret_cast<rf32x4_t *>(&xs[0][0][0]);
-  static_assert(4 * 2 * 64 * sizeof(rf32x4_t) <= sizeof(xs), "partial sums must fit the x buffers");
-  if (kh == 1) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) part[(et * 2 + mt) * 64 + lane] = acc[mt];
-  }
+  part[wave][lane] = acc;
   lds_barrier();
-  if (kh == 0) {
-    const int e = e0 + 16 * et + n;
-    if (e < E) {
-      const float b = bias ? bias[e] : 0.f;
+  // waves 0 and 1 add the four quarters of their expert tile in order
+  if (kq == 0 && ev) {
+    rf32x16_t v = part[et][lane];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const rf32x4_t v = acc[mt] + part[(et * 2 + mt) * 64 + lane];
+    for (int q = 1; q < 4; ++q) v += part[2 * q + et][lane];
+    const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * mt + 4 * q + i;
-          if (t < T) logits[static_cast<size_t>(t) * E + e] = v[i] + b;
-        }
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int tt = t0 + (j & 3) + 8 * (j >> 2) + 4 * g;
+      if (tt < T) logits[static_cast<size_t>(tt) * E + e] = v[j] + b;
     }
   }
 }
@@ -333,7 +352,7 @@ hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-static bool router_mfma_ok(const RouteArgs &a) { return a.T > kFusedTokens && a.H % kRmK == 0; }
+static bool router_mfma_ok(const RouteArgs &a) { return a.T > kFusedTokens && a.H % (8 * kRmK) == 0; }
 
 bool router_writes_x16(const RouteArgs &a) { return a.x16 != nullptr && router_mfma_ok(a); }
 
