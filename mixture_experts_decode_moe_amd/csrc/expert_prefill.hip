@@ -956,13 +956,20 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
       // A(0), B(0), A(1), B(1), A(2), B(2), B(3): the wait before the first
       // step leaves the requests after A(0) pending (B(0) 3, A(1) MS,
       // B(1) 3, A(2) MS, B(2) 3, B(3) 3)
+      // (the waits count requests in issue order: each group is pinned)
       load_a(0, 0, msc);
+      __builtin_amdgcn_sched_barrier(0);
       load_b(0, bw[0], bs[0]);
+      __builtin_amdgcn_sched_barrier(0);
       load_a(1, 1, msc);
+      __builtin_amdgcn_sched_barrier(0);
       load_b(1, bw[1], bs[1]);
+      __builtin_amdgcn_sched_barrier(0);
       load_a(2, 2, msc);
+      __builtin_amdgcn_sched_barrier(0);
       load_b(2, bw[2], bs[2]);
       load_b(3, bw[3], bs[3]);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(12 + 2 * MS));
       lds_barrier();
       auto step = [&](int s, auto slc) __attribute__((always_inline)) {
