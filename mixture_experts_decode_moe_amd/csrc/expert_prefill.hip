@@ -437,9 +437,10 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 // gate/up to down rounded once to fp16 (one plane), so the products
 // accumulate in the matrix core with no sum correction and no per-block
 // scaling on the vector unit.  Measured against the oracle: 3.6e-4 to
-// 4.3e-4 of max|ref| on prefill calls (T = 37 to 2048).  The vector unit
-// (the int4 dequantization, about 15 operations per 8 weights) is the limit
-// of the gate/up loop at 64 rows per item.
+// 4.3e-4 of max|ref| on prefill calls (T = 37 to 2048).  The int4
+// dequantization costs about 15 vector operations per 8 weights, as much
+// vector time as the 32x32 tiles' matrix time at 64 rows per item; the
+// 128-row gate/up items halve its share.
 //
 // The k loop is instantiated once per number of 32-row tiles that hold rows
 // (1, 2), chosen per item: no matrix-core instruction sits under a branch.

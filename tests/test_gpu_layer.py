@@ -62,6 +62,29 @@ def test_layer_parity_token_counts(mb, T):
     say(f"T={T}: rel err {err:.2e}, near ties {ties}")
 
 
+def test_prefill_repeated_calls_one_workspace(mb):
+    """Prefill calls share the workspace's item queues: every call must leave
+    them zero for the next one.  Three calls on one workspace, interleaved
+    with a call of another size, give the same bits each time and match the
+    oracle."""
+    import parity_util as pu
+    T = 200
+    shape = _shape(2, tokens=T, correlated_sigma=0.0, seed=91)
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    dl = mb.layer_to_device(layer)
+    ws = mb.make_workspace(dl, T)
+    say("prefill repeated calls T=200 on one workspace")
+    first = pu.run_layer(dl, pu.dev_u16(x), T, ws=ws)
+    pu.check_layer_against_oracle(layer, x, first)
+    for rep in range(3):
+        say(f"  call {rep + 2}")
+        pu.run_layer(dl, pu.dev_u16(x[:64]), 64, ws=ws, with_logits=False)  # another size in between
+        again = pu.run_layer(dl, pu.dev_u16(x), T, ws=ws, with_logits=False)
+        assert np.array_equal(again["ids"], first["ids"])
+        assert np.array_equal(again["y"], first["y"]), f"call {rep + 2}: bits differ from the first call"
+
+
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_small_batch_one_launch_down_combine(mb, cfg):
     """Batches of up to eight tokens run the down projection and the combine
