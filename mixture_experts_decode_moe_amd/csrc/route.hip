@@ -193,9 +193,13 @@ __global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__
   // rows past T or E read row 0: their sums land in outputs never stored
   const uint4 *xp = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(tv ? t : 0) * H + k0);
   const float4 *wp = reinterpret_cast<const float4 *>(wr + static_cast<size_t>(ev ? e : 0) * H + k0);
-  // the first expert tile's waves of the first column of blocks also write
-  // x in fp16, pair-permuted (the prefill expert GEMMs' operand form)
-  uint16_t *x16p = (x16 && blockIdx.x == 0 && et == 0 && tv) ? x16 + static_cast<size_t>(t) * H + k0 : nullptr;
+  // the first expert tile's waves also write x in fp16, pair-permuted (the
+  // prefill expert GEMMs' operand form): quarter kq of the token rows by the
+  // blocks of expert-tile column kq % gridDim.x, so that the writes are
+  // spread over the columns
+  uint16_t *x16p = (x16 && et == 0 && tv && static_cast<int>(blockIdx.x) == kq % static_cast<int>(gridDim.x))
+                       ? x16 + static_cast<size_t>(t) * H + k0
+                       : nullptr;
   rf32x16_t acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
