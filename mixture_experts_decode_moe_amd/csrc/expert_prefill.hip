@@ -794,14 +794,12 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
 constexpr int kG2Rows = 128;
 constexpr int kG2Bufs = 4;
 
-// The unit table of a layer call for the 128-row gate/up kernel, in the
-// order its items are taken: the shared expert first, then the routed
-// experts by the number of 32-row tiles of their first item (4 down to 1),
-// ties by expert index, so that the items left for the last round are the
-// smallest.  The routed units are the experts with rows (offsets[e + 1] >
-// offsets[e]): one read of the offsets, no dependent reads.  Needs
-// n_experts <= kGmMaxUnits - 1.
-MOE_DEV int gm_units_by_size(const FfnArgs &a, GmUnits &G, int *scratch, int (*cnt)[4]) {
+// The unit table of a layer call for the 128-row gate/up kernel: the shared
+// expert first, then the experts with rows (offsets[e + 1] > offsets[e]) in
+// index order, from one read of the offsets (no dependent reads of the
+// active list).  (Ordering the experts by tile count instead, largest first,
+// measured 6 us slower.)  Needs n_experts <= kGmMaxUnits - 1.
+MOE_DEV int gm_units_from_offsets(const FfnArgs &a, GmUnits &G, int *scratch, int (*cnt)[4]) {
   static_assert(kGmThreads >= kGmMaxUnits, "one unit per thread");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -812,8 +810,8 @@ MOE_DEV int gm_units_by_size(const FfnArgs &a, GmUnits &G, int *scratch, int (*c
     r0 = a.offsets[tid];
     n = a.offsets[tid + 1] - r0;
   }
-  // class 0: four tiles ... 3: one tile; 4: no rows
-  const int cls = (tid < E && n > 0) ? 4 - (min(n, kG2Rows) + 31) / 32 : 4;
+  // class 0: rows; 4: none (one class: index order)
+  const int cls = (tid < E && n > 0) ? 0 : 4;
   uint64_t mine = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -881,7 +879,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
   const bool up_lane = c >= 16;
   const int T = a.T;
   const int H = 128 * KS;
-  const int n_units = gm_units_by_size(a, units, scratch, class_cnt);
+  const int n_units = gm_units_from_offsets(a, units, scratch, class_cnt);
   const int col_tiles = a.F / 128;
   const int n_items = units.pre[n_units] * col_tiles;
   auto abuf = [&](int b, int r) __attribute__((always_inline)) {
