@@ -575,9 +575,7 @@ MOE_DEV PfUnit gm_unit(const GmUnits &G, int u) {
   return x;
 }
 
-// X16: the x rows come already in fp16, pair-permuted (a.x16), and are
-// staged as they are.
-template <int KS, bool X16>
+template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
   static_assert(KS % 4 == 0, "the k loop runs over groups of four steps");
   __shared__ uint4 as[2][kPfRows][17];  // x rows of the tile, pair-permuted fp16, one k-step
@@ -630,7 +628,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
     // past the tile's end read token 0's row: their products land in
     // accumulator rows that are never stored (every row of an MFMA result
     // depends on its own A row only), and the requests stay unconditional.
-    gchar_t *xg = uniform_gptr(X16 ? static_cast<const void *>(a.x16) : static_cast<const void *>(a.x));
+    gchar_t *xg = uniform_gptr(a.x);
     uint32_t xoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -651,13 +649,9 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
       // pair-permuted, in fp16
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        if constexpr (X16) {
-          as[buf][(tid >> 4) + 32 * i][pc] = v[i];
-        } else {
-          const u32x4_t pp = pair_permute(v[i]);
-          as[buf][(tid >> 4) + 32 * i][pc] = make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y),
-                                                        bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
-        }
+        const u32x4_t pp = pair_permute(v[i]);
+        as[buf][(tid >> 4) + 32 * i][pc] = make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y),
+                                                      bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
       }
     };
     auto load_b = [&](int s, uint4(&w)[2], u32x2_t &sc) {
@@ -1288,9 +1282,8 @@ hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
     return launch_kernel(gateup_gemm128_kernel<16>, dim3(cus), dim3(kGmThreads), 0, s, a);
   }
   if (gm_pair_ok(a)) {
-    const dim3 grid(gm_grid(pf_tiles_upper(a) * (a.F / 128), 1));
-    if (a.x16) return launch_kernel(gateup_gemm_kernel<16, true>, grid, dim3(kGmThreads), 0, s, a);
-    return launch_kernel(gateup_gemm_kernel<16, false>, grid, dim3(kGmThreads), 0, s, a);
+    return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128), 1)), dim3(kGmThreads), 0,
+                         s, a);
   }
   return launch_kernel(gateup_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.F / kPfCols))), dim3(kPfThreads), 0,
                        s, a);
