@@ -450,15 +450,10 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 
 typedef __attribute__((address_space(1))) const u32x2_t gu2_t;
 
-
-// An empty volatile statement that takes the value in registers: volatile
-// statements keep their order, so each scaled accumulation happens where it
-// is written, instead of every product of a step being computed first and
-// held (which spills).
-MOE_DEV void pin(f32x4_t &v) { __asm__ volatile("" : "+v"(v)); }
-// The same for a 32-bit offset: the addresses derived from it are then
-// computed where they are used rather than hoisted out of the k loop and
-// kept live (which spills, and a spill reload waits for every load).
+// An empty volatile statement on a 32-bit offset in registers: the
+// addresses derived from it are then computed where they are used rather
+// than hoisted out of the k loop and kept live (which spills, and a spill
+// reload waits for every load).
 MOE_DEV void pin_u32(uint32_t &v) { __asm__ volatile("" : "+v"(v)); }
 
 template <int V>
@@ -786,7 +781,6 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
 // stored at slot piece ^ (row & 15), so that the MFMA operand reads, 16
 // rows at one piece, meet every LDS bank once.
 constexpr int kG2Rows = 128;
-constexpr int kG2Bufs = 4;
 
 // The unit table of a layer call for the 128-row gate/up kernel: the shared
 // expert first, then the experts with rows (offsets[e + 1] > offsets[e]) in

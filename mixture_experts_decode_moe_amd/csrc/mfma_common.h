@@ -13,7 +13,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kMagicPair = 0x43004300u;     // bf16 pair (128, 128)
 constexpr uint32_t kMinus136Pair = 0xC308C308u;  // bf16 pair (-136, -136)
 constexpr int kGuMaxWaves = 16;  // gate/up: waves splitting the hidden dimension
 constexpr int kDnMaxWaves = 8;   // down: waves splitting the SwiGLU dimension
@@ -26,11 +25,6 @@ MOE_DEV f32x4_t mfma_bf16(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2v_t __attribute__((ext_vector_type(2)));
-
-MOE_DEV f32x4_t mfma_f16(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                0, 0, 0);
-}
 
 // A pair of bf16 (one word) -> the same pair in fp16: exact for magnitudes
 // in fp16's normal range [2^-14, 65504], rounded to nearest below it.
