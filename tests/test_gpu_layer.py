@@ -62,6 +62,24 @@ def test_layer_parity_token_counts(mb, T):
     say(f"T={T}: rel err {err:.2e}, near ties {ties}")
 
 
+@pytest.mark.parametrize("fmt,ffn,shared_ffn", [(synth.FMT_INT4_B32, 512, 0), (synth.FMT_INT4_B32, 512, 512),
+                                                 (synth.FMT_INT8_ROW, 256, 256)])
+def test_layer_parity_other_shapes_many_tokens(mb, fmt, ffn, shared_ffn):
+    """Batches above the decode size on a layer shape the pipelined prefill
+    GEMMs do not take (H = 1024, 64 experts, top-4): int4 runs the generic
+    prefill kernels, int8 the vector-unit item kernels."""
+    import parity_util as pu
+    T = 40
+    shape = _shape(0, tokens=T, fmt=fmt, ffn=ffn, shared_ffn=shared_ffn, seed=130 + fmt + shared_ffn)
+    say(f"layer parity H=1024 F={ffn} fmt {fmt} shared {shared_ffn} T={T}")
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    dl = mb.layer_to_device(layer)
+    gpu = pu.run_layer(dl, pu.dev_u16(x), T)
+    err, ties = pu.check_layer_against_oracle(layer, x, gpu)
+    say(f"  rel err {err:.2e}, near ties {ties}")
+
+
 def test_prefill_repeated_calls_one_workspace(mb):
     """Prefill calls share the workspace's item queues: every call must leave
     them zero for the next one.  Three calls on one workspace, interleaved
