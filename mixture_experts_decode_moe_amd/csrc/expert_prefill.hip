@@ -850,11 +850,13 @@ MOE_DEV int gm_units_from_offsets(const FfnArgs &a, GmUnits &G, int *scratch, in
 
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a) {
-  static_assert(KS % 4 == 0, "the k loop runs over groups of four steps");
-  // the A buffers, [kG2Rows][16] pieces each: separate arrays, so that the
-  // compiler sees that the LDS reads of a step do not touch the buffer its
-  // direct loads are filling
-  __shared__ uint4 g2_a0[kG2Rows * 16], g2_a1[kG2Rows * 16], g2_a2[kG2Rows * 16], g2_a3[kG2Rows * 16];
+  static_assert(KS == 16, "the k loop is unrolled over sixteen steps");
+  // three A buffers ([kG2Rows][16] pieces) and three weight buffers (the
+  // item's 256 weight rows x four 16-byte blocks), two steps ahead: separate
+  // arrays, so that the compiler sees that the LDS reads of a step do not
+  // touch the buffers its direct loads are filling
+  __shared__ uint4 g2_a0[kG2Rows * 16], g2_a1[kG2Rows * 16], g2_a2[kG2Rows * 16];
+  __shared__ uint4 g2_b0[256 * 4], g2_b1[256 * 4], g2_b2[256 * 4];
   __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
   __shared__ int class_cnt[kGmThreads / 64][4];
@@ -871,8 +873,9 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
   const int col_tiles = a.F / 128;
   const int n_items = units.pre[n_units] * col_tiles;
   auto abuf = [&](int b, int r) __attribute__((always_inline)) {
-    return (b == 0 ? g2_a0 : b == 1 ? g2_a1 : b == 2 ? g2_a2 : g2_a3) + r * 16;
+    return (b == 0 ? g2_a0 : b == 1 ? g2_a1 : g2_a2) + r * 16;
   };
+  auto bbuf = [&](int b) __attribute__((always_inline)) { return b == 0 ? g2_b0 : b == 1 ? g2_b1 : g2_b2; };
 
   for (;;) {
     if (tid == 0) next_item = static_cast<int>(atomicAdd(&a.queue[0], 1u));
@@ -887,17 +890,30 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
     const int rows = min(kG2Rows, un.n - m0);
     const bool shared = un.e < 0;
     const int F = shared ? a.Fs : a.F;
-    // this lane's weight row: the gate (lanes c < 16) or up (c >= 16) row of
-    // SwiGLU column col
-    const int col = ct * 128 + 16 * wave + (c & 15);
     gchar_t *gq = uniform_gptr(shared ? a.sgq : a.gq);
     gchar_t *uq = uniform_gptr(shared ? a.suq : a.uq);
     gchar_t *gsc = uniform_gptr(shared ? a.sgs : a.gs);
     gchar_t *usc = uniform_gptr(shared ? a.sus : a.us);
-    gchar_t *wq = up_lane ? uq : gq;
+    const uint32_t ebase = static_cast<uint32_t>((shared ? 0 : un.e) * F + ct * 128);
+    // The weight tile of a step in LDS: row R (0-127 the gate rows of the
+    // item's SwiGLU columns, 128-255 their up rows) holds its four blocks at
+    // slots p ^ ((R >> 2) & 3), so that the operand reads (16 rows, one word
+    // each) meet every bank once.  Direct loads: instruction k of wave w
+    // fills rows 32 w + 16 k .. + 15 (waves 0-3 gate, 4-7 up), lane l row
+    // 32 w + 16 k + l / 4, slot l % 4.
+    gchar_t *bq = wave < 4 ? gq : uq;
+    uint32_t boff[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int R = 32 * wave + 16 * k + (lane >> 2);
+      const int p = (lane & 3) ^ ((R >> 2) & 3);
+      boff[k] = (ebase + static_cast<uint32_t>(R & 127)) * (nblk * 16) + 16 * p;
+    }
+    // this lane's operand row (the gate (c < 16) or up (c >= 16) row of
+    // SwiGLU column 16 wave + c % 16) and its block scales (registers)
+    const int Rm = (up_lane ? 128 : 0) + 16 * wave + (c & 15);
     gchar_t *wsc = up_lane ? usc : gsc;
-    const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * F + col);
-    uint32_t woff = row0 * (nblk * 16) + 16 * h, soff = row0 * (nblk * 2);
+    uint32_t soff = (ebase + static_cast<uint32_t>(16 * wave + (c & 15))) * (nblk * 2);
 
     // A: instruction i of this wave fills rows 4 (wave + 8 i) .. + 3 of a
     // buffer, lane l row 4 (wave + 8 i) + l / 16, slot l % 16 (piece
@@ -916,102 +932,92 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
       }
       xoff[i] = static_cast<uint32_t>(t) * (2 * H) + 16 * ((lane & 15) ^ (r & 15));
     }
-    // only the 32-row tiles that hold rows: instruction i covers rows of
-    // tiles < i + 1, so an item of MS tiles issues its first MS
-    auto load_a = [&](int s, int b, auto msc) __attribute__((always_inline)) {
+    // the requests of step s into buffer s % 3: its A tiles (MS), its weight
+    // chunks (2 direct loads), its block scales (1 register load)
+    u32x2_t bs[3];
+    auto load_step = [&](int s, auto msc) __attribute__((always_inline)) {
       constexpr int MS = decltype(msc)::value;
+      const int b = s % 3;
 #pragma unroll
       for (int i = 0; i < MS; ++i)
         __builtin_amdgcn_global_load_lds(xg + (xoff[i] + 256u * s),
                                          (__attribute__((address_space(3))) void *)(abuf(b, 4 * (wave + 8 * i))), 16,
                                          0, 0);
-    };
-    auto load_b = [&](int s, uint4(&w)[2], u32x2_t &sc) __attribute__((always_inline)) {
-      // blocks 4 s + 2 i + h; the four block scales of the step
 #pragma unroll
-      for (int i = 0; i < 2; ++i) w[i] = load16_g(wq + (woff + 64u * s + 32u * i));
-      sc = *reinterpret_cast<gu2_t *>(wsc + (soff + 8u * s));
+      for (int k = 0; k < 2; ++k)
+        __builtin_amdgcn_global_load_lds(bq + (boff[k] + 64u * s),
+                                         (__attribute__((address_space(3))) void *)(bbuf(b) + (32 * wave + 16 * k) * 4),
+                                         16, 0, 0);
+      bs[b] = *reinterpret_cast<gu2_t *>(wsc + (soff + 8u * s));
     };
 
     f32x16_t acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[mt] = zero16();
-    uint4 bw[4][2];  // weight chunks, slot s & 3
-    u32x2_t bs[4];   // their block scales
     with_msub((rows + 31) >> 5, [&](auto msc) __attribute__((always_inline)) {
       constexpr int MS = decltype(msc)::value;
-      // A(0), B(0), A(1), B(1), A(2), B(2), B(3): the wait before the first
-      // step leaves the requests after A(0) pending (B(0) 3, A(1) MS,
-      // B(1) 3, A(2) MS, B(2) 3, B(3) 3)
-      // (the waits count requests in issue order: each group is pinned)
-      load_a(0, 0, msc);
+      constexpr int G = MS + 3;  // requests a step
+      // steps 0 and 1; the wait leaves step 1's requests pending (the waits
+      // count requests in issue order, so each group is pinned)
+      load_step(0, msc);
       __builtin_amdgcn_sched_barrier(0);
-      load_b(0, bw[0], bs[0]);
+      load_step(1, msc);
       __builtin_amdgcn_sched_barrier(0);
-      load_a(1, 1, msc);
-      __builtin_amdgcn_sched_barrier(0);
-      load_b(1, bw[1], bs[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      load_a(2, 2, msc);
-      __builtin_amdgcn_sched_barrier(0);
-      load_b(2, bw[2], bs[2]);
-      load_b(3, bw[3], bs[3]);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(12 + 2 * MS));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
       lds_barrier();
-      auto step = [&](int s, auto slc) __attribute__((always_inline)) {
-        constexpr int sl = decltype(slc)::value;
-        pin_u32(woff);
+      auto step = [&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int b = s % 3;
         pin_u32(soff);
 #pragma unroll
         for (int i = 0; i < 4; ++i) pin_u32(xoff[i]);
-        // A three steps ahead (clamped: past the end it re-reads the last
-        // step into a buffer no later step reads)
-        load_a(min(s + 3, KS - 1), (sl + 3) & 3, msc);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) half_exchange(bw[sl][i]);
-        // k 16 t8 .. 16 t8 + 15 of the step: block 2 i + (t >> 1), t8 = 4 i + t;
-        // the operand of t8 + 1 is dequantized before the products of t8
-        // are issued, so the vector unit has work while they run
-        auto dq = [&](int t8) __attribute__((always_inline)) {
-          const int i = t8 >> 2, t = t8 & 3;
-          return dequant_f16_pairs(word(bw[sl][i], t), bs[sl].x, bs[sl].y, 2 * i + (t >> 1));
-        };
-        u32x4_t Bn = dq(0);
+        for (int k = 0; k < 2; ++k) pin_u32(boff[k]);
+        // two steps ahead (clamped: past the end it re-reads the last step
+        // into a buffer no later step reads)
+        load_step(s + 2 < KS ? s + 2 : KS - 1, msc);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t *brow = reinterpret_cast<const uint32_t *>(bbuf(b) + Rm * 4);
+        const int rsw = (Rm >> 2) & 3;
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) {
-          const u32x4_t B = Bn;
-          if (t8 < 7) Bn = dq(t8 + 1);
+          // k 16 t8 .. 16 t8 + 15 of the step: block t8 / 2, word 2 (t8 % 2) + h
+          const int p = t8 >> 1;
+          const uint32_t w = brow[4 * (p ^ rsw) + 2 * (t8 & 1) + h];
+          const u32x4_t B = dequant_f16_pairs(w, bs[b].x, bs[b].y, p);
           const int slot = (2 * t8 + h) ^ (c & 15);
           uint4 Av[MS];
 #pragma unroll
-          for (int mt = 0; mt < MS; ++mt) Av[mt] = abuf(sl, 32 * mt + c)[slot];
+          for (int mt = 0; mt < MS; ++mt) Av[mt] = abuf(b, 32 * mt + c)[slot];
 #pragma unroll
           for (int mt = 0; mt < MS; ++mt) {
             const u32x4_t A = {Av[mt].x, Av[mt].y, Av[mt].z, Av[mt].w};
             acc[mt] = mfma32_f16(A, B, acc[mt]);
           }
         }
-        load_b(min(s + 4, KS - 1), bw[sl], bs[sl]);
-        __builtin_amdgcn_sched_barrier(0);
-        // A(s + 1) has landed once at most the requests issued after it are
-        // pending: B(s + 2), A(s + 2), B(s + 3), A(s + 3), B(s + 4)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(9 + 2 * MS));
+        // step s + 1 has landed once at most step s + 2's requests are pending
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
         lds_barrier();
       };
-      // fully unrolled: no loop back-edge, so the compiler can tell which
-      // direct loads each step's LDS reads wait for
-#pragma unroll
-      for (int s = 0; s < KS; s += 4) {
-        step(s, IntC<0>{});
-        step(s + 1, IntC<1>{});
-        step(s + 2, IntC<2>{});
-        step(s + 3, IntC<3>{});
-      }
+      step(IntC<0>{});
+      step(IntC<1>{});
+      step(IntC<2>{});
+      step(IntC<3>{});
+      step(IntC<4>{});
+      step(IntC<5>{});
+      step(IntC<6>{});
+      step(IntC<7>{});
+      step(IntC<8>{});
+      step(IntC<9>{});
+      step(IntC<10>{});
+      step(IntC<11>{});
+      step(IntC<12>{});
+      step(IntC<13>{});
+      step(IntC<14>{});
+      step(IntC<15>{});
     });
-    // the clamped A requests still in flight write into the buffers: let
-    // them land before the staging below reuses the memory
+    // the clamped requests still in flight write into the buffers: let them
+    // land before the staging below reuses the memory
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
     // SwiGLU into LDS, rounded once to fp16 (as in gateup_gemm_kernel):
