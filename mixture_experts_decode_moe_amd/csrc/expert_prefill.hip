@@ -776,10 +776,13 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
 // carries up to four 32-row tiles of matrix work per dequantized chunk.
 // Blocks take items from the queue (the shared expert's, the largest,
 // first), so that they finish together although items differ in size.
-// The x rows go from global memory straight into LDS (no registers), three
-// steps ahead, into four buffers; each row's sixteen 16-byte pieces are
-// stored at slot piece ^ (row & 15), so that the MFMA operand reads, 16
-// rows at one piece, meet every LDS bank once.
+// The x rows and the weight chunks go from global memory straight into LDS
+// (no registers), two steps ahead, into three buffers each: each x row's
+// sixteen 16-byte pieces are stored at slot piece ^ (row & 15), each weight
+// row's four blocks at slot block ^ ((row >> 2) & 3), so that the MFMA
+// operand reads (16 rows at one piece, or one word of 16 rows) meet every
+// LDS bank once.  The weight loads cover 64 contiguous bytes of 16 rows
+// each, half the cache lines per request of per-lane register loads.
 constexpr int kG2Rows = 128;
 
 // The unit table of a layer call for the 128-row gate/up kernel: the shared
