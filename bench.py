@@ -161,7 +161,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (expert-parallel sharding is a "
+        print("bench.py measures one GPU: the library runs on one GPU (expert-parallel sharding is a "
               "design note only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
