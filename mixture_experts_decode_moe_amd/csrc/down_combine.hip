@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(kDcMaxThreads) down_combine_kernel(DownCombine
     }
   };
 
-  // --- Round 1: the unit table (for the weight addresses), the slots, the
+  // --- First batch of requests: the unit table (for the weight addresses), the slots, the
   // rows' routing weights and every SwiGLU row of the call.  The weights
   // are requested as soon as the table has arrived, before the staged rows
   // are stored, so both travel together.
