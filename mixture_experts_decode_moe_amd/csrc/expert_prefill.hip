@@ -419,8 +419,8 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 // The k loop runs over groups of steps whose register slots and LDS buffers
 // have constant indices, with no copies between iterations (a register ring
 // copied across a loop back-edge makes the compiler wait for every load).
-// Down (F = 512: four steps) keeps the weights of the next two steps and the
-// A rows of the next one in flight, two blocks per compute unit.  Gate/up
+// Down (F = 512: four steps) stages both operands of the next step in LDS,
+// two blocks per compute unit.  Gate/up
 // (H = 2048: sixteen steps) runs one block per compute unit with 256
 // registers a lane and keeps the weights of the next four steps and the A
 // rows of the next two in flight.  Items are 64 rows by 128 SwiGLU columns
@@ -1080,14 +1080,22 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
   }
 }
 
+// ------------------------------------------------ down, operands through LDS
+// The down GEMM with both operands staged by direct loads, one step ahead,
+// in two buffers each (LDS 64 KB a block: two blocks a compute unit): the
+// act rows (64 rows x 256 bytes a step, pieces swizzled by row as in
+// gateup_gemm128_kernel) and the weight chunks of the item's 256 output
+// columns (16 rows of 64 contiguous bytes a request, blocks swizzled by
+// row); the block scales are register loads.  The products leave the
+// accumulators directly (32 lanes: 32 consecutive columns of one row).
 template <int KS>
 __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
-  static_assert(KS % 2 == 0, "the k loop runs over pairs of steps");
-  // act rows in fp16, one k-step, in [buffer][0]; the whole array holds the
-  // output tile in the epilogue
-  __shared__ uint4 as[2][2][kPfRows][17];
+  static_assert(KS == 4, "four k-steps");
+  __shared__ uint4 dn_a0[kPfRows * 16], dn_a1[kPfRows * 16];
+  __shared__ uint4 dn_b0[256 * 4], dn_b1[256 * 4];
   __shared__ GmUnits units;
   __shared__ int scratch[kGmThreads / 64];
+  __shared__ float wrow[kPfRows];
   constexpr int nblk = 4 * KS;  // 32-element blocks per weight row
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -1097,12 +1105,12 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   const int n_units = gm_units(a, units, scratch);
   const int col_tiles = H / 256;
   const int n_items = units.pre[n_units] * col_tiles;
-  const int pc = tid & 15;
+  auto abuf = [&](int b) __attribute__((always_inline)) { return b == 0 ? dn_a0 : dn_a1; };
+  auto bbuf = [&](int b) __attribute__((always_inline)) { return b == 0 ? dn_b0 : dn_b1; };
 
   // XCD-aware order: the blocks of one XCD (block b runs on XCD b mod 8)
   // take a contiguous run of items per round, so the column tiles of a row
-  // tile, and consecutive row tiles of a unit, share that XCD's L2 for
-  // their A rows and weights
+  // tile share that XCD's L2 for their act rows
   const int per_xcd = gridDim.x >> 3;
   const int my_off = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   for (int round = 0; round < n_items; round += gridDim.x) {
@@ -1115,117 +1123,110 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
     const int m0 = (j - units.pre[u]) * kPfRows;
     const int rows = min(kPfRows, un.n - m0);
     const bool shared = un.e < 0;
-    // output column (weight row) of this lane: hbase; 32-bit offsets from
-    // block-uniform bases
-    const int hbase = ct * 256 + 32 * wave + c;
-    const uint32_t row0 = static_cast<uint32_t>((shared ? 0 : un.e) * H + hbase);
+    const int F = shared ? a.Fs : a.F;  // == 128 KS
     gchar_t *dq = uniform_gptr(shared ? a.sdq : a.dq);
     gchar_t *dsc = uniform_gptr(shared ? a.sds : a.ds);
-    uint32_t woff = row0 * (nblk * 16) + 16 * h, soff = row0 * (nblk * 2);
-
-    // A staging: thread t owns piece t % 16 of rows t / 16 + 32 i (byte
-    // offsets of the rows inside the act buffer, which holds one fp16 plane
-    // per row here); rows past the tile's end read its first row (results
-    // never stored)
+    const uint32_t ebase = static_cast<uint32_t>((shared ? 0 : un.e) * H + ct * 256);
+    // weights: instruction k of wave w fills tile rows 32 w + 16 k .. + 15,
+    // lane l row 32 w + 16 k + l / 4, slot l % 4 (block (l % 4) ^ ((row >> 2) & 3))
+    uint32_t boff[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int R = 32 * wave + 16 * k + (lane >> 2);
+      boff[k] = (ebase + static_cast<uint32_t>(R)) * (nblk * 16) + 16 * ((lane & 3) ^ ((R >> 2) & 3));
+    }
+    // act: instruction i of wave w fills rows 4 (w + 8 i) .. + 3, lane l row
+    // 4 (w + 8 i) + l / 16, slot l % 16 (piece (l % 16) ^ (row % 16)); the
+    // rows are consecutive in the act buffer, 4 bytes a slot element (the
+    // fp16 plane in the first half); rows past the tile's end read its first
     gchar_t *ag = uniform_gptr(a.act);
+    const uint32_t abase = shared ? static_cast<uint32_t>(a.n_rows * a.F + m0 * a.Fs)
+                                  : static_cast<uint32_t>((un.r0 + m0) * a.F);
     uint32_t aoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r = (tid >> 4) + 32 * i;
-      const int rr = m0 + (r < rows ? r : 0);
-      const uint32_t off = shared ? static_cast<uint32_t>(a.n_rows * a.F + rr * a.Fs)
-                                  : static_cast<uint32_t>((un.r0 + rr) * a.F);
-      aoff[i] = 4 * off + 16 * pc;  // the row's slot holds 4 bytes per element; its first half is used
+      const int r = 4 * (wave + 8 * i) + (lane >> 4);
+      aoff[i] = 4 * (abase + static_cast<uint32_t>((r < rows ? r : 0) * F)) + 16 * ((lane & 15) ^ (r & 15));
     }
-    auto load_a = [&](int s, uint4(&v)[2]) {
+    // this lane's operand row (output column hcol) and its block scales
+    const int Rm = 32 * wave + c;
+    const int hcol = ct * 256 + Rm;
+    const uint32_t soff = (ebase + static_cast<uint32_t>(Rm)) * (nblk * 2);
+    if (tid < kPfRows) {
+      const int r = tid < rows ? tid : 0;
+      wrow[tid] = shared || !a.row_w ? 1.f : a.row_w[un.r0 + m0 + r];
+    }
+    u32x2_t bs[2];
+    auto load_step = [&](int s) __attribute__((always_inline)) {
+      const int b = s & 1;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) v[i] = load16_g(ag + (aoff[i] + 256u * s));
-    };
-    auto store_a = [&](int buf, const uint4(&v)[2]) {
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(ag + (aoff[i] + 256u * s),
+                                         (__attribute__((address_space(3))) void *)(abuf(b) + 4 * (wave + 8 * i) * 16),
+                                         16, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) as[buf][0][(tid >> 4) + 32 * i][pc] = v[i];
-    };
-    auto load_b = [&](int s, uint4(&w)[2], u32x2_t &sc) {
-      // blocks 4 s + 2 i + h; the four block scales of the step
-#pragma unroll
-      for (int i = 0; i < 2; ++i) w[i] = load16_g(dq + (woff + 64u * s + 32u * i));
-      sc = *reinterpret_cast<gu2_t *>(dsc + (soff + 8u * s));
+      for (int k = 0; k < 2; ++k)
+        __builtin_amdgcn_global_load_lds(dq + (boff[k] + 64u * s),
+                                         (__attribute__((address_space(3))) void *)(bbuf(b) + (32 * wave + 16 * k) * 4),
+                                         16, 0, 0);
+      bs[b] = *reinterpret_cast<gu2_t *>(dsc + (soff + 8u * s));
     };
 
     f32x16_t acc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) acc[mt] = zero16();
-    uint4 av[2];
-    uint4 bw[2][2];
-    u32x2_t bs[2];
-    // B(0), A(0), B(1): once A(0) has arrived, B(0) has too (the counter of
-    // outstanding loads drains in order) and only B(1) is pending, as at the
-    // top of every later pair of steps
-    load_b(0, bw[0], bs[0]);
-    load_a(0, av);
-    load_b(1, bw[1], bs[1]);
-    store_a(0, av);
+    load_step(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
     with_msub2((rows + 31) >> 5, [&](auto msc) __attribute__((always_inline)) {
       constexpr int MS = decltype(msc)::value;
-      auto step = [&](int s, auto slc) __attribute__((always_inline)) {
-        constexpr int sl = decltype(slc)::value;
-        pin_u32(woff);
-        pin_u32(soff);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) pin_u32(aoff[i]);
-        load_a(min(s + 1, KS - 1), av);  // A(s) is in LDS already; clamped
-#pragma unroll
-        for (int i = 0; i < 2; ++i) half_exchange(bw[sl][i]);
+      auto step = [&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int b = s & 1;
+        // one step ahead
+        if constexpr (s + 1 < KS) load_step(s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t *brow = reinterpret_cast<const uint32_t *>(bbuf(b) + Rm * 4);
+        const int rsw = (Rm >> 2) & 3;
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) {
-          // k 16 t8 .. 16 t8 + 15 of the step: block 2 i + (t >> 1)
-          const int i = t8 >> 2, t = t8 & 3;
-          const u32x4_t B =
-              dequant_f16_pairs(word(bw[sl][i], t), bs[sl].x, bs[sl].y, 2 * i + (t >> 1));
+          const int p = t8 >> 1;
+          const uint32_t w = brow[4 * (p ^ rsw) + 2 * (t8 & 1) + h];
+          const u32x4_t B = dequant_f16_pairs(w, bs[b].x, bs[b].y, p);
+          const int slot = (2 * t8 + h) ^ (c & 15);
+          uint4 Av[MS];
+#pragma unroll
+          for (int mt = 0; mt < MS; ++mt) Av[mt] = abuf(b)[(32 * mt + c) * 16 + slot];
 #pragma unroll
           for (int mt = 0; mt < MS; ++mt) {
-            const uint4 v = as[sl][0][32 * mt + c][2 * t8 + h];
-            const u32x4_t A = {v.x, v.y, v.z, v.w};
+            const u32x4_t A = {Av[mt].x, Av[mt].y, Av[mt].z, Av[mt].w};
             acc[mt] = mfma32_f16(A, B, acc[mt]);
           }
         }
-        load_b(min(s + 2, KS - 1), bw[sl], bs[sl]);
-        __builtin_amdgcn_sched_barrier(0);
-        store_a(sl ^ 1, av);  // unconditional: no branch inside the step
+        // step s + 1 has landed once nothing is pending; after the last
+        // step the barrier frees the tiles for the next item
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         lds_barrier();
       };
-      for (int s = 0; s < KS; s += 2) {
-        step(s, IntC<0>{});
-        step(s + 1, IntC<1>{});
-      }
+      step(IntC<0>{});
+      step(IntC<1>{});
+      step(IntC<2>{});
+      step(IntC<3>{});
     });
-    // the tile into LDS (the A buffers are free now), rows of 256 + 4 floats,
-    // then 16-byte stores of whole row segments with the row's weight
-    float *st = reinterpret_cast<float *>(&as[0][0][0][0]);
-    constexpr int kStRow = 260;
-    static_assert(kPfRows * kStRow * 4 <= sizeof(as), "output staging must fit the A buffers");
+    // rows of the tile times their routing weights, straight to the output
+    // rows: register jj of lane (c, h) is row 32 mt + (jj & 3) + 8 (jj >> 2) + 4 h
+    {
+      const int orow0 = shared ? a.n_rows + m0 : un.r0 + m0;
+      float *op = a.rows_out + static_cast<size_t>(orow0 + 4 * h) * H + hcol;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj)
-        st[(32 * mt + (jj & 3) + 8 * (jj >> 2) + 4 * h) * kStRow + 32 * wave + c] = acc[mt][jj];
-    lds_barrier();
-#pragma unroll
-    for (int k2 = 0; k2 < 8; ++k2) {
-      const int idx = tid + kGmThreads * k2;
-      const int r = idx >> 6, pcs = idx & 63;
-      if (r < rows) {
-        const float4 v = *reinterpret_cast<const float4 *>(st + r * kStRow + 4 * pcs);
-        const int rr = m0 + r;
-        const int row = un.r0 + rr;
-        const float wgt = shared || !a.row_w ? 1.f : a.row_w[row];
-        const size_t orow = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(row);
-        *reinterpret_cast<float4 *>(a.rows_out + orow * H + ct * 256 + 4 * pcs) =
-            make_float4(v.x * wgt, v.y * wgt, v.z * wgt, v.w * wgt);
-      }
+        for (int jj = 0; jj < 16; ++jj) {
+          const int R = 32 * mt + (jj & 3) + 8 * (jj >> 2);
+          if (R + 4 * h < rows) op[R * H] = acc[mt][jj] * wrow[R + 4 * h];
+        }
     }
-    lds_barrier();
+    lds_barrier();  // the next item's tiles and row weights reuse the memory
   }
 }
 
