@@ -114,15 +114,23 @@ size_t moe_workspace_bytes(const moe_layer *L, int32_t max_tokens);
  * the kernels keep zero between calls).  Enqueued on `stream`. */
 int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of workspace moe_route needs for T tokens when it is not given a
+ * logits buffer (host, pure; 0 on invalid arguments). */
+size_t moe_route_workspace_bytes(const moe_layer *L, int32_t T);
+
 /* Router: logits[t][e] = sum_h Wr[e][h] * x[t][h] (+ bias[e]) in float32;
  * topk_ids[t][k] = the K largest logits in descending order, equal logits
  * going to the lower expert index (the pages' rule that the first of equal
  * largest values wins, "Models and backends", What was tuned);
  * topk_w[t][k] = routing weights per L->renorm.
- * x_bf16 [T][H] bfloat16 bits; topk_ids int32 [T][K]; topk_w float [T][K];
- * logits float [T][E] (required; receives the router logits). */
+ * x_bf16 [T][H] bfloat16 bits (16-byte aligned); topk_ids int32 [T][K];
+ * topk_w float [T][K]; logits float [T][E], or NULL when the caller does not
+ * want them: they then pass through `ws`, which must hold
+ * moe_route_workspace_bytes(L, T) bytes (ws is unused when logits is given
+ * and may be NULL).  MOE_ERR_WORKSPACE if logits is NULL and ws is missing
+ * or too small. */
 int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *topk_ids, float *topk_w,
-              float *logits, void *stream);
+              float *logits, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes moe_permute needs for T tokens, K slots, E experts. */
 size_t moe_permute_workspace_bytes(int32_t T, int32_t K, int32_t E);
@@ -157,33 +165,76 @@ int moe_expert_ffn(const moe_experts *W, int32_t hidden, const uint16_t *x_bf16,
                    const int32_t *offsets, const int32_t *active, const int32_t *n_active, const int32_t *row_tok,
                    const float *row_w, float *rows_out, void *ws, size_t ws_bytes, void *stream);
 
-/* Combine ("the MoE end"): y[t][h] = sum_{k<K} rows_out[inv_pos[t][k]][h]
- * (k in order) + shared_out[t][h]; rows with inv_pos < 0 are skipped.
- * shared_out float [T][H] or NULL; y float [T][H]; res (host) or NULL: the
- * residual epilogue above. */
+/* Combine, the MoE end of the layer: the weighted expert outputs plus the
+ * shared expert's, summed per token ("Qwen3.6-35B-A3B: pictures, several
+ * requests at once and speed", Speed (0.1.45): the MoE end in one launch of
+ * 1024 threads, and add+norm of the residual in one launch; "Models and
+ * backends", What was tuned: one launch adds up a call's experts).
+ * y[t][h] = sum_{k<K} rows_out[inv_pos[t][k]][h] (k in order, each row
+ * already scaled by its routing weight) + shared_out[t][h]; slots with
+ * inv_pos < 0 are skipped.  rows_out float [*][H] (16-byte aligned);
+ * inv_pos int32 [T][K]; shared_out float [T][H] or NULL; y float [T][H];
+ * res (host) or NULL: the residual epilogue above.  H a multiple of 256 up
+ * to 8192, K <= 64. */
 int moe_combine(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_t K, int32_t H,
                 const float *shared_out, float *y, const moe_residual *res, void *stream);
 
-/* The whole layer: route, permute, routed experts, shared expert, combine.
- * y float [T][H]; res (host) or NULL: residual epilogue; topk_ids [T][K] /
- * topk_w [T][K] or NULL (copies of the routing used).  ws: at least
- * moe_workspace_bytes(L, T) bytes, prepared once by moe_workspace_init.
- * T = 0 is a no-op. */
+/* Stages of a layer call, for per-call profiling events. */
+enum { MOE_STAGE_NONE = 0, MOE_STAGE_ROUTE = 1, MOE_STAGE_PERMUTE = 2, MOE_STAGE_GATEUP = 3,
+       MOE_STAGE_DOWN = 4, MOE_STAGE_SHARED = 5, MOE_STAGE_COMBINE = 6, MOE_N_STAGES = 7 };
+
+/* Kernel family of a layer call.  AUTO: the decode (GEMV-style) kernels for
+ * T <= 16, the grouped-GEMM prefill kernels above.  DECODE / PREFILL force
+ * one family at any T (the pages' practice of running one kernel family
+ * beside another on the same activations to compare them, "Qwen3.6-35B-A3B:
+ * pictures, several requests at once and speed", Speed (0.1.45)).  Both
+ * families compute the same layer within the output tolerance; the prefill
+ * family's range limits are stated at moe_layer_forward. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
+
+/* Per-call options of moe_layer_forward_ex (host struct; all zero = the
+ * defaults of moe_layer_forward). */
+typedef struct moe_forward_opts {
+  int32_t path;        /* moe_path */
+  int32_t reserved[3]; /* must be 0 */
+  /* Profiling: hipEvent_t pairs (created by the caller) recorded on the
+   * call's stream around each stage: index MOE_STAGE_*; a stage is profiled
+   * when both of its events are non-NULL.  The gate/up and down stages'
+   * kernels record their events at their own start and end (kernel time
+   * without the launch gap); on calls of up to eight tokens the down
+   * stage's kernel also does the combine, and the combine stage records
+   * nothing. */
+  void *stage_start[MOE_N_STAGES];
+  void *stage_stop[MOE_N_STAGES];
+} moe_forward_opts;
+
+/* The whole layer: route, permute, routed experts, shared expert, combine
+ * (the MoE step of "Qwen3.6-35B-A3B: pictures, several requests at once and
+ * speed": 256 experts, top-8, a shared expert beside them; its Several
+ * requests at once: the tokens of a batch share each expert's weight
+ * reads).  y float [T][H]; res (host) or NULL: residual epilogue; topk_ids
+ * [T][K] / topk_w [T][K] or NULL (copies of the routing used).  ws: at least
+ * moe_workspace_bytes(L, T) bytes, 256-byte aligned, prepared once by
+ * moe_workspace_init.  T = 0 is a no-op.
+ *
+ * Range of the prefill family (int4 weights, T > 16 or MOE_PATH_PREFILL):
+ * its matrix products run in fp16, so every |x| must stay below 65504, every
+ * dequantized weight |q * s| below 65504 and every SwiGLU value below 65504
+ * in magnitude; a token outside that range gets non-finite outputs (other
+ * tokens of the call are unaffected), where the decode family computes it
+ * in fp32 and stays finite.  Values of a normalised layer input and of
+ * block scales of real weights are many orders of magnitude inside it.
+ *
+ * The test-only environment variable MOE_FORCE_PATH=decode|prefill, read at
+ * every call, forces the family of calls that leave the choice to AUTO. */
 int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
                       int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
-/* Profiling hook (host, process-wide): after moe_profile_events(stage,
- * start, stop), every later moe_layer_forward records the hipEvent_t `start`
- * on its stream just before that stage's kernels and `stop` just after
- * them, so a caller can time a stage live (events must be created before
- * use; each stage keeps its own pair).  Stages: 1 router + top-k,
- * 2 permutation, 3 gate/up + SwiGLU (routed and shared experts), 4 down
- * (routed and shared), 6 combine; 5 is reserved (the shared expert runs
- * inside 3 and 4).  NULL events switch one stage off; stage 0 switches all
- * off.  Not for concurrent use from several host threads. */
-enum { MOE_STAGE_NONE = 0, MOE_STAGE_ROUTE = 1, MOE_STAGE_PERMUTE = 2, MOE_STAGE_GATEUP = 3,
-       MOE_STAGE_DOWN = 4, MOE_STAGE_SHARED = 5, MOE_STAGE_COMBINE = 6 };
-int moe_profile_events(int32_t stage, void *start_event, void *stop_event);
+/* moe_layer_forward with per-call options (opts NULL = defaults).
+ * MOE_ERR_INVALID_ARG for an unknown path or nonzero reserved words. */
+int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
+                         int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, const moe_forward_opts *opts,
+                         void *stream);
 
 /* Static text for a status code (host). */
 const char *moe_status_string(int status);

@@ -40,6 +40,16 @@ class MoeResidual(ctypes.Structure):
                 ("normed_out", ctypes.c_void_p), ("eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
 
 
+MOE_N_STAGES = 7
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+PATHS = {"auto": MOE_PATH_AUTO, "decode": MOE_PATH_DECODE, "prefill": MOE_PATH_PREFILL}
+
+
+class MoeForwardOpts(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+                ("stage_start", ctypes.c_void_p * MOE_N_STAGES), ("stage_stop", ctypes.c_void_p * MOE_N_STAGES)]
+
+
 class MoeLayer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
@@ -50,18 +60,20 @@ _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _PL = ctypes.POINTER(MoeLayer)
 _PE = ctypes.POINTER(MoeExperts)
 _PR = ctypes.POINTER(MoeResidual)
+_PO = ctypes.POINTER(MoeForwardOpts)
 _SIGS = {
     "moe_workspace_bytes": ([_PL, _i32], _sz),
     "moe_workspace_init": ([_vp, _sz, _vp], ctypes.c_int),
-    "moe_route": ([_PL, _vp, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe_route_workspace_bytes": ([_PL, _i32], _sz),
+    "moe_route": ([_PL, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_permute_workspace_bytes": ([_i32, _i32, _i32], _sz),
     "moe_permute": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_expert_ffn_workspace_bytes": ([_i32, _i32], _sz),
     "moe_expert_ffn": ([_PE, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_combine": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _PR, _vp], ctypes.c_int),
     "moe_layer_forward": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe_layer_forward_ex": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _PO, _vp], ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
-    "moe_profile_events": ([_i32, _vp, _vp], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -173,11 +185,17 @@ def make_workspace(layer: Layer, max_tokens: int, device="cuda", stream=None) ->
     return ws
 
 
-def route(layer: Layer, x_bf16: torch.Tensor, topk_ids, topk_w, logits, stream=None):
+def route_workspace_bytes(layer: Layer, T: int) -> int:
+    c = layer.c()
+    return int(_lib.moe_route_workspace_bytes(ctypes.byref(c), T))
+
+
+def route(layer: Layer, x_bf16: torch.Tensor, topk_ids, topk_w, logits=None, ws=None, stream=None):
+    """Router + top-k.  logits None: they pass through ws (see moe_route)."""
     c = layer.c()
     T = x_bf16.shape[0]
     _check("moe_route", _lib.moe_route(ctypes.byref(c), _ptr(x_bf16), T, _ptr(topk_ids), _ptr(topk_w),
-                                       _ptr(logits), _stream(stream)))
+                                       _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def permute(topk_ids, topk_w, E: int, out: dict, ws: torch.Tensor, stream=None):
@@ -217,30 +235,33 @@ def combine(rows_out, inv_pos, T: int, K: int, H: int, shared_out, y, res: MoeRe
                                            ctypes.byref(res) if res is not None else None, _stream(stream)))
 
 
-def layer_forward(layer: Layer, x_bf16, y, ws, res: MoeResidual | None = None, topk_ids=None, topk_w=None,
-                  stream=None, c_layer: MoeLayer | None = None):
-    c = layer.c() if c_layer is None else c_layer
-    T = x_bf16.shape[0]
-    _check("moe_layer_forward", _lib.moe_layer_forward(
-        ctypes.byref(c), _ptr(x_bf16), T, _ptr(y), ctypes.byref(res) if res is not None else None,
-        _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
-
-
 STAGES = {"route": 1, "permute": 2, "gateup": 3, "down": 4, "shared": 5, "combine": 6}
 
 
-def profile_events(stage, start=None, stop=None):
-    """Have later layer_forward calls record torch.cuda.Event `start`/`stop`
-    around one stage (see moe_profile_events).  stage None switches every
-    stage off; start None switches this stage off."""
-    if stage is None:
-        _check("moe_profile_events", _lib.moe_profile_events(0, None, None))
-        return
-    if start is None:
-        _check("moe_profile_events", _lib.moe_profile_events(STAGES[stage], None, None))
-        return
-    _check("moe_profile_events", _lib.moe_profile_events(STAGES[stage], ctypes.c_void_p(start.cuda_event),
-                                                          ctypes.c_void_p(stop.cuda_event)))
+def forward_opts(path="auto", events=None) -> MoeForwardOpts:
+    """Per-call options: path "auto" | "decode" | "prefill"; events a dict
+    stage name -> (start, stop) torch.cuda.Event pairs (already created, e.g.
+    by one record) that the call records around that stage."""
+    o = MoeForwardOpts()
+    o.path = PATHS[path]
+    for name, (a, b) in (events or {}).items():
+        o.stage_start[STAGES[name]] = a.cuda_event
+        o.stage_stop[STAGES[name]] = b.cuda_event
+    return o
+
+
+def layer_forward(layer: Layer, x_bf16, y, ws, res: MoeResidual | None = None, topk_ids=None, topk_w=None,
+                  stream=None, c_layer: MoeLayer | None = None, opts: MoeForwardOpts | None = None):
+    c = layer.c() if c_layer is None else c_layer
+    T = x_bf16.shape[0]
+    if opts is None:
+        _check("moe_layer_forward", _lib.moe_layer_forward(
+            ctypes.byref(c), _ptr(x_bf16), T, _ptr(y), ctypes.byref(res) if res is not None else None,
+            _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        _check("moe_layer_forward_ex", _lib.moe_layer_forward_ex(
+            ctypes.byref(c), _ptr(x_bf16), T, _ptr(y), ctypes.byref(res) if res is not None else None,
+            _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), ctypes.byref(opts), _stream(stream)))
 
 
 def raw_lib():

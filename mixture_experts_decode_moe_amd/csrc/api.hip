@@ -3,17 +3,11 @@
 // allocates nothing; every buffer is the caller's.
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "common.h"
 
 using namespace moe;
-
-namespace {
-thread_local LaunchEvents t_launch_events;
-}  // namespace
-
-// the profiling hook's events for the next expert-kernel launch
-LaunchEvents &moe::launch_events() { return t_launch_events; }
 
 namespace {
 
@@ -59,30 +53,43 @@ int check_layer(const moe_layer *L) {
 
 constexpr size_t kControlBytes = 256;  // control words kept zero between calls
 
-// profiling hook state (see moe_profile_events): one event pair per stage
-constexpr int kStages = MOE_STAGE_COMBINE + 1;
-hipEvent_t g_prof_start[kStages] = {}, g_prof_stop[kStages] = {};
+// The profiling events a call asked for (moe_forward_opts), one pair per
+// stage.  A stage's expert kernel records its pair itself at its own start
+// and end (launch_kernel); other stages are bracketed here.
+struct CallEvents {
+  hipEvent_t start[MOE_N_STAGES] = {}, stop[MOE_N_STAGES] = {};
+  LaunchEvents of(int32_t st) const { return LaunchEvents{start[st], stop[st]}; }
+};
 
-// A stage's events: the stage's expert kernel, when it has one, records
-// them itself at its own start and end (launch_kernel); otherwise they
-// bracket the stage's launches here.
+// Records a stage's start event on construction and its stop event on
+// destruction, unless the stage's expert kernel took the pair
+// (kernel_takes = true).
 struct StageMark {
+  const CallEvents &ev;
   int32_t stage;
   hipStream_t s;
-  StageMark(int32_t st, hipStream_t str) : stage(st), s(str) {
-    if (g_prof_start[stage]) {
-      (void)hipEventRecord(g_prof_start[stage], s);
-      t_launch_events = LaunchEvents{g_prof_start[stage], g_prof_stop[stage]};
-    }
+  bool kernel_takes;
+  StageMark(const CallEvents &e, int32_t st, hipStream_t str, bool kernel = false)
+      : ev(e), stage(st), s(str), kernel_takes(kernel) {
+    if (!kernel_takes && ev.start[stage]) (void)hipEventRecord(ev.start[stage], s);
   }
   ~StageMark() {
-    if (g_prof_stop[stage] && t_launch_events.stop == g_prof_stop[stage]) {
-      // no expert kernel took the events
-      t_launch_events = LaunchEvents{};
-      (void)hipEventRecord(g_prof_stop[stage], s);
-    }
+    if (!kernel_takes && ev.stop[stage]) (void)hipEventRecord(ev.stop[stage], s);
   }
 };
+
+// The kernel family a call takes: the caller's choice, else the test-only
+// override MOE_FORCE_PATH=decode|prefill (read at every call, so a process
+// can switch it), else chosen from the token count.
+int32_t effective_path(const moe_forward_opts *opts) {
+  if (opts && opts->path != MOE_PATH_AUTO) return opts->path;
+  const char *env = getenv("MOE_FORCE_PATH");
+  if (env) {
+    if (strcmp(env, "decode") == 0) return MOE_PATH_DECODE;
+    if (strcmp(env, "prefill") == 0) return MOE_PATH_PREFILL;
+  }
+  return MOE_PATH_AUTO;
+}
 
 struct LayerWs {
   uint32_t *control;  // kControlBytes of words kept zero between calls; [0..1]: prefill gate/up item queue
@@ -190,15 +197,25 @@ int moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   return hip_status(launch_fill_zero(ws, kControlBytes, as_stream(stream)));
 }
 
+size_t moe_route_workspace_bytes(const moe_layer *L, int32_t T) {
+  if (check_layer(L) != MOE_OK || T < 0) return 0;
+  return align_up(static_cast<size_t>(T) * L->n_experts * sizeof(float), 256);
+}
+
 int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *topk_ids, float *topk_w, float *logits,
-              void *stream) {
+              void *ws, size_t ws_bytes, void *stream) {
   int rc = check_layer(L);
   if (rc != MOE_OK) return rc;
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
-  if (!x_bf16 || !topk_ids || !topk_w || !logits || !aligned(x_bf16, 16)) return MOE_ERR_INVALID_ARG;
+  if (!x_bf16 || !topk_ids || !topk_w || !aligned(x_bf16, 16)) return MOE_ERR_INVALID_ARG;
+  if (!logits) {
+    // the logits pass between the two kernels through the caller's workspace
+    if (!ws || !aligned(ws, 16) || ws_bytes < moe_route_workspace_bytes(L, T)) return MOE_ERR_WORKSPACE;
+    logits = static_cast<float *>(ws);
+  }
   RouteArgs a{L->router_w, L->router_bias, x_bf16, T, L->hidden, L->n_experts, L->top_k, L->renorm, logits,
-              topk_ids, topk_w};
+              topk_ids, topk_w, nullptr, kPathAuto};
   hipError_t e = launch_router_logits(a, as_stream(stream));
   if (e == hipSuccess) e = launch_topk(a, as_stream(stream));
   return hip_status(e);
@@ -321,11 +338,17 @@ int moe_combine(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_
   return hip_status(launch_combine(combine_args(rows_out, inv_pos, T, K, H, shared_out, y, res), as_stream(stream)));
 }
 
-int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
-                      int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
+                         int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, const moe_forward_opts *opts,
+                         void *stream) {
   int rc = check_layer(L);
   if (rc != MOE_OK) return rc;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (opts) {
+    if (opts->path < MOE_PATH_AUTO || opts->path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
+    for (int32_t r : opts->reserved)
+      if (r != 0) return MOE_ERR_INVALID_ARG;
+  }
   if (T == 0) return MOE_OK;
   if (static_cast<int64_t>(T) * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if (!x_bf16 || !y || !aligned(x_bf16, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
@@ -338,6 +361,16 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
   const int32_t K = L->top_k, E = L->n_experts, H = L->hidden;
   int32_t *ids = topk_ids ? topk_ids : w.ids;
   float *tw = topk_w ? topk_w : w.w;
+  const int32_t path = effective_path(opts);
+  CallEvents ev;
+  if (opts)
+    for (int st = 1; st < MOE_N_STAGES; ++st) {
+      // a stage is profiled only with both of its events
+      if (opts->stage_start[st] && opts->stage_stop[st]) {
+        ev.start[st] = static_cast<hipEvent_t>(opts->stage_start[st]);
+        ev.stop[st] = static_cast<hipEvent_t>(opts->stage_stop[st]);
+      }
+    }
 
   const int32_t TK = T * K;
   const bool has_shared = L->shared.n_experts == 1;
@@ -350,9 +383,12 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
   xa.act = w.act;
   xa.rows_out = w.rows_out;
   xa.max_units = TK < E ? TK : E;
+  xa.path = path;
+  xa.distinct_ids = 1;  // the layer's own top-k picks distinct experts per token
 
   hipError_t e;
-  if (T <= kFusedTokens) {
+  const bool decode_batch = T <= kFusedTokens && path != MOE_PATH_PREFILL;
+  if (decode_batch) {
     // decode batch: the router's partial logits; the top-k and the
     // permutation then run inside the gate/up kernel when it is the
     // matrix-core one, else in one block of their own
@@ -382,16 +418,16 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
     xa.route_here = (mfma_decode_ok(xa) && E <= 256) ? 1 : 0;
     if (xa.route_here) xa.units = w.units;  // published by the gate/up kernel's routing
     xa.route = fa;
-    StageMark m(MOE_STAGE_ROUTE, s);
+    StageMark m(ev, MOE_STAGE_ROUTE, s);
     e = xa.route_here ? launch_route_partial(fa, s) : launch_route_fused(fa, s);
   } else {
-    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw, w.x16};
+    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw, w.x16, path};
     if (router_writes_x16(ra)) {
       xa.x16 = w.x16;
       xa.queue = w.control;
     }
     {
-      StageMark m(MOE_STAGE_ROUTE, s);
+      StageMark m(ev, MOE_STAGE_ROUTE, s);
       e = launch_router_logits(ra, s);
       if (e == hipSuccess) e = launch_topk(ra, s);
     }
@@ -411,52 +447,41 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
     pa.n_active = w.n_active;
     pa.rank = w.rank;
     pa.tile_hist = w.tile_hist;
-    StageMark m(MOE_STAGE_PERMUTE, s);
+    StageMark m(ev, MOE_STAGE_PERMUTE, s);
     e = launch_permute(pa, s);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   {
-    StageMark m(MOE_STAGE_GATEUP, s);
+    StageMark m(ev, MOE_STAGE_GATEUP, s, true);
+    xa.ev = ev.of(MOE_STAGE_GATEUP);
     e = launch_gateup(xa, s);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (xa.route_here && (!res || !res->normed_out) && down_combine_ok(xa, K)) {
-    // a few tokens: down projection and combine in one launch
+    // a few tokens: down projection and combine in one launch (the down
+    // stage's events bracket it; the combine stage has no launch of its own)
+    xa.ev = ev.of(MOE_STAGE_DOWN);
     DownCombineArgs d{xa, w.units, w.inv_pos, K, E, y, res ? res->residual_in : nullptr,
                       res ? res->residual_out : nullptr};
-    {
-      StageMark m(MOE_STAGE_DOWN, s);
-      e = launch_down_combine(d, s);
-    }
-    StageMark m(MOE_STAGE_COMBINE, s);  // no launch of its own
-    return hip_status(e);
+    return hip_status(launch_down_combine(d, s));
   }
   {
-    StageMark m(MOE_STAGE_DOWN, s);
+    StageMark m(ev, MOE_STAGE_DOWN, s, true);
+    xa.ev = ev.of(MOE_STAGE_DOWN);
     e = launch_down(xa, s);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   CombineArgs ca = combine_args(w.rows_out, w.inv_pos, T, K, H,
                                 has_shared ? w.rows_out + static_cast<size_t>(TK) * H : nullptr, y, res);
-  StageMark m(MOE_STAGE_COMBINE, s);
+  StageMark m(ev, MOE_STAGE_COMBINE, s);
   return hip_status(launch_combine(ca, s));
 }
 
-int moe_profile_events(int32_t stage, void *start_event, void *stop_event) {
-  if (stage < MOE_STAGE_NONE || stage > MOE_STAGE_COMBINE) return MOE_ERR_INVALID_ARG;
-  if (stage == MOE_STAGE_NONE) {
-    for (int i = 0; i < kStages; ++i) g_prof_start[i] = g_prof_stop[i] = nullptr;
-    return MOE_OK;
-  }
-  if (!start_event || !stop_event) {
-    g_prof_start[stage] = g_prof_stop[stage] = nullptr;
-    return MOE_OK;
-  }
-  g_prof_start[stage] = static_cast<hipEvent_t>(start_event);
-  g_prof_stop[stage] = static_cast<hipEvent_t>(stop_event);
-  return MOE_OK;
+int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
+                      int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  return moe_layer_forward_ex(L, x_bf16, T, y, res, topk_ids, topk_w, ws, ws_bytes, nullptr, stream);
 }
 
 }  // extern "C"

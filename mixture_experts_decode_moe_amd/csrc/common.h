@@ -87,6 +87,16 @@ struct Carver {
 
 // ---- launch helpers declared by each translation unit -----------------------
 
+// Profiling events for one expert-kernel launch (both null when the call
+// asks for none).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Which kernel family a call takes: chosen from the token count, or forced
+// by the caller (moe_forward_opts::path).
+enum PathSel : int32_t { kPathAuto = 0, kPathDecode = 1, kPathPrefill = 2 };
+
 struct RouteArgs {
   const float *router_w;
   const float *router_bias;
@@ -96,6 +106,7 @@ struct RouteArgs {
   int32_t *ids;
   float *w;
   uint16_t *x16;  // optional [T][H]: x in fp16, pair-permuted 8-element pieces
+  int32_t path;   // PathSel: kPathPrefill takes the matrix-core router GEMM at any T
 };
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s);
 // whether launch_router_logits writes x16 (when given) for this call
@@ -165,6 +176,9 @@ struct FfnArgs {
   // point at the same buffers for the kernels that follow)
   int32_t route_here;
   RouteFusedArgs route;
+  int32_t path;          // PathSel
+  int32_t distinct_ids;  // 1: every token picks an expert at most once, so a unit has at most T rows
+  LaunchEvents ev;       // profiling events of the expert kernel of this stage (host side only)
 };
 hipError_t launch_gateup(const FfnArgs &a, hipStream_t s);
 bool mfma_decode_ok(const FfnArgs &a);  // the decode matrix-core kernels take this call
@@ -199,25 +213,16 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
-// Events of the profiling hook for the next expert-kernel launch of a stage
-// (both null when nothing is profiled): that launch has the runtime record
-// them at the kernel's own start and end, so the interval is the kernel's
-// execution time without the launch gap.
-struct LaunchEvents {
-  hipEvent_t start = nullptr, stop = nullptr;
-};
-LaunchEvents &launch_events();
-
+// Launches a kernel; with profiling events (a caller's per-call request)
+// the runtime records them at the kernel's own start and end, so the
+// interval is the kernel's execution time without the launch gap.
 template <typename... KArgs, typename... Args>
 hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
-                         Args... args) {
-  LaunchEvents &ev = launch_events();
-  if (ev.start) {
+                         const LaunchEvents &ev, Args... args) {
+  if (ev.start)
     hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.start, ev.stop, 0u, args...);
-    ev = LaunchEvents{};
-  } else {
+  else
     kernel<<<grid, block, lds, s>>>(args...);
-  }
   return hipGetLastError();
 }
 

@@ -308,7 +308,7 @@ static hipError_t launch_dc_t(const DownCombineArgs &d, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   return launch_kernel(down_combine_kernel<FMT, NQ>, dim3(d.f.H / kDcFeat), dim3(64 * dc_waves(d.f)),
-                       static_cast<uint32_t>(lds), s, d);
+                       static_cast<uint32_t>(lds), s, d.f.ev, d);
 }
 
 template <int FMT>

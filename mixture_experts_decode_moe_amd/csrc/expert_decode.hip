@@ -429,7 +429,7 @@ static hipError_t launch_gateup_t(const FfnArgs &a, hipStream_t s) {
   hipError_t e = set_lds(gateup_kernel<FMT, NI>, lds);
   if (e != hipSuccess) return e;
   const int items = max_items(a, a.F / kGuSlice, a.Fs / kGuSlice);
-  return launch_kernel(gateup_kernel<FMT, NI>, dim3(grid_for(items)), dim3(256), lds, s, a);
+  return launch_kernel(gateup_kernel<FMT, NI>, dim3(grid_for(items)), dim3(256), lds, s, a.ev, a);
 }
 
 template <int FMT, int NI>
@@ -438,7 +438,7 @@ static hipError_t launch_down_t(const FfnArgs &a, hipStream_t s) {
   hipError_t e = set_lds(down_kernel<FMT, NI>, lds);
   if (e != hipSuccess) return e;
   const int items = max_items(a, a.H / kDnSlice, a.H / kDnSlice);
-  return launch_kernel(down_kernel<FMT, NI>, dim3(grid_for(items)), dim3(256), lds, s, a);
+  return launch_kernel(down_kernel<FMT, NI>, dim3(grid_for(items)), dim3(256), lds, s, a.ev, a);
 }
 
 template <int FMT>

@@ -616,7 +616,12 @@ bool mfma_decode_ok(const FfnArgs &a) {
   // staged x plus the gate/up kernel's fixed LDS (partial tiles, item
   // table, SwiGLU staging) must fit one compute unit's 160 KiB
   const size_t lds = static_cast<size_t>(a.T) * (a.H / 8 + 1) * 16 + 80 * 1024;
-  return (a.fmt == MOE_W_INT4_B32 || a.fmt == MOE_W_INT8_ROW) && a.T <= kFusedTokens && lds <= 160 * 1024 &&
+  // the gate/up kernel holds at most 16 rows of a unit (one MFMA tile):
+  // every unit's rows are among the n_rows routed rows, and with distinct
+  // experts per token a unit has at most T rows
+  const bool rows16 = a.n_rows <= 16 || a.distinct_ids;
+  return a.path != kPathPrefill && rows16 && (a.fmt == MOE_W_INT4_B32 || a.fmt == MOE_W_INT8_ROW) &&
+         a.T <= kFusedTokens && lds <= 160 * 1024 &&
          (a.Fs == 0 || a.Fs == a.F) && split_k(a.H, block_k(a.fmt), kGuMaxWaves, jw, ks) &&
          split_k(a.F, block_k(a.fmt), kDnMaxWaves, jw, ks);
 }
@@ -650,7 +655,7 @@ static hipError_t launch_gateup_mfma_t(const FfnArgs &a, int ks, hipStream_t s) 
   const int cus = cu_count();
   int grid = (items + kGuTable - 1) / kGuTable;
   if (grid < cus) grid = items < cus ? (items < 1 ? 1 : items) : cus;
-  return launch_kernel(gateup_mfma_kernel<FMT, JW, D>, dim3(grid), dim3(64 * ks), lds, s, a);
+  return launch_kernel(gateup_mfma_kernel<FMT, JW, D>, dim3(grid), dim3(64 * ks), lds, s, a.ev, a);
 }
 
 template <int FMT>
@@ -669,11 +674,11 @@ static hipError_t launch_down_mfma_f(const FfnArgs &a, hipStream_t s) {
   const int tiles = a.H / 64;
   const int grid = mfma_grid((a.Fs > 0 ? tiles : 0) + a.max_units * tiles);
   if (jw == 1)
-    return launch_kernel(down_mfma_kernel<FMT, 1>, dim3(grid), dim3(64 * ks), 0, s, a);
+    return launch_kernel(down_mfma_kernel<FMT, 1>, dim3(grid), dim3(64 * ks), 0, s, a.ev, a);
   else if (jw == 2)
-    return launch_kernel(down_mfma_kernel<FMT, 2>, dim3(grid), dim3(64 * ks), 0, s, a);
+    return launch_kernel(down_mfma_kernel<FMT, 2>, dim3(grid), dim3(64 * ks), 0, s, a.ev, a);
   else
-    return launch_kernel(down_mfma_kernel<FMT, 4>, dim3(grid), dim3(64 * ks), 0, s, a);
+    return launch_kernel(down_mfma_kernel<FMT, 4>, dim3(grid), dim3(64 * ks), 0, s, a.ev, a);
 }
 
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t s) {

@@ -1234,7 +1234,8 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
 
 bool prefill_ok(const FfnArgs &a) {
   const int units = (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1);
-  return a.fmt == MOE_W_INT4_B32 && a.T > kFusedTokens && (a.Fs == 0 || a.Fs == a.F) && a.H % 128 == 0 &&
+  const bool many = a.path == kPathPrefill || (a.path == kPathAuto && a.T > kFusedTokens);
+  return a.fmt == MOE_W_INT4_B32 && many && (a.Fs == 0 || a.Fs == a.F) && a.H % 128 == 0 &&
          a.F % 128 == 0 && a.F % kPfCols == 0 && a.H % kPfCols == 0 && units <= kPfMaxUnits;
 }
 
@@ -1283,23 +1284,23 @@ hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    return launch_kernel(gateup_gemm128_kernel<16>, dim3(cus), dim3(kGmThreads), 0, s, a);
+    return launch_kernel(gateup_gemm128_kernel<16>, dim3(cus), dim3(kGmThreads), 0, s, a.ev, a);
   }
   if (gm_pair_ok(a)) {
     return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128), 1)), dim3(kGmThreads), 0,
-                         s, a);
+                         s, a.ev, a);
   }
   return launch_kernel(gateup_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.F / kPfCols))), dim3(kPfThreads), 0,
-                       s, a);
+                       s, a.ev, a);
 }
 
 hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
   if (gm_pair_ok(a)) {
-    return launch_kernel(down_gemm_kernel<4>, dim3(gm_grid(pf_tiles_upper(a) * (a.H / 256), 2)), dim3(kGmThreads), 0, s,
+    return launch_kernel(down_gemm_kernel<4>, dim3(gm_grid(pf_tiles_upper(a) * (a.H / 256), 2)), dim3(kGmThreads), 0, s, a.ev,
                          a);
   }
   return launch_kernel(down_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.H / kPfCols))), dim3(kPfThreads), 0,
-                       s, a);
+                       s, a.ev, a);
 }
 
 }  // namespace moe

@@ -356,7 +356,10 @@ hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-static bool router_mfma_ok(const RouteArgs &a) { return a.T > kFusedTokens && a.H % (8 * kRmK) == 0; }
+static bool router_mfma_ok(const RouteArgs &a) {
+  const bool many = a.path == kPathPrefill || (a.path == kPathAuto && a.T > kFusedTokens);
+  return many && a.H % (8 * kRmK) == 0;
+}
 
 bool router_writes_x16(const RouteArgs &a) { return a.x16 != nullptr && router_mfma_ok(a); }
 

@@ -58,9 +58,10 @@ def rel_max_err(y, ref):
     return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
-def run_layer(dlayer, x_dev, T, ws=None, residual=None, with_logits=True, normed=True):
-    """Runs moe_layer_forward; also runs moe_route on the same input (same
-    kernels) to read the GPU's fp32 logits."""
+def run_layer(dlayer, x_dev, T, ws=None, residual=None, with_logits=True, normed=True, opts=None):
+    """Runs moe_layer_forward (moe_layer_forward_ex with `opts`); also runs
+    moe_route on the same input (same kernels) to read the GPU's fp32
+    logits, unless with_logits is False."""
     from mixture_experts_decode_moe_amd import binding as mb
     H, K, E = dlayer.hidden, dlayer.top_k, dlayer.n_experts
     if ws is None:
@@ -74,7 +75,7 @@ def run_layer(dlayer, x_dev, T, ws=None, residual=None, with_logits=True, normed
         r_out = torch.empty((T, H), dtype=torch.int16, device="cuda")
         n_out = torch.empty((T, H), dtype=torch.int16, device="cuda") if normed else None
         res = mb.residual(residual, r_out, n_out)
-    mb.layer_forward(dlayer, x_dev, y, ws, res=res, topk_ids=ids, topk_w=w)
+    mb.layer_forward(dlayer, x_dev, y, ws, res=res, topk_ids=ids, topk_w=w, opts=opts)
     out = {}
     if with_logits:
         lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
@@ -93,6 +94,19 @@ def run_layer(dlayer, x_dev, T, ws=None, residual=None, with_logits=True, normed
         if normed:
             out["normed_out"] = host_u16(n_out)
     return out
+
+
+def bf16_rne_f32(v: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def residual_expected(r_bf16: np.ndarray, y_f32: np.ndarray) -> np.ndarray:
+    """The residual epilogue's exact result: bf16_rne(float32(r) + y) with
+    one float32 addition."""
+    rf = (np.asarray(r_bf16, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return bf16_rne_f32(rf + np.asarray(y_f32, np.float32))
 
 
 def logit_error_bound(layer_host, x_host):

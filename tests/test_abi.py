@@ -97,7 +97,12 @@ def test_other_entry_points_reject_bad_arguments(mb):
     assert lib.moe_layer_forward(ctypes.byref(L), p, 4, p, None, None, None, p, 16, None) == -3
     assert lib.moe_layer_forward(ctypes.byref(L), ctypes.c_void_p((1 << 20) + 2), 4, p, None, None, None, p,
                                  1 << 30, None) == -1
-    assert lib.moe_route(ctypes.byref(L), p, 4, None, p, p, None) == -1
+    assert lib.moe_route(ctypes.byref(L), p, 4, None, p, p, None, 0, None) == -1
+    # logits optional: without them the call needs a workspace for them
+    assert lib.moe_route(ctypes.byref(L), p, 4, p, p, None, None, 0, None) == -3
+    assert lib.moe_route(ctypes.byref(L), p, 4, p, p, None, p, 16, None) == -3
+    assert lib.moe_route_workspace_bytes(ctypes.byref(L), 4) >= 4 * 256 * 4
+    assert lib.moe_route_workspace_bytes(ctypes.byref(L), -1) == 0
     assert lib.moe_permute(p, p, 4, 9, 8, p, p, p, p, p, p, p, p, 1 << 20, None) == -1  # K > E
     assert lib.moe_permute(p, p, 4, 2, 4096, p, p, p, p, p, p, p, p, 1 << 20, None) == -2
     assert lib.moe_permute(p, p, 4, 2, 8, p, p, p, p, p, p, p, None, 0, None) == -3
@@ -110,3 +115,34 @@ def test_other_entry_points_reject_bad_arguments(mb):
     assert lib.moe_layer_forward(ctypes.byref(_fake_layer(mb)), p, 4, p, ctypes.byref(bad), None, None, p,
                                  1 << 30, None) == -1
     assert lib.moe_workspace_init(None, 0, None) == -3
+
+
+def test_forward_options_are_validated(mb):
+    """Per-call options: an unknown path or a nonzero reserved word is
+    rejected before anything is launched; all-zero options are the
+    defaults."""
+    lib = mb.raw_lib()
+    p = ctypes.c_void_p(1 << 20)
+    L = _fake_layer(mb)
+    o = mb.forward_opts()
+    assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 0, p, None, None, None, p, 1 << 30, ctypes.byref(o),
+                                    None) == 0
+    o.path = 3
+    assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
+                                    None) == -1
+    o = mb.forward_opts("prefill")
+    o.reserved[1] = 5
+    assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
+                                    None) == -1
+    assert mb.forward_opts("decode").path == 1 and mb.forward_opts("prefill").path == 2
+
+
+def test_no_process_global_mutable_state_in_the_host_code():
+    """The host side keeps nothing between calls: no file-scope variables
+    (the profiling events are a per-call option), only functions, types and
+    constants."""
+    src = open(os.path.join(ROOT, "mixture_experts_decode_moe_amd", "csrc", "api.hip")).read()
+    src = re.sub(r"//.*", "", src)
+    assert "thread_local" not in src
+    assert not re.search(r"^static\s+(?!inline|bool|int|size_t|hipError_t|void|const)", src, flags=re.M)
+    assert not re.search(r"^(hipEvent_t|int|float|bool)\s+\w+\s*(\[.*\])?\s*(=.*)?;", src, flags=re.M)

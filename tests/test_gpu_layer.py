@@ -138,30 +138,34 @@ def test_small_batch_residual_without_norm(mb):
     say("residual without norm, T=3")
     gpu = pu.run_layer(dl, pu.dev_u16(x), 3, residual=pu.dev_u16(r), normed=False)
     err, ties = pu.check_layer_against_oracle(layer, x, gpu)
+    # the epilogue exactly: one float32 addition of the layer's own y, then
+    # round to nearest even
+    assert np.array_equal(gpu["residual_out"], pu.residual_expected(r, gpu["y"])), \
+        "residual_out is not bf16_rne(float32(r) + y)"
+    # and against the oracle's double-precision rounding of the same sum
     r_ref = oracle.residual(r, gpu["y"].astype(np.float32).astype(np.float64))
-    d_r = np.abs(r_ref.astype(np.int32) - gpu["residual_out"].astype(np.int32))
-    assert d_r.max() <= 1, "residual_out differs from bf16(r + y) by more than one bf16 step"
+    assert np.abs(r_ref.astype(np.int32) - gpu["residual_out"].astype(np.int32)).max() <= 1
     say(f"  rel err {err:.2e}, near ties {ties}")
 
 
-def test_prefill_chunk_sampled(mb):
-    """Config 4 at full size (2048 tokens), oracle on 64 sampled tokens."""
+@pytest.mark.timeout(600)
+def test_prefill_chunk_full(mb):
+    """Config 4 at full size (2048 tokens, the launch configuration the
+    benchmark times), every token checked against the oracle (threaded on
+    the host cores)."""
     import parity_util as pu
     shape = synth.CONFIGS[4]
-    say("prefill cfg4 T=2048 sampled")
+    say("prefill cfg4 T=2048, all tokens")
     layer = synth.make_layer(shape)
     x = synth.make_x(shape)
     dl = mb.layer_to_device(layer)
     gpu = pu.run_layer(dl, pu.dev_u16(x), shape.tokens)
-    rng = np.random.default_rng(0)
-    sample = np.unique(np.concatenate([[0, 1, shape.tokens - 1], rng.choice(shape.tokens, 61, replace=False)]))
-    err, ties = pu.check_layer_against_oracle(layer, x, gpu, sample=sample)
-    # properties that hold at any size: every token got K distinct experts
     ids = gpu["ids"]
     assert ids.min() >= 0 and ids.max() < shape.n_experts
     assert all(len(set(r.tolist())) == shape.top_k for r in ids)
     assert np.all(np.abs(gpu["w"].sum(axis=1) - 1.0) <= 1e-6)
-    say(f"cfg4 sampled: rel err {err:.2e}, near ties {ties}")
+    err, ties = pu.check_layer_against_oracle(layer, x, gpu)
+    say(f"cfg4 all tokens: rel err {err:.2e}, near ties {ties}")
 
 
 @pytest.mark.timeout(900)
@@ -183,9 +187,10 @@ def test_stack_teacher_forced(mb):
         gpu = pu.run_layer(dl, pu.dev_u16(x), shape.tokens, residual=pu.dev_u16(r))
         err, ties = pu.check_layer_against_oracle(layer, x, gpu)
         worst = max(worst, err)
+        assert np.array_equal(gpu["residual_out"], pu.residual_expected(r, gpu["y"])), \
+            "residual_out is not bf16_rne(float32(r) + y)"
         r_ref = oracle.residual(r, gpu["y"].astype(np.float32).astype(np.float64))
-        d_r = np.abs(r_ref.astype(np.int32) - gpu["residual_out"].astype(np.int32))
-        assert d_r.max() <= 1, "residual_out differs from bf16(r + y) by more than one bf16 step"
+        assert np.abs(r_ref.astype(np.int32) - gpu["residual_out"].astype(np.int32)).max() <= 1
         n_ref = oracle.rmsnorm(gpu["residual_out"])
         d_n = np.abs(n_ref.astype(np.int32) - gpu["normed_out"].astype(np.int32))
         assert d_n.max() <= 1, "normed_out differs from bf16(rmsnorm(r)) by more than one bf16 step"
