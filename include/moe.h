@@ -236,6 +236,30 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
                          int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, const moe_forward_opts *opts,
                          void *stream);
 
+/* Bytes of the device array moe_layer_forward_noalloc uses as its
+ * workspace (one array per GPU the library runs on). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_layer_forward_ex without a workspace argument.  The workspace is a
+ * file-scope device array of MOE_NOALLOC_SCRATCH_BYTES bytes that each GPU
+ * holds from the library's load until the process ends; the call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * The first call on a device looks up that device's array address (with
+ * the device current) and clears its control words on `stream`.
+ * Arguments, results and errors are those of moe_layer_forward_ex, plus
+ * MOE_ERR_UNSUPPORTED when the call needs more workspace than the array
+ * holds (moe_workspace_bytes(L, T) > MOE_NOALLOC_SCRATCH_BYTES: e.g. about
+ * 150 tokens of a 256-expert, H = 2048, top-8 layer) and MOE_ERR_HIP when
+ * the array's address cannot be obtained.  Every call on one GPU shares
+ * that GPU's array and leaves its contents behind: calls that overlap on
+ * one GPU (other streams, other host threads) race and must be ordered by
+ * the caller. */
+int moe_layer_forward_noalloc(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y,
+                              const moe_residual *res, int32_t *topk_ids, float *topk_w,
+                              const moe_forward_opts *opts, void *stream);
+
 /* Static text for a status code (host). */
 const char *moe_status_string(int status);
 

@@ -73,6 +73,7 @@ _SIGS = {
     "moe_combine": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _PR, _vp], ctypes.c_int),
     "moe_layer_forward": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_layer_forward_ex": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _PO, _vp], ctypes.c_int),
+    "moe_layer_forward_noalloc": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _PO, _vp], ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 for _name, (_args, _ret) in _SIGS.items():
@@ -262,6 +263,17 @@ def layer_forward(layer: Layer, x_bf16, y, ws, res: MoeResidual | None = None, t
         _check("moe_layer_forward_ex", _lib.moe_layer_forward_ex(
             ctypes.byref(c), _ptr(x_bf16), T, _ptr(y), ctypes.byref(res) if res is not None else None,
             _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), ctypes.byref(opts), _stream(stream)))
+
+
+def layer_forward_noalloc(layer: Layer, x_bf16, y, res: MoeResidual | None = None, topk_ids=None, topk_w=None,
+                          stream=None, c_layer: MoeLayer | None = None, opts: MoeForwardOpts | None = None):
+    """moe_layer_forward_noalloc: the layer with the library's own per-device
+    scratch array as its workspace."""
+    c = layer.c() if c_layer is None else c_layer
+    T = x_bf16.shape[0]
+    _check("moe_layer_forward_noalloc", _lib.moe_layer_forward_noalloc(
+        ctypes.byref(c), _ptr(x_bf16), T, _ptr(y), ctypes.byref(res) if res is not None else None,
+        _ptr(topk_ids), _ptr(topk_w), ctypes.byref(opts) if opts is not None else None, _stream(stream)))
 
 
 def raw_lib():
