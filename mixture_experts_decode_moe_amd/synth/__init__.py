@@ -34,7 +34,7 @@ FMT_INT8_ROW = 1
 FMT_INT4_B32 = 2
 
 # stream ids: one per tensor role, so every tensor is an independent stream
-S_X, S_X_NOISE, S_ROUTER_W, S_ZIPF_PERM = 1, 2, 3, 4
+S_X, S_X_NOISE, S_ROUTER_W, S_ZIPF_PERM, S_SHARED_GATE = 1, 2, 3, 4, 5
 S_GATE_Q, S_GATE_S, S_UP_Q, S_UP_S, S_DOWN_Q, S_DOWN_S = 10, 11, 12, 13, 14, 15
 S_SH_OFFSET = 100  # shared expert streams = routed streams + this
 
@@ -158,6 +158,7 @@ class Shape:
     correlated_sigma: float = 0.0  # > 0: token t>0 = bf16(token 0 + N(0, sigma^2))
     jitter_scales: bool = False  # int8: per-row scale u/(127 sqrt(Kin)), u ~ U[0.5,1.5]
     seed: int = 0
+    shared_gate: bool = False  # a gate row for the shared expert, N(0, 0.02) like the router
 
 
 # The five workloads.  Sizes follow the Qwen3.6-35B-A3B-shaped layer; see
@@ -214,6 +215,7 @@ class LayerHost:
     router_bias: np.ndarray | None  # float32 [E] or None
     routed: ExpertsHost
     shared: ExpertsHost | None = None
+    shared_gate_w: np.ndarray | None = None  # float32 [H] or None
     extras: dict = field(default_factory=dict)
 
 
@@ -272,8 +274,11 @@ def make_layer(shape: Shape, layer: int = 0, jitter=None, routed_range=None) -> 
     shared = None
     if shape.shared_ffn:
         shared = make_experts(shape.fmt, seed, 1, shape.hidden, shape.shared_ffn, shared=True, jitter=jitter)
+    gate = None
+    if shape.shared_gate and shape.shared_ffn:
+        gate = normal_f32(seed, S_SHARED_GATE, shape.hidden, 0.0, 0.02)
     return LayerHost(shape.hidden, shape.n_experts, shape.top_k, shape.renorm, wr, make_router_bias(shape, seed),
-                     routed, shared)
+                     routed, shared, gate)
 
 
 def make_x(shape: Shape, tokens: int | None = None, seed: int | None = None) -> np.ndarray:

@@ -41,7 +41,11 @@ class _Experts(ctypes.Structure):
 class _Layer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
-                ("routed", _Experts), ("shared", ctypes.POINTER(_Experts))]
+                ("routed", _Experts), ("shared", ctypes.POINTER(_Experts)), ("shared_gate_w", ctypes.c_void_p)]
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("tail_skip", ctypes.c_int32), ("act_quant", ctypes.c_int32)]
 
 
 _lib = None
@@ -74,6 +78,11 @@ def lib():
         L.oracle_permute.restype = None
         L.oracle_layer_forward.argtypes = [ctypes.POINTER(_Layer), vp, i32, vp, vp, vp, vp, vp, i32]
         L.oracle_layer_forward.restype = ctypes.c_int
+        L.oracle_layer_forward_ex.argtypes = [ctypes.POINTER(_Layer), vp, i32, vp, ctypes.POINTER(_Opts), vp, vp,
+                                              vp, vp, i32]
+        L.oracle_layer_forward_ex.restype = ctypes.c_int
+        L.oracle_quantize_row.argtypes = [vp, i64, vp, vp]
+        L.oracle_quantize_row.restype = None
         L.oracle_expert_rows.argtypes = [ctypes.POINTER(_Experts), vp, vp, vp, vp, i32, vp, i32]
         L.oracle_expert_rows.restype = ctypes.c_int
         L.oracle_residual.argtypes = [vp, vp, i64, vp]
@@ -113,7 +122,11 @@ def _layer_struct(layer, keep):
         s = _experts_struct(layer.shared, keep)
         keep.append(s)
         sh = ctypes.pointer(s)
-    st = _Layer(layer.hidden, layer.n_experts, layer.top_k, layer.renorm, _p(wr), _p(b), routed, sh)
+    g = None
+    if getattr(layer, "shared_gate_w", None) is not None:
+        g = np.ascontiguousarray(layer.shared_gate_w, np.float32)
+        keep.append(g)
+    st = _Layer(layer.hidden, layer.n_experts, layer.top_k, layer.renorm, _p(wr), _p(b), routed, sh, _p(g))
     keep.append(st)
     return st
 
@@ -191,8 +204,9 @@ def permute(ids, w, E):
                 active=active[:na].copy(), n_active=na)
 
 
-def layer_forward(layer, x_bf16, ids=None, nthreads=0):
-    """Returns y [T][H] float64, ids [T][K], w [T][K], logits [T][E]."""
+def layer_forward(layer, x_bf16, ids=None, nthreads=0, tail_skip=0, act_quant=0):
+    """Returns y [T][H] float64, ids [T][K], w [T][K], logits [T][E].
+    tail_skip / act_quant: the variants of oracle_opts (0 = off)."""
     keep = []
     st = _layer_struct(layer, keep)
     x = np.ascontiguousarray(x_bf16, np.uint16)
@@ -203,11 +217,21 @@ def layer_forward(layer, x_bf16, ids=None, nthreads=0):
     w_out = np.empty((T, K), np.float64)
     logits = np.empty((T, layer.n_experts), np.float64)
     ids_in = None if ids is None else np.ascontiguousarray(ids, np.int32)
-    rc = lib().oracle_layer_forward(ctypes.byref(st), _p(x), T, _p(ids_in), _p(y), _p(ids_out), _p(w_out),
-                                    _p(logits), nthreads)
+    opts = _Opts(int(tail_skip), int(act_quant))
+    rc = lib().oracle_layer_forward_ex(ctypes.byref(st), _p(x), T, _p(ids_in), ctypes.byref(opts), _p(y),
+                                       _p(ids_out), _p(w_out), _p(logits), nthreads)
     if rc != 0:
         raise ValueError("malformed expert weights (int4 nibble 0)")
     return y, ids_out, w_out, logits
+
+
+def quantize_row(v):
+    """Per-row int8 quantisation in float32: returns (q int8 [n], d float32)."""
+    v = np.ascontiguousarray(v, np.float32)
+    q = np.empty(v.shape, np.int8)
+    d = np.zeros(1, np.float32)
+    lib().oracle_quantize_row(_p(v), v.size, _p(q), _p(d))
+    return q, d[0]
 
 
 def expert_rows(experts, x_bf16, offsets, row_tok, row_w, nthreads=0):

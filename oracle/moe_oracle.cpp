@@ -20,6 +20,19 @@
 //  * "Every Public GGUF of This Model Is Missing Its Head", section 5: raw
 //    Q4 nibbles are offset-binary (one XOR with 0x8 per nibble gives the
 //    signed value), i.e. stored as q + 8.
+// Variants (oracle_opts, shared gate):
+//  * "Qwen3.6-35B-A3B: pictures, several requests at once and speed",
+//    Speed (0.1.45): the router and the shared expert's gate are one product
+//    (a gate row beside the router rows); the gate scales the shared
+//    expert's output through a sigmoid.
+//  * "Models and backends", What was tuned, the tail-skip passage and its
+//    table: an expert that every token of a call ranks at place N+1 or later
+//    is left out, and the experts computed keep the router's weights.
+//  * "Strata on an Intel Arc", Arc Pro B70: the fused int8 expert path for
+//    the prompt; "Models and backends", How each backend was checked: the
+//    engines quantise activations to 8 bits at every quantised matrix.  Here
+//    one symmetric scale per row (a token's input, or one expert's SwiGLU
+//    row), every quantiser decision in float32.
 // The remaining steps (softmax router, renormalised top-k weights, SwiGLU
 // experts, weighted combine plus an always-on shared expert, int8 per-row
 // and int4 32-block scaling) are the plain definition of the layer.
@@ -113,8 +126,39 @@ double weight_at(int32_t fmt, const void *q, const void *s, int64_t e, int64_t r
 
 double silu(double g) { return g / (1.0 + std::exp(-g)); }
 
-// out = D (silu(G x) * (U x)) for expert e.  Returns false on a NaN weight.
-bool expert_apply(const oracle_experts &W, int32_t e, const double *x, double *out) {
+double sigmoid(double z) { return 1.0 / (1.0 + std::exp(-z)); }
+
+// Symmetric int8 quantisation of one row in float32 (see the header).
+void quantize_row(const float *v, int64_t n, int8_t *q, float *d) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) amax = std::max(amax, std::fabs(v[i]));
+  if (amax == 0.0f) {
+    for (int64_t i = 0; i < n; ++i) q[i] = 0;
+    *d = 0.0f;
+    return;
+  }
+  const float inv = 127.0f / amax;
+  *d = amax / 127.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    const float p = v[i] * inv;  // one float32 rounding
+    float r = std::nearbyint(p);  // ties to even (the default rounding mode)
+    r = std::min(127.0f, std::max(-127.0f, r));
+    q[i] = static_cast<int8_t>(r);
+  }
+}
+
+// A row after quantisation and back: q * d, exactly, in double.
+void quantize_dequantize(const float *v, int64_t n, double *out) {
+  std::vector<int8_t> q(n);
+  float d = 0.0f;
+  quantize_row(v, n, q.data(), &d);
+  for (int64_t i = 0; i < n; ++i) out[i] = static_cast<double>(q[i]) * static_cast<double>(d);
+}
+
+// out = D (silu(G x) * (U x)) for expert e.  With quant_a the SwiGLU row
+// is rounded to float32 (the precision the GPU holds it in) and quantised
+// per row before the down projection.  Returns false on a NaN weight.
+bool expert_apply(const oracle_experts &W, int32_t e, const double *x, double *out, bool quant_a = false) {
   const int64_t H = W.hidden, F = W.ffn;
   std::vector<double> a(F);
   bool ok = true;
@@ -128,6 +172,11 @@ bool expert_apply(const oracle_experts &W, int32_t e, const double *x, double *o
     }
     if (std::isnan(g) || std::isnan(u)) ok = false;
     a[f] = silu(g) * u;
+  }
+  if (quant_a) {
+    std::vector<float> a32(F);
+    for (int64_t f = 0; f < F; ++f) a32[f] = static_cast<float>(a[f]);
+    quantize_dequantize(a32.data(), F, a.data());
   }
   for (int64_t h = 0; h < H; ++h) {
     double o = 0.0;
@@ -257,16 +306,22 @@ void oracle_permute(const int32_t *ids, const float *w, int32_t T, int32_t K, in
   *n_active = na;
 }
 
-int oracle_layer_forward(const oracle_layer *L, const uint16_t *x_bf16, int32_t T, const int32_t *ids_in,
-                         double *y, int32_t *ids_out, double *w_out, double *logits_out, int32_t nthreads) {
+int oracle_layer_forward_ex(const oracle_layer *L, const uint16_t *x_bf16, int32_t T, const int32_t *ids_in,
+                            const oracle_opts *opts, double *y, int32_t *ids_out, double *w_out, double *logits_out,
+                            int32_t nthreads) {
   const int32_t H = L->hidden, E = L->n_experts, K = L->top_k;
-  std::vector<int> bad(T, 0);
+  const int32_t tail_skip = opts ? opts->tail_skip : 0;
+  const bool act_quant = opts && opts->act_quant;
+  // Routing of every token first: the tail-skip rule looks at the whole call.
+  std::vector<int32_t> ids(static_cast<size_t>(T) * K);
+  std::vector<double> w(static_cast<size_t>(T) * K), gate(T, 1.0);
   parallel_over(T, nthreads, [&](int32_t t) {
-    std::vector<double> x(H), l(E), w(K), o(H), acc(H, 0.0);
-    std::vector<int32_t> ids(K);
+    std::vector<double> x(H), l(E);
+    int32_t *id = ids.data() + static_cast<int64_t>(t) * K;
+    double *wt = w.data() + static_cast<int64_t>(t) * K;
     for (int h = 0; h < H; ++h) x[h] = bf16_value(x_bf16[static_cast<int64_t>(t) * H + h]);
     token_logits(*L, x.data(), l.data());
-    token_select(l.data(), E, K, L->renorm, ids.data(), w.data());
+    token_select(l.data(), E, K, L->renorm, id, wt);
     if (ids_in) {
       // Selection supplied by the caller (a near-tie token may legitimately
       // pick either expert): weights from the logits at the given ids.
@@ -279,30 +334,69 @@ int oracle_layer_forward(const oracle_layer *L, const uint16_t *x_bf16, int32_t 
       else
         for (int32_t e = 0; e < E; ++e) denom += std::exp(l[e] - m);
       for (int32_t k = 0; k < K; ++k) {
-        ids[k] = sel[k];
-        w[k] = std::exp(l[sel[k]] - m) / denom;
+        id[k] = sel[k];
+        wt[k] = std::exp(l[sel[k]] - m) / denom;
       }
     }
-    for (int32_t k = 0; k < K; ++k) {
-      if (!expert_apply(L->routed, ids[k], x.data(), o.data())) bad[t] = 1;
-      for (int h = 0; h < H; ++h) acc[h] += w[k] * o[h];
-    }
-    if (L->shared) {
-      if (!expert_apply(*L->shared, 0, x.data(), o.data())) bad[t] = 1;
-      for (int h = 0; h < H; ++h) acc[h] += o[h];
-    }
-    for (int h = 0; h < H; ++h) y[static_cast<int64_t>(t) * H + h] = acc[h];
-    for (int32_t k = 0; k < K; ++k) {
-      if (ids_out) ids_out[static_cast<int64_t>(t) * K + k] = ids[k];
-      if (w_out) w_out[static_cast<int64_t>(t) * K + k] = w[k];
+    if (L->shared && L->shared_gate_w) {
+      // the shared expert's gate: one more row of the router's product
+      double z = 0.0;
+      for (int h = 0; h < H; ++h) z += static_cast<double>(L->shared_gate_w[h]) * x[h];
+      gate[t] = sigmoid(z);
     }
     if (logits_out)
       for (int32_t e = 0; e < E; ++e) logits_out[static_cast<int64_t>(t) * E + e] = l[e];
+  });
+  // Tail-skip: an expert is kept when some token of the call ranks it among
+  // its first tail_skip picks.
+  std::vector<char> keep(E, 1);
+  if (tail_skip > 0) {
+    std::fill(keep.begin(), keep.end(), 0);
+    for (int32_t t = 0; t < T; ++t)
+      for (int32_t k = 0; k < std::min(tail_skip, K); ++k) keep[ids[static_cast<int64_t>(t) * K + k]] = 1;
+  }
+  std::vector<int> bad(T, 0);
+  parallel_over(T, nthreads, [&](int32_t t) {
+    std::vector<double> x(H), o(H), acc(H, 0.0);
+    for (int h = 0; h < H; ++h) x[h] = bf16_value(x_bf16[static_cast<int64_t>(t) * H + h]);
+    if (act_quant) {
+      // the token's input to every expert, quantised once per row
+      std::vector<float> x32(H);
+      for (int h = 0; h < H; ++h) x32[h] = static_cast<float>(x[h]);  // exact: x is bf16
+      quantize_dequantize(x32.data(), H, x.data());
+    }
+    for (int32_t k = 0; k < K; ++k) {
+      const int32_t e = ids[static_cast<int64_t>(t) * K + k];
+      if (!keep[e]) continue;
+      if (!expert_apply(L->routed, e, x.data(), o.data(), act_quant)) bad[t] = 1;
+      const double wk = w[static_cast<int64_t>(t) * K + k];
+      for (int h = 0; h < H; ++h) acc[h] += wk * o[h];
+    }
+    if (L->shared) {
+      if (!expert_apply(*L->shared, 0, x.data(), o.data(), act_quant)) bad[t] = 1;
+      if (L->shared_gate_w) {
+        for (int h = 0; h < H; ++h) acc[h] += gate[t] * o[h];
+      } else {
+        for (int h = 0; h < H; ++h) acc[h] += o[h];
+      }
+    }
+    for (int h = 0; h < H; ++h) y[static_cast<int64_t>(t) * H + h] = acc[h];
+    for (int32_t k = 0; k < K; ++k) {
+      if (ids_out) ids_out[static_cast<int64_t>(t) * K + k] = ids[static_cast<int64_t>(t) * K + k];
+      if (w_out) w_out[static_cast<int64_t>(t) * K + k] = w[static_cast<int64_t>(t) * K + k];
+    }
   });
   for (int32_t t = 0; t < T; ++t)
     if (bad[t]) return -1;
   return 0;
 }
+
+int oracle_layer_forward(const oracle_layer *L, const uint16_t *x_bf16, int32_t T, const int32_t *ids_in,
+                         double *y, int32_t *ids_out, double *w_out, double *logits_out, int32_t nthreads) {
+  return oracle_layer_forward_ex(L, x_bf16, T, ids_in, nullptr, y, ids_out, w_out, logits_out, nthreads);
+}
+
+void oracle_quantize_row(const float *v, int64_t n, int8_t *q, float *d) { quantize_row(v, n, q, d); }
 
 int oracle_expert_rows(const oracle_experts *W, const uint16_t *x_bf16, const int32_t *offsets,
                        const int32_t *row_tok, const float *row_w, int32_t n_rows, double *rows_out,

@@ -40,7 +40,22 @@ typedef struct {
   const float *router_bias; /* float32 [E] or NULL */
   oracle_experts routed;
   const oracle_experts *shared; /* NULL: no shared expert */
+  /* float32 [H] or NULL: the shared expert's gate row; its output is then
+   * scaled by sigmoid(sum_h g[h] x[h]) instead of 1 */
+  const float *shared_gate_w;
 } oracle_layer;
+
+/* Variants of a layer call (all zero = the plain layer). */
+typedef struct {
+  /* 0: off.  N > 0: an expert that no token of the call ranks among its
+   * first N picks is not computed; the others keep their router weights
+   * (no renormalisation). */
+  int32_t tail_skip;
+  /* 0: bf16 activations as given.  1: the input of every expert's gate/up
+   * and of its down projection is first quantised per row to int8 with
+   * oracle_quantize_row (the W8A8 variant). */
+  int32_t act_quant;
+} oracle_opts;
 
 /* IEEE decoders written from the bit layouts. */
 double oracle_bf16_to_double(uint16_t bits);
@@ -77,6 +92,16 @@ void oracle_permute(const int32_t *ids, const float *w, int32_t T, int32_t K, in
  * on malformed weights. */
 int oracle_layer_forward(const oracle_layer *L, const uint16_t *x_bf16, int32_t T, const int32_t *ids_in,
                          double *y, int32_t *ids_out, double *w_out, double *logits_out, int32_t nthreads);
+/* oracle_layer_forward with the variants of `opts` (NULL = none). */
+int oracle_layer_forward_ex(const oracle_layer *L, const uint16_t *x_bf16, int32_t T, const int32_t *ids_in,
+                            const oracle_opts *opts, double *y, int32_t *ids_out, double *w_out, double *logits_out,
+                            int32_t nthreads);
+/* Per-row symmetric int8 quantisation, every step in float32 (the
+ * precision the GPU takes the same decisions in): amax = max |v|; amax = 0
+ * gives q = 0, d = 0; else inv = 127 / amax, d = amax / 127 (each one
+ * correctly rounded division) and q[i] = round-half-even(v[i] * inv) (one
+ * rounded product), clamped to [-127, 127].  The row is then q * d. */
+void oracle_quantize_row(const float *v, int64_t n, int8_t *q, float *d);
 /* rows_out[r] = row_w[r] * o_e(x_{row_tok[r]}) for the expert e whose
  * offsets range holds r (row_w NULL: weight 1; row_tok NULL: r). */
 int oracle_expert_rows(const oracle_experts *W, const uint16_t *x_bf16, const int32_t *offsets,

@@ -399,3 +399,221 @@ def test_rmsnorm_closed_forms():
         np.float64)) or np.allclose(f[2], np.r_[np.full(H // 2, 0.2), np.full(H // 2, 1.4)], rtol=2 ** -8)
     out_eps = oracle.rmsnorm(r[:1], eps=7.0)  # 3 / sqrt(9 + 7) = 0.75 exactly
     assert np.all(bf16_bits_to_f64(out_eps) == 0.75)
+
+
+# ----------------------------------------------------------- variants
+# The shared expert's sigmoid gate ("Qwen3.6-35B-A3B: pictures, several
+# requests at once and speed", Speed (0.1.45)), tail-skip ("Models and
+# backends", What was tuned) and int8 activations (the W8A8 variant, "Strata
+# on an Intel Arc", Arc Pro B70: the fused int8 expert path for the prompt).
+
+def np_quantize_row(v):
+    """Independent numpy float32 statement of the per-row quantiser."""
+    v = np.asarray(v, np.float32)
+    amax = np.float32(np.max(np.abs(v))) if v.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(v.shape, np.int8), np.float32(0)
+    inv = np.float32(127) / amax
+    d = amax / np.float32(127)
+    q = np.clip(np.rint(v * inv), -127, 127).astype(np.int8)  # v * inv in float32, rint ties to even
+    return q, d
+
+
+def dense_forward_variant(layer, x_bits, tail_skip=0, act_quant=0):
+    """Every expert on every token in numpy float64 (independent of the
+    oracle), then the top-k mask, the tail-skip rule over the whole call and
+    the shared gate; with act_quant the inputs of the gate/up and down
+    products are quantised per row with np_quantize_row."""
+    x = bf16_bits_to_f64(x_bits)
+    T = x.shape[0]
+    l = x @ layer.router_w.astype(np.float64).T
+    if layer.router_bias is not None:
+        l = l + layer.router_bias.astype(np.float64)[None, :]
+    E, K = l.shape[1], layer.top_k
+    sel = np.stack([np.lexsort((np.arange(E), -l[t]))[:K] for t in range(T)])
+    keep = np.ones(E, bool)
+    if tail_skip > 0:
+        keep[:] = False
+        keep[np.unique(sel[:, :tail_skip])] = True
+
+    def qd(v):
+        q, d = np_quantize_row(v.astype(np.float32))
+        return q.astype(np.float64) * np.float64(d)
+
+    def expert(ex, e, xt):
+        G, U, D = (np_dequant(ex, r)[e] for r in ("gate", "up", "down"))
+        xi = qd(xt) if act_quant else xt
+        g, u = G @ xi, U @ xi
+        a = g / (1.0 + np.exp(-g)) * u
+        if act_quant:
+            a = qd(a)
+        return D @ a
+
+    y = np.zeros((T, layer.hidden))
+    for t in range(T):
+        lv = l[t, sel[t]]
+        w = np.exp(lv - lv[0])
+        w /= w.sum()
+        for k in range(K):
+            if keep[sel[t, k]]:
+                y[t] += w[k] * expert(layer.routed, sel[t, k], x[t])
+        if layer.shared is not None:
+            gate = 1.0
+            if layer.shared_gate_w is not None:
+                gate = 1.0 / (1.0 + np.exp(-(x[t] @ layer.shared_gate_w.astype(np.float64))))
+            y[t] += gate * expert(layer.shared, 0, x[t])
+    return y, sel, keep
+
+
+def test_quantizer_hand_cases():
+    g = json.load(open(os.path.join(GOLDEN, "int8_row_quant_cases.json")))
+    for c in g["cases"]:
+        q, d = oracle.quantize_row(np.array(c["v"], np.float32))
+        assert q.tolist() == c["q"], c["note"]
+        assert d == np.float32(c["d_num"]) / np.float32(c["d_den"]), c["note"]
+
+
+def test_quantizer_against_numpy_and_invariants():
+    rng = np.random.default_rng(21)
+    for n, scale in ((2048, 1.0), (512, 3e-3), (33, 250.0), (7, 1e-30)):
+        for _ in range(20):
+            v = (rng.standard_normal(n) * scale).astype(np.float32)
+            q, d = oracle.quantize_row(v)
+            qn, dn = np_quantize_row(v)
+            assert np.array_equal(q, qn) and d == dn
+            i = int(np.argmax(np.abs(v)))
+            assert abs(int(q[i])) == 127 and np.sign(q[i]) == np.sign(v[i])
+            assert np.all(np.abs(q.astype(np.float64) * d - v) <= 0.5 * d * (1 + 2.0 ** -20))
+            # a power-of-two rescale changes the scale, never the codes
+            q2, d2 = oracle.quantize_row(v * np.float32(4.0))
+            assert np.array_equal(q2, q) and d2 == d * 4
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_INT8_ROW, synth.FMT_INT4_B32])
+def test_w8a8_variant_dense_brute_force(fmt):
+    shape, layer = tiny_layer(fmt, 96, 64, 12, 3, shared_F=32, bias=True)
+    x = synth.normal_bf16(31, 1, 5 * 96).reshape(5, 96)
+    y, ids, w, _ = oracle.layer_forward(layer, x, act_quant=1)
+    yd, sel, _ = dense_forward_variant(layer, x, act_quant=1)
+    assert np.array_equal(ids, sel)
+    assert rel_err(y, yd) <= 1e-12
+    # the quantisation is visible against the exact layer, at the size an
+    # 8-bit grid implies (about 1% of the output scale, never 0)
+    y0, _, _, _ = oracle.layer_forward(layer, x)
+    assert 1e-4 < rel_err(y, y0) < 5e-2
+
+
+def test_w8a8_variant_is_exact_on_the_int8_grid_input():
+    """When x already lies on its int8 grid (integers with max |x| = 127),
+    quantising it changes nothing: the gate/up products equal the exact
+    layer's, so the variant differs only through the SwiGLU row's grid."""
+    shape, layer = tiny_layer(synth.FMT_INT8_ROW, 64, 32, 6, 2, shared_F=0)
+    rng = np.random.default_rng(3)
+    xi = rng.integers(-127, 128, size=(2, 64)).astype(np.float64)
+    xi[:, 0] = 127
+    x = synth.f64_to_bf16(xi)
+    q, d = oracle.quantize_row(bf16_bits_to_f64(x[0]).astype(np.float32))
+    assert d == 1.0 and np.array_equal(q.astype(np.float64), xi[0])
+    y, _, _, _ = oracle.layer_forward(layer, x, act_quant=1)
+    yd, _, _ = dense_forward_variant(layer, x, act_quant=1)
+    assert rel_err(y, yd) <= 1e-12
+
+
+@pytest.mark.parametrize("N", [1, 2, 3])
+def test_tail_skip_dense_brute_force(N):
+    """Config 0 (4 tokens, top-4 of 64): the experts computed are those some
+    token ranks among its first N; the others are left out and nothing is
+    renormalised."""
+    shape = synth.CONFIGS[0]
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    y, ids, w, _ = oracle.layer_forward(layer, x, tail_skip=N)
+    yd, sel, keep = dense_forward_variant(layer, x, tail_skip=N)
+    assert np.array_equal(ids, sel)
+    assert rel_err(y, yd) <= 1e-12
+    # the weights stay the router's (they still sum to 1 over all K slots)
+    assert np.all(np.abs(w.sum(axis=1) - 1) <= 1e-12)
+    dropped = ~keep[sel]
+    assert dropped.any(), "the case should leave some slot out"
+    assert not dropped[:, :N].any()
+
+
+def test_tail_skip_keeps_a_late_slot_another_token_ranks_early():
+    """Tail-skip looks at the whole call: a token's 4th pick is computed when
+    another token of the call ranks that expert first, and left out when the
+    token is alone."""
+    shape = synth.CONFIGS[0]
+    layer = synth.make_layer(shape)
+    found = False
+    for seed in range(200):
+        x = synth.make_x(shape, seed=1000 + seed)
+        l = bf16_bits_to_f64(x) @ layer.router_w.astype(np.float64).T
+        sel = np.stack([np.lexsort((np.arange(shape.n_experts), -l[t]))[:shape.top_k] for t in range(4)])
+        first = set(sel[:, 0].tolist())
+        late = [(t, k) for t in range(4) for k in range(1, 4) if sel[t, k] in first]
+        if late:
+            t, k = late[0]
+            found = True
+            break
+    assert found
+    y_call, _, _, _ = oracle.layer_forward(layer, x, tail_skip=1)
+    y_alone, _, _, _ = oracle.layer_forward(layer, x[t:t + 1], tail_skip=1)
+    y_plain, _, _, _ = oracle.layer_forward(layer, x[t:t + 1])
+    assert rel_err(y_call[t], y_alone[0]) > 1e-6  # the call kept slot k, the lone token did not
+    yd, _, _ = dense_forward_variant(layer, x, tail_skip=1)
+    assert rel_err(y_call, yd) <= 1e-12
+    del y_plain
+
+
+def test_tail_skip_at_or_beyond_k_is_the_plain_layer():
+    shape = synth.CONFIGS[0]
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    y0, _, _, _ = oracle.layer_forward(layer, x)
+    for N in (shape.top_k, shape.top_k + 3):
+        y, _, _, _ = oracle.layer_forward(layer, x, tail_skip=N)
+        assert np.array_equal(y, y0)
+
+
+def _gated_pair(gate_w, x=None):
+    shape, layer = tiny_layer(synth.FMT_INT4_B32, 64, 32, 6, 2, shared_F=32)
+    if x is None:
+        x = synth.normal_bf16(41, 1, 3 * 64).reshape(3, 64)
+    y_plain, _, _, _ = oracle.layer_forward(layer, x)
+    no_shared = LayerHost(layer.hidden, layer.n_experts, layer.top_k, layer.renorm, layer.router_w,
+                          layer.router_bias, layer.routed, None)
+    y_routed, _, _, _ = oracle.layer_forward(no_shared, x)
+    layer.shared_gate_w = None if gate_w is None else np.asarray(gate_w(x), np.float32)
+    y_gated, _, _, _ = oracle.layer_forward(layer, x)
+    return layer, x, y_plain, y_routed, y_gated
+
+
+def test_shared_gate_zero_row_halves_the_shared_expert():
+    _, _, y_plain, y_routed, y_gated = _gated_pair(lambda x: np.zeros(64))
+    assert rel_err(y_gated, 0.5 * (y_plain + y_routed)) <= 1e-12
+
+
+def test_shared_gate_saturates_to_on_and_off():
+    """A gate row along token 0's own input gives a logit of +-|x|^2 / 2
+    (about 30): the gate is 1 (or 0) to double precision, i.e. the plain
+    layer (or the routed experts alone)."""
+    _, x, y_plain, y_routed, y_on = _gated_pair(lambda x: 0.5 * bf16_bits_to_f64(x[0]))
+    assert rel_err(y_on[0], y_plain[0]) <= 1e-12
+    _, _, _, _, y_off = _gated_pair(lambda x: -0.5 * bf16_bits_to_f64(x[0]))
+    assert rel_err(y_off[0], y_routed[0]) <= 1e-12
+
+
+def test_shared_gate_three_quarters():
+    """A gate logit of ln 3 (a row along the token's input scaled to it)
+    gives sigmoid = 3/4: y = routed + 3/4 shared = (y_routed + 3 y_plain)/4.
+    A sign slip (sigmoid(-z) = 1/4) fails."""
+    def row(x):
+        xf = bf16_bits_to_f64(x[1])
+        return xf * (math.log(3.0) / float(xf @ xf))
+    _, _, y_plain, y_routed, y_g = _gated_pair(row)
+    assert rel_err(y_g[1], 0.25 * y_routed[1] + 0.75 * y_plain[1]) <= 1e-6
+    shape, layer = tiny_layer(synth.FMT_INT4_B32, 64, 32, 6, 2, shared_F=32)
+    x = synth.normal_bf16(41, 1, 3 * 64).reshape(3, 64)
+    layer.shared_gate_w = np.asarray(row(x), np.float32)
+    yd, _, _ = dense_forward_variant(layer, x)
+    assert rel_err(y_g, yd) <= 1e-12
