@@ -79,7 +79,12 @@ typedef struct moe_experts {
  * added to the logits before selection and softmax).  renorm = 1: the k
  * weights are a softmax over the k selected logits (softmax over all E then
  * renormalised); renorm = 0: the full softmax's values at the selected
- * experts. */
+ * experts.  shared_gate_w (float32 [hidden], 16-byte aligned, or NULL;
+ * requires a shared expert): the shared expert's gate row.  Its product
+ * with x is formed with the router's ("Qwen3.6-35B-A3B: pictures, several
+ * requests at once and speed", Speed (0.1.45): the router and the shared
+ * gate in one product) and the shared expert's output is scaled by its
+ * sigmoid; NULL adds the shared expert with weight 1. */
 typedef struct moe_layer {
   int32_t hidden;    /* H */
   int32_t n_experts; /* E */
@@ -89,6 +94,7 @@ typedef struct moe_layer {
   const float *router_bias; /* [E] or NULL */
   moe_experts routed;       /* n_experts == E */
   moe_experts shared;       /* n_experts == 1, or 0 for no shared expert */
+  const float *shared_gate_w; /* [H] or NULL */
 } moe_layer;
 
 /* Residual epilogue of a layer stack (host struct).  residual_out =
@@ -128,9 +134,10 @@ size_t moe_route_workspace_bytes(const moe_layer *L, int32_t T);
  * want them: they then pass through `ws`, which must hold
  * moe_route_workspace_bytes(L, T) bytes (ws is unused when logits is given
  * and may be NULL).  MOE_ERR_WORKSPACE if logits is NULL and ws is missing
- * or too small. */
+ * or too small.  shared_gate float [T] or NULL: with L->shared_gate_w it
+ * receives sigmoid(shared_gate_w . x[t]) per token. */
 int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *topk_ids, float *topk_w,
-              float *logits, void *ws, size_t ws_bytes, void *stream);
+              float *logits, float *shared_gate, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes moe_permute needs for T tokens, K slots, E experts. */
 size_t moe_permute_workspace_bytes(int32_t T, int32_t K, int32_t E);
@@ -171,13 +178,14 @@ int moe_expert_ffn(const moe_experts *W, int32_t hidden, const uint16_t *x_bf16,
  * 1024 threads, and add+norm of the residual in one launch; "Models and
  * backends", What was tuned: one launch adds up a call's experts).
  * y[t][h] = sum_{k<K} rows_out[inv_pos[t][k]][h] (k in order, each row
- * already scaled by its routing weight) + shared_out[t][h]; slots with
- * inv_pos < 0 are skipped.  rows_out float [*][H] (16-byte aligned);
- * inv_pos int32 [T][K]; shared_out float [T][H] or NULL; y float [T][H];
- * res (host) or NULL: the residual epilogue above.  H a multiple of 256 up
- * to 8192, K <= 64. */
+ * already scaled by its routing weight) + g[t] * shared_out[t][h] (one
+ * fused multiply-add; g[t] = shared_gate[t], or 1 when shared_gate is
+ * NULL); slots with inv_pos < 0 are skipped.  rows_out float [*][H]
+ * (16-byte aligned); inv_pos int32 [T][K]; shared_out float [T][H] or NULL;
+ * shared_gate float [T] or NULL; y float [T][H]; res (host) or NULL: the
+ * residual epilogue above.  H a multiple of 256 up to 8192, K <= 64. */
 int moe_combine(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_t K, int32_t H,
-                const float *shared_out, float *y, const moe_residual *res, void *stream);
+                const float *shared_out, const float *shared_gate, float *y, const moe_residual *res, void *stream);
 
 /* Stages of a layer call, for per-call profiling events. */
 enum { MOE_STAGE_NONE = 0, MOE_STAGE_ROUTE = 1, MOE_STAGE_PERMUTE = 2, MOE_STAGE_GATEUP = 3,
@@ -196,7 +204,14 @@ typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } mo
  * defaults of moe_layer_forward). */
 typedef struct moe_forward_opts {
   int32_t path;        /* moe_path */
-  int32_t reserved[3]; /* must be 0 */
+  /* Tail-skip ("Models and backends", What was tuned: --tail-skip N): 0 =
+   * off; N > 0: on a decode batch (T <= 16, not forced to the prefill
+   * family) an expert that no token of the call ranks among its first N
+   * picks is not computed, and the experts computed keep the weights the
+   * router gave them (no renormalisation).  An approximation: it changes
+   * the output.  Prompt batches are left untouched, as on the pages. */
+  int32_t tail_skip;
+  int32_t reserved[2]; /* must be 0 */
   /* Profiling: hipEvent_t pairs (created by the caller) recorded on the
    * call's stream around each stage: index MOE_STAGE_*; a stage is profiled
    * when both of its events are non-NULL.  The gate/up and down stages'
@@ -231,7 +246,8 @@ int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, flo
                       int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
 /* moe_layer_forward with per-call options (opts NULL = defaults).
- * MOE_ERR_INVALID_ARG for an unknown path or nonzero reserved words. */
+ * MOE_ERR_INVALID_ARG for an unknown path, a negative tail_skip or nonzero
+ * reserved words. */
 int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
                          int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, const moe_forward_opts *opts,
                          void *stream);

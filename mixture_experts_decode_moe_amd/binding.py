@@ -46,14 +46,14 @@ PATHS = {"auto": MOE_PATH_AUTO, "decode": MOE_PATH_DECODE, "prefill": MOE_PATH_P
 
 
 class MoeForwardOpts(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+    _fields_ = [("path", ctypes.c_int32), ("tail_skip", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
                 ("stage_start", ctypes.c_void_p * MOE_N_STAGES), ("stage_stop", ctypes.c_void_p * MOE_N_STAGES)]
 
 
 class MoeLayer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
-                ("routed", MoeExperts), ("shared", MoeExperts)]
+                ("routed", MoeExperts), ("shared", MoeExperts), ("shared_gate_w", ctypes.c_void_p)]
 
 
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -65,12 +65,12 @@ _SIGS = {
     "moe_workspace_bytes": ([_PL, _i32], _sz),
     "moe_workspace_init": ([_vp, _sz, _vp], ctypes.c_int),
     "moe_route_workspace_bytes": ([_PL, _i32], _sz),
-    "moe_route": ([_PL, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe_route": ([_PL, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_permute_workspace_bytes": ([_i32, _i32, _i32], _sz),
     "moe_permute": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_expert_ffn_workspace_bytes": ([_i32, _i32], _sz),
     "moe_expert_ffn": ([_PE, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
-    "moe_combine": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _PR, _vp], ctypes.c_int),
+    "moe_combine": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _PR, _vp], ctypes.c_int),
     "moe_layer_forward": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_layer_forward_ex": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _PO, _vp], ctypes.c_int),
     "moe_layer_forward_noalloc": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _PO, _vp], ctypes.c_int),
@@ -146,11 +146,12 @@ class Layer:
     router_bias: torch.Tensor | None
     routed: Experts
     shared: Experts | None = None
+    shared_gate_w: torch.Tensor | None = None
 
     def c(self) -> MoeLayer:
         sh = self.shared.c() if self.shared is not None else MoeExperts()
         return MoeLayer(self.hidden, self.n_experts, self.top_k, self.renorm, _ptr(self.router_w),
-                        _ptr(self.router_bias), self.routed.c(), sh)
+                        _ptr(self.router_bias), self.routed.c(), sh, _ptr(self.shared_gate_w))
 
 
 def experts_to_device(ex, device="cuda") -> Experts:
@@ -165,9 +166,11 @@ def experts_to_device(ex, device="cuda") -> Experts:
 
 def layer_to_device(layer, device="cuda") -> Layer:
     bias = None if layer.router_bias is None else torch.from_numpy(layer.router_bias).to(device)
+    gate = getattr(layer, "shared_gate_w", None)
     return Layer(layer.hidden, layer.n_experts, layer.top_k, layer.renorm,
                  torch.from_numpy(layer.router_w).to(device), bias, experts_to_device(layer.routed, device),
-                 None if layer.shared is None else experts_to_device(layer.shared, device))
+                 None if layer.shared is None else experts_to_device(layer.shared, device),
+                 None if gate is None else torch.from_numpy(gate).to(device))
 
 
 # ------------------------------------------------------------ entry points
@@ -191,12 +194,15 @@ def route_workspace_bytes(layer: Layer, T: int) -> int:
     return int(_lib.moe_route_workspace_bytes(ctypes.byref(c), T))
 
 
-def route(layer: Layer, x_bf16: torch.Tensor, topk_ids, topk_w, logits=None, ws=None, stream=None):
-    """Router + top-k.  logits None: they pass through ws (see moe_route)."""
+def route(layer: Layer, x_bf16: torch.Tensor, topk_ids, topk_w, logits=None, ws=None, stream=None,
+          shared_gate=None):
+    """Router + top-k (+ the shared gate's sigmoid into shared_gate [T]).
+    logits None: they pass through ws (see moe_route)."""
     c = layer.c()
     T = x_bf16.shape[0]
     _check("moe_route", _lib.moe_route(ctypes.byref(c), _ptr(x_bf16), T, _ptr(topk_ids), _ptr(topk_w),
-                                       _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+                                       _ptr(logits), _ptr(shared_gate), _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(stream)))
 
 
 def permute(topk_ids, topk_w, E: int, out: dict, ws: torch.Tensor, stream=None):
@@ -231,20 +237,23 @@ def residual(residual_in, residual_out, normed_out=None, eps=1e-6) -> MoeResidua
 
 
 def combine(rows_out, inv_pos, T: int, K: int, H: int, shared_out, y, res: MoeResidual | None = None,
-            stream=None):
-    _check("moe_combine", _lib.moe_combine(_ptr(rows_out), _ptr(inv_pos), T, K, H, _ptr(shared_out), _ptr(y),
+            stream=None, shared_gate=None):
+    _check("moe_combine", _lib.moe_combine(_ptr(rows_out), _ptr(inv_pos), T, K, H, _ptr(shared_out),
+                                           _ptr(shared_gate), _ptr(y),
                                            ctypes.byref(res) if res is not None else None, _stream(stream)))
 
 
 STAGES = {"route": 1, "permute": 2, "gateup": 3, "down": 4, "shared": 5, "combine": 6}
 
 
-def forward_opts(path="auto", events=None) -> MoeForwardOpts:
-    """Per-call options: path "auto" | "decode" | "prefill"; events a dict
-    stage name -> (start, stop) torch.cuda.Event pairs (already created, e.g.
-    by one record) that the call records around that stage."""
+def forward_opts(path="auto", events=None, tail_skip=0) -> MoeForwardOpts:
+    """Per-call options: path "auto" | "decode" | "prefill"; tail_skip N (0 =
+    off); events a dict stage name -> (start, stop) torch.cuda.Event pairs
+    (already created, e.g. by one record) that the call records around that
+    stage."""
     o = MoeForwardOpts()
     o.path = PATHS[path]
+    o.tail_skip = int(tail_skip)
     for name, (a, b) in (events or {}).items():
         o.stage_start[STAGES[name]] = a.cuda_event
         o.stage_stop[STAGES[name]] = b.cuda_event

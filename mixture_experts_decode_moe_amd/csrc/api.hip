@@ -48,8 +48,16 @@ int check_layer(const moe_layer *L) {
   if (!L->router_w || !aligned(L->router_w, 16)) return MOE_ERR_INVALID_ARG;
   int rc = check_experts(L->routed, L->hidden, true, L->n_experts);
   if (rc != MOE_OK) return rc;
-  return check_experts(L->shared, L->hidden, false, 1);
+  rc = check_experts(L->shared, L->hidden, false, 1);
+  if (rc != MOE_OK) return rc;
+  // a gate row needs the shared expert it gates, and whole 16-byte rows
+  if (L->shared_gate_w && (L->shared.n_experts != 1 || !aligned(L->shared_gate_w, 16))) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
 }
+
+// Partial-logit rows of the decode routing: the experts, plus the shared
+// gate row when there is one.
+int32_t router_rows(const moe_layer *L) { return L->n_experts + (L->shared_gate_w ? 1 : 0); }
 
 constexpr size_t kControlBytes = 256;  // control words kept zero between calls
 
@@ -102,6 +110,7 @@ struct LayerWs {
   float *row_w;
   float *act, *rows_out;
   uint16_t *x16;  // x in fp16 for the prefill GEMMs, written by the router GEMM
+  float *gate;    // [T]: the shared expert's gate values
   size_t bytes;
 };
 
@@ -114,7 +123,7 @@ LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
   const size_t n_tiles = (TK + kPermuteTile - 1) / kPermuteTile;
   const size_t S = static_cast<size_t>(L->hidden / route_fused_slice(L->hidden));
   // sized for min(T, kFusedTokens) tokens so that the total grows with T
-  w.part = c.take<float>(S * static_cast<size_t>(T < kFusedTokens ? T : kFusedTokens) * E);
+  w.part = c.take<float>(S * static_cast<size_t>(T < kFusedTokens ? T : kFusedTokens) * router_rows(L));
   w.logits = c.take<float>(static_cast<size_t>(T) * E);
   w.ids = c.take<int32_t>(TK);
   w.w = c.take<float>(TK);
@@ -134,6 +143,7 @@ LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
   w.act = c.take<float>(TK * L->routed.ffn + static_cast<size_t>(T) * Fs);
   w.rows_out = c.take<float>((TK + (Fs ? T : 0)) * L->hidden);
   w.x16 = c.take<uint16_t>(static_cast<size_t>(T) * L->hidden);
+  w.gate = c.take<float>(T);
   w.bytes = align_up(c.off, 256);
   return w;
 }
@@ -203,7 +213,7 @@ size_t moe_route_workspace_bytes(const moe_layer *L, int32_t T) {
 }
 
 int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *topk_ids, float *topk_w, float *logits,
-              void *ws, size_t ws_bytes, void *stream) {
+              float *shared_gate, void *ws, size_t ws_bytes, void *stream) {
   int rc = check_layer(L);
   if (rc != MOE_OK) return rc;
   if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -214,8 +224,9 @@ int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *to
     if (!ws || !aligned(ws, 16) || ws_bytes < moe_route_workspace_bytes(L, T)) return MOE_ERR_WORKSPACE;
     logits = static_cast<float *>(ws);
   }
+  const bool gate = L->shared_gate_w && shared_gate;
   RouteArgs a{L->router_w, L->router_bias, x_bf16, T, L->hidden, L->n_experts, L->top_k, L->renorm, logits,
-              topk_ids, topk_w, nullptr, kPathAuto};
+              topk_ids, topk_w, nullptr, kPathAuto, gate ? L->shared_gate_w : nullptr, gate ? shared_gate : nullptr};
   hipError_t e = launch_router_logits(a, as_stream(stream));
   if (e == hipSuccess) e = launch_topk(a, as_stream(stream));
   return hip_status(e);
@@ -313,8 +324,9 @@ int check_residual(const moe_residual *res, int32_t H) {
 }
 
 CombineArgs combine_args(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_t K, int32_t H,
-                         const float *shared_out, float *y, const moe_residual *res) {
-  CombineArgs a{rows_out, inv_pos, T, K, H, shared_out, y, nullptr, nullptr, nullptr, 0.f};
+                         const float *shared_out, const float *shared_gate, float *y, const moe_residual *res) {
+  CombineArgs a{rows_out, inv_pos, T, K, H, shared_out, shared_out ? shared_gate : nullptr, y, nullptr, nullptr,
+                nullptr, 0.f};
   if (res) {
     a.residual_in = res->residual_in;
     a.residual_out = res->residual_out;
@@ -326,7 +338,7 @@ CombineArgs combine_args(const float *rows_out, const int32_t *inv_pos, int32_t 
 }  // namespace
 
 int moe_combine(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_t K, int32_t H,
-                const float *shared_out, float *y, const moe_residual *res, void *stream) {
+                const float *shared_out, const float *shared_gate, float *y, const moe_residual *res, void *stream) {
   if (T < 0 || K <= 0 || H <= 0 || H % 256 || H > 8192) return MOE_ERR_INVALID_ARG;
   if (K > 64) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
@@ -335,7 +347,8 @@ int moe_combine(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_
     return MOE_ERR_INVALID_ARG;
   int rc = check_residual(res, H);
   if (rc != MOE_OK) return rc;
-  return hip_status(launch_combine(combine_args(rows_out, inv_pos, T, K, H, shared_out, y, res), as_stream(stream)));
+  return hip_status(
+      launch_combine(combine_args(rows_out, inv_pos, T, K, H, shared_out, shared_gate, y, res), as_stream(stream)));
 }
 
 int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
@@ -345,7 +358,8 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
   if (rc != MOE_OK) return rc;
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (opts) {
-    if (opts->path < MOE_PATH_AUTO || opts->path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
+    if (opts->path < MOE_PATH_AUTO || opts->path > MOE_PATH_PREFILL || opts->tail_skip < 0)
+      return MOE_ERR_INVALID_ARG;
     for (int32_t r : opts->reserved)
       if (r != 0) return MOE_ERR_INVALID_ARG;
   }
@@ -415,13 +429,19 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
     fa.n_active = w.n_active;
     fa.row_w = w.row_w;
     fa.units = w.units;
+    fa.gate_w = L->shared_gate_w;
+    fa.gate = w.gate;
+    fa.Ep = router_rows(L);
+    fa.tail_skip = opts ? opts->tail_skip : 0;
     xa.route_here = (mfma_decode_ok(xa) && E <= 256) ? 1 : 0;
     if (xa.route_here) xa.units = w.units;  // published by the gate/up kernel's routing
     xa.route = fa;
     StageMark m(ev, MOE_STAGE_ROUTE, s);
     e = xa.route_here ? launch_route_partial(fa, s) : launch_route_fused(fa, s);
   } else {
-    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw, w.x16, path};
+    // (prompt batches: tail-skip leaves them untouched)
+    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw, w.x16, path,
+                 L->shared_gate_w, w.gate};
     if (router_writes_x16(ra)) {
       xa.x16 = w.x16;
       xa.queue = w.control;
@@ -463,7 +483,7 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
     // stage's events bracket it; the combine stage has no launch of its own)
     xa.ev = ev.of(MOE_STAGE_DOWN);
     DownCombineArgs d{xa, w.units, w.inv_pos, K, E, y, res ? res->residual_in : nullptr,
-                      res ? res->residual_out : nullptr};
+                      res ? res->residual_out : nullptr, L->shared_gate_w ? w.gate : nullptr};
     return hip_status(launch_down_combine(d, s));
   }
   {
@@ -474,7 +494,8 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   CombineArgs ca = combine_args(w.rows_out, w.inv_pos, T, K, H,
-                                has_shared ? w.rows_out + static_cast<size_t>(TK) * H : nullptr, y, res);
+                                has_shared ? w.rows_out + static_cast<size_t>(TK) * H : nullptr,
+                                L->shared_gate_w ? w.gate : nullptr, y, res);
   StageMark m(ev, MOE_STAGE_COMBINE, s);
   return hip_status(launch_combine(ca, s));
 }

@@ -58,7 +58,19 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
       }
     }
     const size_t o4 = static_cast<size_t>(t) * n4 + c;
-    if (a.shared_out) add4(acc, reinterpret_cast<const float4 *>(a.shared_out)[o4]);
+    if (a.shared_out) {
+      const float4 sv = reinterpret_cast<const float4 *>(a.shared_out)[o4];
+      if (a.shared_gate) {
+        // the shared expert's row scaled by its gate, fused into the sum
+        const float g = a.shared_gate[t];
+        acc.x = fmaf(g, sv.x, acc.x);
+        acc.y = fmaf(g, sv.y, acc.y);
+        acc.z = fmaf(g, sv.z, acc.z);
+        acc.w = fmaf(g, sv.w, acc.w);
+      } else {
+        add4(acc, sv);
+      }
+    }
     reinterpret_cast<float4 *>(a.y)[o4] = acc;
     if (a.residual_out) {
       const uint2 xv = reinterpret_cast<const uint2 *>(a.residual_in)[o4];

@@ -107,6 +107,8 @@ struct RouteArgs {
   float *w;
   uint16_t *x16;  // optional [T][H]: x in fp16, pair-permuted 8-element pieces
   int32_t path;   // PathSel: kPathPrefill takes the matrix-core router GEMM at any T
+  const float *gate_w;  // [H] or NULL: the shared expert's gate row
+  float *gate;          // [T] (with gate_w): sigmoid of the gate row's product with x
 };
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s);
 // whether launch_router_logits writes x16 (when given) for this call
@@ -126,10 +128,14 @@ struct RouteFusedArgs {
   float *logits;      // [T][E] or NULL
   int32_t *ids;       // [T][K]
   float *w;           // [T][K]
-  float *part;        // [S][T][E] partial logits
+  float *part;        // [S][T][Ep] partial logits (column E: the shared gate row's)
   int32_t *counts, *offsets, *row_tok, *inv_pos, *active, *n_active;
   float *row_w;
   int32_t *units;     // [E] int4 (expert, first row, rows, 0) per active unit, or NULL
+  const float *gate_w;  // [H] or NULL: the shared expert's gate row, one more row of the product
+  float *gate;          // [T] (with gate_w): sigmoid of the gate logit, published with the routing
+  int32_t Ep;           // row stride of part: E, or E + 1 with the gate row
+  int32_t tail_skip;    // 0, or N: experts no token ranks among its first N are left out
 };
 hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s);    // partials + selection
 hipError_t launch_route_partial(const RouteFusedArgs &a, hipStream_t s);  // partials only
@@ -194,6 +200,7 @@ struct DownCombineArgs {
   float *y;                     // [T][H]
   const uint16_t *residual_in;  // with residual_out
   uint16_t *residual_out;       // NULL: no residual epilogue
+  const float *shared_gate;     // [T] or NULL: the shared expert's row is scaled by it
 };
 bool down_combine_ok(const FfnArgs &a, int K);
 hipError_t launch_down_combine(const DownCombineArgs &d, hipStream_t s);
@@ -203,6 +210,7 @@ struct CombineArgs {
   const int32_t *inv_pos;
   int32_t T, K, H;
   const float *shared_out;      // [T][H] or NULL
+  const float *shared_gate;     // [T] or NULL: shared_out's row t is scaled by it
   float *y;
   const uint16_t *residual_in;  // with residual_out
   uint16_t *residual_out;       // NULL: no residual epilogue

@@ -268,7 +268,12 @@ __global__ void __launch_bounds__(kDcMaxThreads) down_combine_kernel(DownCombine
 #pragma unroll
     for (int k = 0; k < kDcMaxK; ++k)
       if (k < K && pos[k] >= 0 && pos[k] < a.n_rows) y += vals[k];
-    if (has_shared) y += pout[(a.n_rows + ct) * kDcFeat + cf];
+    if (has_shared) {
+      // the shared row, scaled by its gate when there is one, exactly as
+      // the combine kernel adds it
+      const float sv = pout[(a.n_rows + ct) * kDcFeat + cf];
+      y = d.shared_gate ? fmaf(d.shared_gate[ct], sv, y) : y + sv;
+    }
     const size_t o = static_cast<size_t>(ct) * H + h0 + cf;
     d.y[o] = y;
     if (d.residual_out) d.residual_out[o] = f32_to_bf16_rne(bf16_to_f32(d.residual_in[o]) + y);

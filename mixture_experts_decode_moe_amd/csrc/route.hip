@@ -39,13 +39,17 @@ MOE_DEV float rows4_sum(float v) {
 
 // Stages the router rows of the block's 4 experts (slice [h0, h0 + Hs)) and
 // the slice of nt token rows starting at token t0 into LDS.
-MOE_DEV void stage_router_slice(const float *__restrict__ router_w, const uint16_t *__restrict__ x, int E, int H,
-                                int Hs, int e0, int h0, int t0, int nt, float *wr_l, uint16_t *xs) {
+// Row E is the shared expert's gate row when gate_w is given (the router
+// and the shared gate as one product); rows past the last read row 0.
+MOE_DEV void stage_router_slice(const float *__restrict__ router_w, const float *__restrict__ gate_w,
+                                const uint16_t *__restrict__ x, int E, int H, int Hs, int e0, int h0, int t0, int nt,
+                                float *wr_l, uint16_t *xs) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int e = e0 + wave;
-  const float4 *src = reinterpret_cast<const float4 *>(router_w + static_cast<size_t>(e < E ? e : 0) * H + h0);
+  const float *row = e < E ? router_w + static_cast<size_t>(e) * H : (gate_w && e == E ? gate_w : router_w);
+  const float4 *src = reinterpret_cast<const float4 *>(row + h0);
   float4 *dst = reinterpret_cast<float4 *>(wr_l + wave * Hs);
   const int n4 = Hs / 256;  // float4 per lane, <= kFusedMaxChunks
   float4 v[kFusedMaxChunks];
@@ -101,10 +105,14 @@ size_t router_slice_lds_bytes(int Hs, int tokens) {
 }
 
 // One block per (4 experts, 16 tokens); the slices are visited in order.
+// With gate_w, expert row E is the shared gate row: gate[t] receives the
+// sigmoid of its logit (no bias).
 __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restrict__ wr,
                                                             const float *__restrict__ bias,
                                                             const uint16_t *__restrict__ x, int32_t T, int32_t H,
-                                                            int32_t E, float *__restrict__ logits) {
+                                                            int32_t E, float *__restrict__ logits,
+                                                            const float *__restrict__ gate_w,
+                                                            float *__restrict__ gate) {
   extern __shared__ float4 smem_router[];
   const int Hs = route_fused_slice(H);
   float *wr_l = reinterpret_cast<float *>(smem_router);
@@ -118,11 +126,12 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restr
   float total = 0.f;
   for (int h0 = 0; h0 < H; h0 += Hs) {
     lds_barrier();  // the previous slice's readers are done
-    stage_router_slice(wr, x, E, H, Hs, e0, h0, t0, nt, wr_l, xs);
+    stage_router_slice(wr, gate_w, x, E, H, Hs, e0, h0, t0, nt, wr_l, xs);
     lds_barrier();
-    total += slice_partial(wr_l + wave * Hs, xs, Hs, nt, e < E);
+    total += slice_partial(wr_l + wave * Hs, xs, Hs, nt, e < E || (gate_w && e == E));
   }
   if (e < E && lane < nt) logits[static_cast<size_t>(t0 + lane) * E + e] = total + (bias ? bias[e] : 0.f);
+  if (gate_w && e == E && lane < nt) gate[t0 + lane] = 1.f / (1.f + expf(-total));
 }
 
 // ---------------------------------------------------------- large batches
@@ -266,14 +275,27 @@ __global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__
 }
 
 // One wave per token.  Lane l holds experts l, l+64, ... (up to 16 each).
+// With gate_w (a call whose logits came from the matrix-core GEMM) the wave
+// also forms its token's shared gate logit, lane l summing elements
+// l, l + 64, ... and the wave adding the lanes in a fixed order, and writes
+// its sigmoid to gate[t].
 template <int NPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int32_t T, int32_t E,
                                                    int32_t K, int32_t renorm, int32_t *__restrict__ ids,
-                                                   float *__restrict__ wout) {
+                                                   float *__restrict__ wout, const uint16_t *__restrict__ x,
+                                                   int32_t H, const float *__restrict__ gate_w,
+                                                   float *__restrict__ gate) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
+  if (gate_w) {
+    const uint16_t *xr = x + static_cast<size_t>(t) * H;
+    float acc = 0.f;
+    for (int h = lane; h < H; h += 64) acc = fmaf(gate_w[h], bf16_to_f32(xr[h]), acc);
+    const float z = sum64(acc);
+    if (lane == 0) gate[t] = 1.f / (1.f + expf(-z));
+  }
   const float *l = logits + static_cast<size_t>(t) * E;
   float v[NPL];
 #pragma unroll
@@ -310,16 +332,16 @@ __global__ void __launch_bounds__(256) route_partial_kernel(RouteFusedArgs a) {
   extern __shared__ float4 smem_route[];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int T = a.T, E = a.E, H = a.H, Hs = a.Hs, S = a.S;
+  const int T = a.T, E = a.E, H = a.H, Hs = a.Hs, S = a.S, Ep = a.Ep;
   const int slice = blockIdx.x % S;
-  const int e = (blockIdx.x / S) * 4 + wave;
+  const int e = (blockIdx.x / S) * 4 + wave;  // e == E: the shared gate row (Ep = E + 1)
   const int h0 = slice * Hs;
   float *wr_l = reinterpret_cast<float *>(smem_route);        // [4][Hs]
   uint16_t *xs = reinterpret_cast<uint16_t *>(wr_l + 4 * Hs);  // [T][Hs + 8]
-  stage_router_slice(a.router_w, a.x, E, H, Hs, e - wave, h0, 0, T, wr_l, xs);
+  stage_router_slice(a.router_w, a.gate_w, a.x, E, H, Hs, e - wave, h0, 0, T, wr_l, xs);
   lds_barrier();
-  const float p = slice_partial(wr_l + wave * Hs, xs, Hs, T, e < E);
-  if (lane < T && e < E) a.part[(static_cast<size_t>(slice) * T + lane) * E + e] = p;
+  const float p = slice_partial(wr_l + wave * Hs, xs, Hs, T, e < Ep);
+  if (lane < T && e < Ep) a.part[(static_cast<size_t>(slice) * T + lane) * Ep + e] = p;
 }
 
 // One block of kSelectThreads: the routing of a decode batch (top-k and
@@ -336,7 +358,7 @@ __global__ void __launch_bounds__(kSelectThreads) route_select_kernel(RouteFused
 }
 
 hipError_t launch_route_partial(const RouteFusedArgs &a, hipStream_t s) {
-  const int groups = (a.E + 3) / 4;
+  const int groups = (a.Ep + 3) / 4;
   route_partial_kernel<<<groups * a.S, 256, router_slice_lds_bytes(a.Hs, a.T), s>>>(a);
   return hipGetLastError();
 }
@@ -369,25 +391,32 @@ hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s) {
     router_mfma_kernel<<<g, kRmThreads, 0, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits, a.x16);
     return hipGetLastError();
   }
-  dim3 grid((a.E + 3) / 4, (a.T + kRouterTokens - 1) / kRouterTokens);
+  const int rows = a.E + (a.gate_w ? 1 : 0);  // the gate row rides with the router rows
+  dim3 grid((rows + 3) / 4, (a.T + kRouterTokens - 1) / kRouterTokens);
   const size_t lds = router_slice_lds_bytes(route_fused_slice(a.H), kRouterTokens);
-  router_logits_kernel<<<grid, 256, lds, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits);
+  router_logits_kernel<<<grid, 256, lds, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits, a.gate_w,
+                                              a.gate);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const RouteArgs &a, hipStream_t s) {
   dim3 grid((a.T + 3) / 4);
   const int npl = (a.E + 63) / 64;
+  // the shared gate is formed here only when the router GEMM left it out
+  const float *gw = router_mfma_ok(a) ? a.gate_w : nullptr;
+#define MOE_TOPK(N) \
+  topk_kernel<N><<<grid, 256, 0, s>>>(a.logits, a.T, a.E, a.K, a.renorm, a.ids, a.w, a.x, a.H, gw, a.gate)
   if (npl <= 1)
-    topk_kernel<1><<<grid, 256, 0, s>>>(a.logits, a.T, a.E, a.K, a.renorm, a.ids, a.w);
+    MOE_TOPK(1);
   else if (npl <= 2)
-    topk_kernel<2><<<grid, 256, 0, s>>>(a.logits, a.T, a.E, a.K, a.renorm, a.ids, a.w);
+    MOE_TOPK(2);
   else if (npl <= 4)
-    topk_kernel<4><<<grid, 256, 0, s>>>(a.logits, a.T, a.E, a.K, a.renorm, a.ids, a.w);
+    MOE_TOPK(4);
   else if (npl <= 8)
-    topk_kernel<8><<<grid, 256, 0, s>>>(a.logits, a.T, a.E, a.K, a.renorm, a.ids, a.w);
+    MOE_TOPK(8);
   else
-    topk_kernel<16><<<grid, 256, 0, s>>>(a.logits, a.T, a.E, a.K, a.renorm, a.ids, a.w);
+    MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

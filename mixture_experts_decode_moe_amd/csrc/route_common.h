@@ -178,7 +178,8 @@ constexpr int kRouteMaxPairs = 1024;  // T * K for T <= 16, K <= 64
 constexpr int kRouteMaxExperts = 1024;
 
 struct RouteLds {
-  uint32_t mask[16][kRouteMaxExperts / 32];  // experts chosen by each token
+  uint32_t mask[16][kRouteMaxExperts / 32];   // experts chosen by each token
+  uint32_t early[16][kRouteMaxExperts / 32];  // tail-skip: experts each token ranks among its first N
   int ids[kRouteMaxPairs];
   float w[kRouteMaxPairs];
   int row_tok[kRouteMaxPairs];  // token of each permuted row
@@ -214,6 +215,23 @@ MOE_DEV int block_scan(int v, int *scratch, int &total) {
   return before + inc - v;
 }
 
+// The shared gate of token t from the partials of row E (slices added in
+// order, as the logits are): every lane gets sigmoid(logit).
+MOE_DEV float route_gate(const RouteFusedArgs &a, int t) {
+  float z = 0.f;
+  for (int s0 = 0; s0 < a.S; ++s0) z += a.part[(static_cast<size_t>(s0) * a.T + t) * a.Ep + a.E];
+  return 1.f / (1.f + expf(-z));
+}
+
+// Tail-skip: whether some token of the call ranks expert ex among its first
+// N picks (always true without tail-skip).
+MOE_DEV bool route_kept(const RouteFusedArgs &a, const RouteLds &L, int ex) {
+  if (a.tail_skip <= 0) return true;
+  uint32_t any = 0;
+  for (int q = 0; q < a.T; ++q) any |= L.early[q][ex >> 5];
+  return (any >> (ex & 31)) & 1u;
+}
+
 template <int NPL>
 MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) {
   const int tid = threadIdx.x;
@@ -221,11 +239,15 @@ MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) 
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int nw = nthr >> 6;
-  const int T = a.T, E = a.E, S = a.S, K = a.K;
+  const int T = a.T, E = a.E, S = a.S, K = a.K, Ep = a.Ep;
   const int TK = T * K;
   const int mwords = (E + 31) / 32;
+  const int N = a.tail_skip > 0 ? min(a.tail_skip, K) : 0;
   for (int i = tid; i < E; i += nthr) L.cnt[i] = 0;
-  for (int i = tid; i < T * mwords; i += nthr) L.mask[i / mwords][i % mwords] = 0u;
+  for (int i = tid; i < T * mwords; i += nthr) {
+    L.mask[i / mwords][i % mwords] = 0u;
+    L.early[i / mwords][i % mwords] = 0u;
+  }
   for (int t = wave; t < T; t += nw) {
     // the partials of four slices at a time as independent loads, then
     // their sums in slice order
@@ -240,7 +262,7 @@ MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int ex = lane + 64 * j;
-          pv[j][q] = (ex < E && s0 + q < S) ? part[(static_cast<size_t>(s0 + q) * T + t) * E + ex] : 0.f;
+          pv[j][q] = (ex < E && s0 + q < S) ? part[(static_cast<size_t>(s0 + q) * T + t) * Ep + ex] : 0.f;
         }
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
@@ -268,23 +290,30 @@ MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) 
         a.w[p] = my_w;
       }
     }
+    if (a.gate_w) {
+      const float gv = route_gate(a, t);
+      if (publish && lane == 0) a.gate[t] = gv;
+    }
   }
   lds_barrier();
   for (int p = tid; p < TK; p += nthr) {
     const int ex = L.ids[p];
     atomicAdd(&L.cnt[ex], 1);
     atomicOr(&L.mask[p / K][ex >> 5], 1u << (ex & 31));
+    if (p % K < N) atomicOr(&L.early[p / K][ex >> 5], 1u << (ex & 31));
   }
   lds_barrier();
   // thread tid owns the experts [tid * ept, tid * ept + ept)
   const int ept = (E + nthr - 1) / nthr;  // <= 4
-  int c4[4], n_here = 0, nz_here = 0;
+  // an active unit is an expert with rows that tail-skip keeps
+  int c4[4], act4[4], n_here = 0, nz_here = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ex = tid * ept + i;
     c4[i] = (i < ept && ex < E) ? L.cnt[ex] : 0;
+    act4[i] = c4[i] > 0 && route_kept(a, L, ex);
     n_here += c4[i];
-    nz_here += c4[i] > 0;
+    nz_here += act4[i];
   }
   int total = 0, n_act = 0;
   int base = block_scan(n_here, L.scan, total);
@@ -294,13 +323,16 @@ MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) 
     const int ex = tid * ept + i;
     if (i < ept && ex < E) {
       L.off[ex] = base;
-      if (c4[i] > 0) L.active[abase] = ex;
+      if (act4[i]) L.active[abase] = ex;
       if (publish) {
         a.counts[ex] = c4[i];
         a.offsets[ex] = base;
-        if (c4[i] > 0) a.active[abase] = ex;
+        if (act4[i]) {
+          a.active[abase] = ex;
+          if (a.units) reinterpret_cast<int4 *>(a.units)[abase] = make_int4(ex, base, c4[i], 0);
+        }
       }
-      abase += c4[i] > 0;
+      abase += act4[i];
     }
     base += c4[i];
   }
@@ -324,7 +356,7 @@ MOE_DEV void route_in_block(const RouteFusedArgs &a, RouteLds &L, bool publish) 
     if (publish) {
       a.row_tok[pos] = p / K;
       a.row_w[pos] = L.w[p];
-      a.inv_pos[p] = pos;
+      a.inv_pos[p] = route_kept(a, L, ex) ? pos : -1;  // a left-out slot adds nothing
     }
   }
   lds_barrier();
@@ -355,8 +387,9 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
-  const int T = a.T, E = a.E, S = a.S, K = a.K;
+  const int T = a.T, E = a.E, S = a.S, K = a.K, Ep = a.Ep;
   const int mwords = (E + 31) / 32;  // <= 8
+  const int N = a.tail_skip > 0 ? min(a.tail_skip, K) : 0;
   for (int t = wave; t < T; t += nw) {
     const float *__restrict__ part = a.part;
     float acc[NPL];
@@ -372,7 +405,7 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
         for (int q = 0; q < 4; ++q) {
           const int ex = min(lane + 64 * j, E - 1);
           const int sl = min(s0 + q, S - 1);
-          pv[j][q] = part[(static_cast<size_t>(sl) * T + t) * E + ex];
+          pv[j][q] = part[(static_cast<size_t>(sl) * T + t) * Ep + ex];
         }
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
@@ -391,7 +424,10 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
     float my_w;
     wave_topk<NPL>(v, E, K, a.renorm, my_e, my_w);
     // the wave's own LDS operations run in order: clear, then set the bits
-    if (lane < mwords) L.mask[t][lane] = 0u;
+    if (lane < mwords) {
+      L.mask[t][lane] = 0u;
+      L.early[t][lane] = 0u;
+    }
     if (lane < K) {
       const int p = t * K + lane;
       L.ids[p] = my_e;
@@ -401,6 +437,11 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
         a.w[p] = my_w;
       }
       atomicOr(&L.mask[t][my_e >> 5], 1u << (my_e & 31));
+      if (lane < N) atomicOr(&L.early[t][my_e >> 5], 1u << (my_e & 31));
+    }
+    if (a.gate_w) {
+      const float gv = route_gate(a, t);
+      if (publish && lane == 0) a.gate[t] = gv;
     }
   }
 }
@@ -419,12 +460,14 @@ MOE_DEV void route_small_scan(const RouteFusedArgs &a, RouteLds &L, bool publish
       for (int i = 0; i < 4; ++i) c[i] += (m >> i) & 1u;
     }
   }
-  int n_here = 0, nz_here = 0;
+  // an active unit is an expert with rows that tail-skip keeps
+  int n_here = 0, nz_here = 0, act[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (4 * lane + i >= E) c[i] = 0;
+    act[i] = c[i] > 0 && route_kept(a, L, 4 * lane + i);
     n_here += c[i];
-    nz_here += c[i] > 0;
+    nz_here += act[i];
   }
   const int inc = wave_incl_sum(n_here), incz = wave_incl_sum(nz_here);
   int base = inc - n_here, abase = incz - nz_here;
@@ -435,16 +478,16 @@ MOE_DEV void route_small_scan(const RouteFusedArgs &a, RouteLds &L, bool publish
     if (ex < E) {
       L.cnt[ex] = c[i];
       L.off[ex] = base;
-      if (c[i] > 0) L.active[abase] = ex;
+      if (act[i]) L.active[abase] = ex;
       if (publish) {
         a.counts[ex] = c[i];
         a.offsets[ex] = base;
-        if (c[i] > 0) {
+        if (act[i]) {
           a.active[abase] = ex;
           if (a.units) reinterpret_cast<int4 *>(a.units)[abase] = make_int4(ex, base, c[i], 0);
         }
       }
-      abase += c[i] > 0;
+      abase += act[i];
     }
     base += c[i];
   }
@@ -471,7 +514,7 @@ MOE_DEV void route_small_rows(const RouteFusedArgs &a, RouteLds &L, bool publish
     if (publish) {
       a.row_tok[pos] = t;
       a.row_w[pos] = L.w[p];
-      a.inv_pos[p] = pos;
+      a.inv_pos[p] = route_kept(a, L, ex) ? pos : -1;  // a left-out slot adds nothing
     }
   }
 }

@@ -75,6 +75,7 @@ def test_workspace_bytes_is_pure_and_grows(mb):
     (lambda L: setattr(L.routed, "reserved", 1), -1),
     (lambda L: setattr(L.shared, "n_experts", 2), -1),
     (lambda L: setattr(L, "router_w", None), -1),
+    (lambda L: setattr(L, "shared_gate_w", (1 << 20) + 4), -1),  # a gate row not 16-byte aligned
 ])
 def test_layer_validation_rejects_before_launch(mb, mutate, expect):
     lib = mb.raw_lib()
@@ -97,10 +98,10 @@ def test_other_entry_points_reject_bad_arguments(mb):
     assert lib.moe_layer_forward(ctypes.byref(L), p, 4, p, None, None, None, p, 16, None) == -3
     assert lib.moe_layer_forward(ctypes.byref(L), ctypes.c_void_p((1 << 20) + 2), 4, p, None, None, None, p,
                                  1 << 30, None) == -1
-    assert lib.moe_route(ctypes.byref(L), p, 4, None, p, p, None, 0, None) == -1
+    assert lib.moe_route(ctypes.byref(L), p, 4, None, p, p, None, None, 0, None) == -1
     # logits optional: without them the call needs a workspace for them
-    assert lib.moe_route(ctypes.byref(L), p, 4, p, p, None, None, 0, None) == -3
-    assert lib.moe_route(ctypes.byref(L), p, 4, p, p, None, p, 16, None) == -3
+    assert lib.moe_route(ctypes.byref(L), p, 4, p, p, None, None, None, 0, None) == -3
+    assert lib.moe_route(ctypes.byref(L), p, 4, p, p, None, None, p, 16, None) == -3
     assert lib.moe_route_workspace_bytes(ctypes.byref(L), 4) >= 4 * 256 * 4
     assert lib.moe_route_workspace_bytes(ctypes.byref(L), -1) == 0
     assert lib.moe_permute(p, p, 4, 9, 8, p, p, p, p, p, p, p, p, 1 << 20, None) == -1  # K > E
@@ -109,9 +110,9 @@ def test_other_entry_points_reject_bad_arguments(mb):
     ex = mb.MoeExperts(2, 256, 512, 0, p, p, p, p, p, p)
     assert lib.moe_expert_ffn(ctypes.byref(ex), 2048, p, 4, 32, None, None, None, p, p, p, p, 1 << 30,
                               None) == -1  # routed set without offsets
-    assert lib.moe_combine(p, p, 4, 8, 2046, None, p, None, None) == -1
+    assert lib.moe_combine(p, p, 4, 8, 2046, None, None, p, None, None) == -1
     bad = mb.MoeResidual(None, 1 << 20, None, 1e-6, 0)  # residual_out without residual_in
-    assert lib.moe_combine(p, p, 4, 8, 2048, None, p, ctypes.byref(bad), None) == -1
+    assert lib.moe_combine(p, p, 4, 8, 2048, None, None, p, ctypes.byref(bad), None) == -1
     assert lib.moe_layer_forward(ctypes.byref(_fake_layer(mb)), p, 4, p, ctypes.byref(bad), None, None, p,
                                  1 << 30, None) == -1
     assert lib.moe_workspace_init(None, 0, None) == -3
@@ -130,6 +131,9 @@ def test_forward_options_are_validated(mb):
     o.path = 3
     assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
                                     None) == -1
+    o = mb.forward_opts(tail_skip=-1)
+    assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
+                                    None) == -1
     o = mb.forward_opts("prefill")
     o.reserved[1] = 5
     assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
@@ -146,3 +150,15 @@ def test_no_process_global_mutable_state_in_the_host_code():
     assert "thread_local" not in src
     assert not re.search(r"^static\s+(?!inline|bool|int|size_t|hipError_t|void|const)", src, flags=re.M)
     assert not re.search(r"^(hipEvent_t|int|float|bool)\s+\w+\s*(\[.*\])?\s*(=.*)?;", src, flags=re.M)
+
+
+def test_shared_gate_needs_a_shared_expert(mb):
+    lib = mb.raw_lib()
+    p = ctypes.c_void_p(1 << 20)
+    L = _fake_layer(mb, shared=False)
+    L.shared_gate_w = 1 << 20
+    assert lib.moe_workspace_bytes(ctypes.byref(L), 4) == 0
+    assert lib.moe_layer_forward(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, None) == -1
+    L = _fake_layer(mb, shared=True)
+    L.shared_gate_w = 1 << 20
+    assert lib.moe_workspace_bytes(ctypes.byref(L), 4) > 0
