@@ -211,7 +211,19 @@ typedef struct moe_forward_opts {
    * router gave them (no renormalisation).  An approximation: it changes
    * the output.  Prompt batches are left untouched, as on the pages. */
   int32_t tail_skip;
-  int32_t reserved[2]; /* must be 0 */
+  /* W8A8 variant: 0 = off; 1: the expert products take int8 activations
+   * ("Strata on an Intel Arc", Arc Pro B70: the fused int8 expert path for
+   * the prompt; "Models and backends", How each backend was checked: 8-bit
+   * activations at every quantised matrix).  Every token's input and every
+   * (token, expert) SwiGLU row is quantised with one symmetric scale per
+   * row: amax = max |v|, q = round-half-even(v * (127 / amax)) in float32,
+   * d = amax / 127; the int8 products accumulate exactly in int32 on the
+   * int8 matrix cores and the row scales are applied once.  Needs int8
+   * row-scaled weights (MOE_ERR_UNSUPPORTED otherwise; a shared expert must
+   * be as wide as the routed ones) and changes the result by the
+   * quantisation (about 1% of the output scale for N(0, 1) inputs). */
+  int32_t act_quant;
+  int32_t reserved; /* must be 0 */
   /* Profiling: hipEvent_t pairs (created by the caller) recorded on the
    * call's stream around each stage: index MOE_STAGE_*; a stage is profiled
    * when both of its events are non-NULL.  The gate/up and down stages'

@@ -46,7 +46,8 @@ PATHS = {"auto": MOE_PATH_AUTO, "decode": MOE_PATH_DECODE, "prefill": MOE_PATH_P
 
 
 class MoeForwardOpts(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("tail_skip", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
+    _fields_ = [("path", ctypes.c_int32), ("tail_skip", ctypes.c_int32), ("act_quant", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
                 ("stage_start", ctypes.c_void_p * MOE_N_STAGES), ("stage_stop", ctypes.c_void_p * MOE_N_STAGES)]
 
 
@@ -246,14 +247,15 @@ def combine(rows_out, inv_pos, T: int, K: int, H: int, shared_out, y, res: MoeRe
 STAGES = {"route": 1, "permute": 2, "gateup": 3, "down": 4, "shared": 5, "combine": 6}
 
 
-def forward_opts(path="auto", events=None, tail_skip=0) -> MoeForwardOpts:
+def forward_opts(path="auto", events=None, tail_skip=0, act_quant=0) -> MoeForwardOpts:
     """Per-call options: path "auto" | "decode" | "prefill"; tail_skip N (0 =
-    off); events a dict stage name -> (start, stop) torch.cuda.Event pairs
-    (already created, e.g. by one record) that the call records around that
-    stage."""
+    off); act_quant 1 for the W8A8 variant; events a dict stage name ->
+    (start, stop) torch.cuda.Event pairs (already created, e.g. by one
+    record) that the call records around that stage."""
     o = MoeForwardOpts()
     o.path = PATHS[path]
     o.tail_skip = int(tail_skip)
+    o.act_quant = int(act_quant)
     for name, (a, b) in (events or {}).items():
         o.stage_start[STAGES[name]] = a.cuda_event
         o.stage_stop[STAGES[name]] = b.cuda_event

@@ -111,6 +111,8 @@ struct LayerWs {
   float *act, *rows_out;
   uint16_t *x16;  // x in fp16 for the prefill GEMMs, written by the router GEMM
   float *gate;    // [T]: the shared expert's gate values
+  int8_t *qx, *qa;  // W8A8: quantised x [T][H] and SwiGLU rows [rows][F]
+  float *dx, *da;   // their per-row scales
   size_t bytes;
 };
 
@@ -144,6 +146,10 @@ LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
   w.rows_out = c.take<float>((TK + (Fs ? T : 0)) * L->hidden);
   w.x16 = c.take<uint16_t>(static_cast<size_t>(T) * L->hidden);
   w.gate = c.take<float>(T);
+  w.qx = c.take<int8_t>(static_cast<size_t>(T) * L->hidden);
+  w.dx = c.take<float>(T);
+  w.qa = c.take<int8_t>((TK + (Fs ? T : 0)) * L->routed.ffn);
+  w.da = c.take<float>(TK + (Fs ? T : 0));
   w.bytes = align_up(c.off, 256);
   return w;
 }
@@ -358,10 +364,16 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
   if (rc != MOE_OK) return rc;
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (opts) {
-    if (opts->path < MOE_PATH_AUTO || opts->path > MOE_PATH_PREFILL || opts->tail_skip < 0)
+    if (opts->path < MOE_PATH_AUTO || opts->path > MOE_PATH_PREFILL || opts->tail_skip < 0 ||
+        (opts->act_quant != 0 && opts->act_quant != 1))
       return MOE_ERR_INVALID_ARG;
-    for (int32_t r : opts->reserved)
-      if (r != 0) return MOE_ERR_INVALID_ARG;
+    // the W8A8 variant takes int8 row-scaled weights (and a shared expert as
+    // wide as the routed ones)
+    if (opts->act_quant &&
+        (L->routed.fmt != MOE_W_INT8_ROW || (L->shared.n_experts == 1 && (L->shared.fmt != MOE_W_INT8_ROW ||
+                                                                          L->shared.ffn != L->routed.ffn))))
+      return MOE_ERR_UNSUPPORTED;
+    if (opts->reserved != 0) return MOE_ERR_INVALID_ARG;
   }
   if (T == 0) return MOE_OK;
   if (static_cast<int64_t>(T) * L->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
@@ -401,7 +413,15 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
   xa.distinct_ids = 1;  // the layer's own top-k picks distinct experts per token
 
   hipError_t e;
-  const bool decode_batch = T <= kFusedTokens && path != MOE_PATH_PREFILL;
+  const bool w8a8 = opts && opts->act_quant;
+  if (w8a8) {
+    xa.qx = w.qx;
+    xa.dx = w.dx;
+    xa.qa = w.qa;
+    xa.da = w.da;
+    if (!w8a8_ok(xa)) return MOE_ERR_UNSUPPORTED;
+  }
+  const bool decode_batch = T <= kFusedTokens && path != MOE_PATH_PREFILL && !w8a8;
   if (decode_batch) {
     // decode batch: the router's partial logits; the top-k and the
     // permutation then run inside the gate/up kernel when it is the
@@ -472,7 +492,12 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
 
-  {
+  if (w8a8) {
+    // the W8A8 expert products (gate/up and down record their stages' events)
+    StageMark mg(ev, MOE_STAGE_GATEUP, s, true);
+    StageMark md(ev, MOE_STAGE_DOWN, s, true);
+    e = launch_w8a8(xa, s, ev.of(MOE_STAGE_GATEUP), ev.of(MOE_STAGE_DOWN));
+  } else {
     StageMark m(ev, MOE_STAGE_GATEUP, s, true);
     xa.ev = ev.of(MOE_STAGE_GATEUP);
     e = launch_gateup(xa, s);
@@ -486,7 +511,7 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
                       res ? res->residual_out : nullptr, L->shared_gate_w ? w.gate : nullptr};
     return hip_status(launch_down_combine(d, s));
   }
-  {
+  if (!w8a8) {
     StageMark m(ev, MOE_STAGE_DOWN, s, true);
     xa.ev = ev.of(MOE_STAGE_DOWN);
     e = launch_down(xa, s);

@@ -185,6 +185,12 @@ struct FfnArgs {
   int32_t path;          // PathSel
   int32_t distinct_ids;  // 1: every token picks an expert at most once, so a unit has at most T rows
   LaunchEvents ev;       // profiling events of the expert kernel of this stage (host side only)
+  // W8A8 variant: x quantised per token [T][H] with scales [T]; the SwiGLU
+  // rows (fp32 in act, F each) quantised per row [rows][F] with scales [rows]
+  int8_t *qx;
+  float *dx;
+  int8_t *qa;
+  float *da;
 };
 hipError_t launch_gateup(const FfnArgs &a, hipStream_t s);
 bool mfma_decode_ok(const FfnArgs &a);  // the decode matrix-core kernels take this call
@@ -203,6 +209,11 @@ struct DownCombineArgs {
   const float *shared_gate;     // [T] or NULL: the shared expert's row is scaled by it
 };
 bool down_combine_ok(const FfnArgs &a, int K);
+
+// The W8A8 variant (int8 row-scaled weights, int8 activations): quantise x,
+// gate/up + SwiGLU, quantise the SwiGLU rows, down x routing weight.
+bool w8a8_ok(const FfnArgs &a);
+hipError_t launch_w8a8(const FfnArgs &a, hipStream_t s, const LaunchEvents &ev_gu, const LaunchEvents &ev_dn);
 hipError_t launch_down_combine(const DownCombineArgs &d, hipStream_t s);
 
 struct CombineArgs {

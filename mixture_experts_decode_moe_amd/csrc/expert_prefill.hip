@@ -1230,6 +1230,270 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   }
 }
 
+// ---------------------------------------------------------- W8A8 variant
+//
+// int8 activations with int8 row-scaled weights (the W8A8 variant: the
+// pages' engines quantise activations to 8 bits at every quantised matrix,
+// "Models and backends", How each backend was checked; the B70 prompt path
+// multiplies int8 weights by int8 activations, "Strata on an Intel Arc",
+// Arc Pro B70: the fused int8 expert path for the prompt).  Every token's
+// input and every (token, expert) SwiGLU row is quantised with one symmetric
+// scale per row; since the weights carry one scale per row too, both scales
+// factor out of the whole reduction: I = sum_k qa[k] qw[k] accumulates
+// exactly in int32 on the int8 matrix cores (v_mfma_i32_32x32x32_i8) and
+// the epilogue applies d_row * s_col once.
+//
+// Quantiser (one block per row): amax = max |v|, inv = 127 / amax and
+// d = amax / 127 (correctly rounded divisions), q = round-half-even(v * inv)
+// (one rounded product), clamped to [-127, 127]; amax = 0 gives q = 0, d = 0.
+// Every decision in float32, as the reference statement of the variant.
+//
+// GEMM tiles.  An item is (unit, 64 rows, 128 output columns); each of the 4
+// waves owns 32 of the columns for all 64 rows (two 32x32 tiles along M;
+// gate/up: the gate and the up tile of its 32 SwiGLU columns).  Operands go
+// straight from global memory (through the caches) into registers: lane l
+// supplies row / column l % 32 and the 16 consecutive k of group l / 32 of
+// each 32-wide step, two steps requested ahead.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+MOE_DEV i32x16_t mfma_i8(const i32x4_t &a, const i32x4_t &b, const i32x16_t &c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+constexpr int kQrThreads = 256;
+constexpr int kQrMaxPer = 16;  // elements a thread holds: rows of up to 4096
+
+MOE_DEV float qr_value(const uint16_t *p, int i) { return bf16_to_f32(p[i]); }
+MOE_DEV float qr_value(const float *p, int i) { return p[i]; }
+
+template <typename In>
+__global__ void __launch_bounds__(kQrThreads) quant_rows_kernel(const In *__restrict__ in, int K,
+                                                                int8_t *__restrict__ q, float *__restrict__ d) {
+  __shared__ float wmax[kQrThreads / 64];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const In *src = in + static_cast<size_t>(row) * K;
+  float v[kQrMaxPer];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kQrMaxPer; ++i) {
+    const int idx = tid + kQrThreads * i;
+    v[i] = idx < K ? qr_value(src, idx) : 0.f;
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  // block maximum (non-negative floats order as their bit patterns)
+  uint32_t m = __float_as_uint(amax);
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1)));
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2)));
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 4)));
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 8)));
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16)));
+  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32)));
+  if ((tid & 63) == 0) wmax[tid >> 6] = __uint_as_float(m);
+  lds_barrier();
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kQrThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+  const float inv = amax > 0.f ? 127.f / amax : 0.f;
+  int8_t *dst = q + static_cast<size_t>(row) * K;
+#pragma unroll
+  for (int i = 0; i < kQrMaxPer; ++i) {
+    const int idx = tid + kQrThreads * i;
+    if (idx < K) {
+      const float r = rintf(v[i] * inv);  // one rounded product, ties to even
+      dst[idx] = static_cast<int8_t>(static_cast<int>(fminf(127.f, fmaxf(-127.f, r))));
+    }
+  }
+  if (tid == 0) d[row] = amax > 0.f ? amax / 127.f : 0.f;
+}
+
+constexpr int kW8Cols = 128;  // output columns per item (gate/up: SwiGLU columns)
+static int pf_grid(int items_upper);
+
+MOE_DEV i32x4_t load_i8x16(const int8_t *p) {
+  const uint4 v = *reinterpret_cast<const uint4 *>(p);
+  return i32x4_t{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
+}
+
+// GATEUP: a[row][f] = silu(g) u with g = I_g dx[t] sg[f] (and u alike), the
+// rows' tokens' inputs against the gate and up rows f.  Otherwise (down):
+// rows_out[row][h] = I dA[row] sd[h] w[row], the rows' quantised SwiGLU
+// rows against the down rows h.
+template <bool GATEUP>
+__global__ void __launch_bounds__(kPfThreads) w8a8_gemm_kernel(FfnArgs a) {
+  __shared__ int pre[kPfMaxUnits + 1];
+  __shared__ int scratch[4];
+  __shared__ int rtok[kPfRows];    // GATEUP: token of each tile row; down: its act row
+  __shared__ float rscale[kPfRows];  // the row's activation scale (x weight for down)
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31, kg = lane >> 5;
+  const int H = a.H, T = a.T;
+  const int K = GATEUP ? H : a.F;        // reduction
+  const int N = GATEUP ? a.F : H;        // output columns (SwiGLU columns for gate/up)
+  const int n_units = pf_tiles(a, pre, scratch);
+  const int col_groups = N / kW8Cols;
+  const int n_items = pre[n_units] * col_groups;
+  const int steps = K / 32;
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int j = item / col_groups;
+    const int cg = item - j * col_groups;
+    const int u = pf_find(pre, n_units, j);
+    const PfUnit un = pf_unit(a, u);
+    const int m0 = (j - pre[u]) * kPfRows;  // first row of the tile inside the unit
+    const int rows = min(kPfRows, un.n - m0);
+    const bool shared = un.e < 0;
+    const int e = shared ? 0 : un.e;
+    lds_barrier();  // the previous item's readers of rtok / rscale are done
+    if (tid < kPfRows) {
+      int t = 0;
+      float sc = 0.f;
+      if (tid < rows) {
+        const int rr = un.r0 + m0 + tid;  // routed: row index; shared: token
+        if (GATEUP) {
+          t = shared ? rr : (a.row_tok ? a.row_tok[rr] : rr);
+          t = t < 0 ? 0 : (t >= T ? T - 1 : t);  // memory safety for malformed row lists
+          sc = a.dx[t];
+        } else {
+          t = shared ? a.n_rows + rr : rr;  // the row's act row (= its output row)
+          sc = a.da[t] * (shared || !a.row_w ? 1.f : a.row_w[rr]);
+        }
+      }
+      rtok[tid] = t;
+      rscale[tid] = sc;
+    }
+    lds_barrier();
+    // this lane's A rows (two 32-row tiles) and B columns
+    const int8_t *ap[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int r = 32 * mt + c;
+      const int src = rtok[r < rows ? r : 0];
+      ap[mt] = (GATEUP ? a.qx + static_cast<size_t>(src) * H : a.qa + static_cast<size_t>(src) * a.F) + 16 * kg;
+    }
+    const int col = cg * kW8Cols + 32 * wave + c;
+    const int8_t *bp0, *bp1;
+    if (GATEUP) {
+      const int8_t *gq = static_cast<const int8_t *>(shared ? a.sgq : a.gq);
+      const int8_t *uq = static_cast<const int8_t *>(shared ? a.suq : a.uq);
+      const size_t row = static_cast<size_t>(e) * (shared ? a.Fs : a.F) + col;
+      bp0 = gq + row * H + 16 * kg;
+      bp1 = uq + row * H + 16 * kg;
+    } else {
+      const int8_t *dq = static_cast<const int8_t *>(shared ? a.sdq : a.dq);
+      bp0 = dq + (static_cast<size_t>(e) * H + col) * a.F + 16 * kg;
+      bp1 = bp0;
+    }
+    const bool mv0 = c < rows, mv1 = 32 + c < rows;
+    i32x16_t acc[2][2];  // [B tile (gate, up)][M tile]
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][mt][r] = 0;
+    // two steps in flight: operands of step s + 2 requested before step s is multiplied
+    i32x4_t A0[3], A1[3], B0[3], B1[3];
+    auto load = [&](int s, int slot) __attribute__((always_inline)) {
+      const int ks = min(s, steps - 1) * 32;  // past the end: re-request the last step
+      A0[slot] = load_i8x16(ap[0] + ks);
+      A1[slot] = load_i8x16(ap[1] + ks);
+      B0[slot] = load_i8x16(bp0 + ks);
+      if (GATEUP) B1[slot] = load_i8x16(bp1 + ks);
+    };
+    const i32x4_t z4 = {0, 0, 0, 0};
+    auto step = [&](int slot) __attribute__((always_inline)) {
+      const i32x4_t a0 = mv0 ? A0[slot] : z4, a1 = mv1 ? A1[slot] : z4;
+      acc[0][0] = mfma_i8(a0, B0[slot], acc[0][0]);
+      acc[0][1] = mfma_i8(a1, B0[slot], acc[0][1]);
+      if (GATEUP) {
+        acc[1][0] = mfma_i8(a0, B1[slot], acc[1][0]);
+        acc[1][1] = mfma_i8(a1, B1[slot], acc[1][1]);
+      }
+    };
+    load(0, 0);
+    load(1, 1);
+    int s = 0;
+    for (; s + 3 <= steps; s += 3) {  // slots by step modulo 3, constant inside the body
+      load(s + 2, 2);
+      step(0);
+      load(s + 3, 0);
+      step(1);
+      load(s + 4, 1);
+      step(2);
+    }
+    for (; s < steps; ++s) {  // the remaining (at most two) steps are in slots 0 and 1
+      if (s % 3 == 0) step(0); else if (s % 3 == 1) step(1); else step(2);
+      if (s + 2 < steps) {
+        if ((s + 2) % 3 == 0) load(s + 2, 0); else if ((s + 2) % 3 == 1) load(s + 2, 1); else load(s + 2, 2);
+      }
+    }
+    // epilogue: result (m, n) of a 32x32 tile sits in lane n + 32 ((m / 4) % 2),
+    // register 4 (m / 8) + m % 4
+    if (GATEUP) {
+      const float *gs = static_cast<const float *>(shared ? a.sgs : a.gs);
+      const float *us = static_cast<const float *>(shared ? a.sus : a.us);
+      const size_t srow = static_cast<size_t>(e) * (shared ? a.Fs : a.F) + col;
+      const float sg = gs[srow], su = us[srow];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 32 * mt + 8 * (r >> 2) + 4 * kg + (r & 3);
+          if (m < rows) {
+            const float dxr = rscale[m];
+            const float gv = static_cast<float>(acc[0][mt][r]) * dxr * sg;
+            const float uv = static_cast<float>(acc[1][mt][r]) * dxr * su;
+            const int rr = m0 + m;
+            const size_t arow = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(un.r0) + rr;
+            a.act[arow * a.F + col] = gv / (1.f + expf(-gv)) * uv;
+          }
+        }
+    } else {
+      const float sd = static_cast<const float *>(shared ? a.sds : a.ds)[static_cast<size_t>(e) * H + col];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 32 * mt + 8 * (r >> 2) + 4 * kg + (r & 3);
+          if (m < rows) {
+            const float v = static_cast<float>(acc[0][mt][r]) * rscale[m] * sd;
+            a.rows_out[static_cast<size_t>(rtok[m]) * H + col] = v;
+          }
+        }
+    }
+  }
+}
+
+bool w8a8_ok(const FfnArgs &a) {
+  const int units = (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1);
+  return a.fmt == MOE_W_INT8_ROW && (a.Fs == 0 || a.Fs == a.F) && a.F % kW8Cols == 0 && a.H % kW8Cols == 0 &&
+         a.H <= kQrThreads * kQrMaxPer && a.F <= kQrThreads * kQrMaxPer && units <= kPfMaxUnits && a.qx && a.dx &&
+         a.qa && a.da;
+}
+
+hipError_t launch_w8a8(const FfnArgs &a, hipStream_t s, const LaunchEvents &ev_gu, const LaunchEvents &ev_dn) {
+  if (!w8a8_ok(a)) return hipErrorInvalidValue;
+  // every token's input, quantised per row
+  quant_rows_kernel<uint16_t><<<a.T, kQrThreads, 0, s>>>(a.x, a.H, a.qx, a.dx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int units = (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1);
+  const int tiles = (a.n_rows + kPfRows - 1) / kPfRows + units + (a.Fs > 0 ? (a.T + kPfRows - 1) / kPfRows : 0);
+  e = launch_kernel(w8a8_gemm_kernel<true>, dim3(pf_grid(tiles * (a.F / kW8Cols))), dim3(kPfThreads), 0, s, ev_gu, a);
+  if (e != hipSuccess) return e;
+  // every SwiGLU row (routed, then the shared expert's), quantised per row
+  const int rows_all = a.n_rows + (a.Fs > 0 ? a.T : 0);
+  quant_rows_kernel<float><<<rows_all, kQrThreads, 0, s>>>(a.act, a.F, a.qa, a.da);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_kernel(w8a8_gemm_kernel<false>, dim3(pf_grid(tiles * (a.H / kW8Cols))), dim3(kPfThreads), 0, s, ev_dn,
+                       a);
+}
+
 // ----------------------------------------------------------------- launches
 
 bool prefill_ok(const FfnArgs &a) {

@@ -134,8 +134,14 @@ def test_forward_options_are_validated(mb):
     o = mb.forward_opts(tail_skip=-1)
     assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
                                     None) == -1
+    o = mb.forward_opts(act_quant=2)
+    assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
+                                    None) == -1
+    o = mb.forward_opts(act_quant=1)  # the W8A8 variant needs int8 row-scaled weights
+    assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
+                                    None) == -2
     o = mb.forward_opts("prefill")
-    o.reserved[1] = 5
+    o.reserved = 5
     assert lib.moe_layer_forward_ex(ctypes.byref(L), p, 4, p, None, None, None, p, 1 << 30, ctypes.byref(o),
                                     None) == -1
     assert mb.forward_opts("decode").path == 1 and mb.forward_opts("prefill").path == 2

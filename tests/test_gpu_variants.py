@@ -185,3 +185,65 @@ def test_tail_skip_with_shared_gate_and_residual_norm(mb):
     y_ref, _, _, _ = oracle.layer_forward(layer, x, ids=gpu["ids"], tail_skip=N)
     assert pu.rel_max_err(gpu["y"], y_ref) <= pu.Y_REL
     assert np.array_equal(gpu["residual_out"], pu.residual_expected(r, gpu["y"]))
+
+
+# ------------------------------------------------------------ W8A8
+
+def _check_w8a8(mb, layer, x, T, path="auto"):
+    """The W8A8 call against the oracle's int8-activation mode on the GPU's
+    own selection (identical to the oracle's away from near ties, checked)."""
+    import oracle
+    import parity_util as pu
+    dl = mb.layer_to_device(layer)
+    gpu = pu.run_layer(dl, pu.dev_u16(x), T, with_logits=False, opts=mb.forward_opts(path, act_quant=1))
+    _, ids_ref, _, logits_ref = oracle.layer_forward(layer, x)
+    pu.check_selection(gpu["ids"], ids_ref, logits_ref, layer.top_k)
+    y_ref, _, _, _ = oracle.layer_forward(layer, x, ids=gpu["ids"], act_quant=1)
+    err = pu.rel_max_err(gpu["y"], y_ref)
+    exact, _, _, _ = oracle.layer_forward(layer, x, ids=gpu["ids"])
+    moved = pu.rel_max_err(y_ref, exact)
+    say(f"  W8A8 T={T}: rel err {err:.2e} against the W8A8 oracle (quantisation moves the output by {moved:.2e})")
+    assert err <= pu.Y_REL
+    assert moved > 1e-4  # the variant is really quantised
+    return gpu
+
+
+@pytest.mark.parametrize("T,jitter", [(3, False), (40, True), (300, True)])
+def test_w8a8_parity_real_shape(mb, T, jitter):
+    """int8 weights at the real shape (H=2048, 256 experts, top-8, F=512 +
+    shared expert), int8 activations."""
+    shape = _shape(1, tokens=T, jitter_scales=jitter, seed=900 + T)
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    say(f"W8A8 cfg1 shape T={T} jitter={jitter}")
+    _check_w8a8(mb, layer, x, T)
+
+
+def test_w8a8_parity_small_layer_with_gate_no_shared(mb):
+    """H=1024, 64 experts, top-4, F=256: no shared expert, bias routing."""
+    shape = _shape(0, tokens=70, seed=910, jitter_scales=True)
+    layer = synth.make_layer(shape)
+    layer.router_bias = synth.normal_f32(910, 99, shape.n_experts, 0.0, 0.5)
+    x = synth.make_x(shape)
+    say("W8A8 H=1024 E=64 K=4 F=256 T=70")
+    _check_w8a8(mb, layer, x, 70)
+
+
+def test_w8a8_with_shared_gate(mb):
+    shape = _shape(1, tokens=33, seed=920, shared_gate=True)
+    layer = synth.make_layer(shape)
+    x = synth.make_x(shape)
+    say("W8A8 with the shared gate, T=33")
+    _check_w8a8(mb, layer, x, 33)
+
+
+def test_w8a8_refuses_int4_weights(mb):
+    import torch
+    shape = _shape(2, tokens=4, correlated_sigma=0.0, seed=930)
+    dl = mb.layer_to_device(synth.make_layer(shape))
+    ws = mb.make_workspace(dl, 4)
+    x = torch.zeros((4, shape.hidden), dtype=torch.int16, device="cuda")
+    y = torch.empty((4, shape.hidden), dtype=torch.float32, device="cuda")
+    with pytest.raises(mb.MoeError) as ei:
+        mb.layer_forward(dl, x, y, ws, opts=mb.forward_opts(act_quant=1))
+    assert ei.value.status == mb.MOE_ERR_UNSUPPORTED
