@@ -48,7 +48,12 @@ WORKLOADS = {
     "batch16-stack-int4": 3,
     "prefill-int4": 4,
     "tiny-int8": 0,
+    "prefill-int8-w8a8": 4,  # the prefill chunk with int8 row-scaled weights and int8 activations
 }
+# per-workload changes of the configuration's shape and per-call options
+WORKLOAD_SHAPE = {"prefill-int8-w8a8": {"fmt": 1}}
+WORKLOAD_OPTS = {"prefill-int8-w8a8": {"act_quant": 1}}
+INT8_PEAK_TOPS = 5033.2  # MI355X dense int8 MFMA
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA % (prefill), 1 GPU"
 
 
@@ -106,18 +111,54 @@ def hip_elapsed_ms(start, stop) -> float:
     return float(ms.value)
 
 
+def copy_ceiling_gbs(torch, traffic_bytes, n_copies=60):
+    """HBM rate (GB/s of traffic) of the runtime's plain device copy moving
+    the given number of bytes in one launch (half read, half written): the
+    streaming rate one launch of that size reaches, the practical ceiling
+    beside the 8 TB/s peak for a kernel of the same traffic.  The copies
+    rotate over at least 2 GiB of buffers so that none starts from data the
+    256 MB last-level cache still holds (for the larger sizes, where the
+    pool holds fewer buffers than copies, a source comes round again only
+    after 2 GiB of other sources)."""
+    half = max(int(traffic_bytes) // 2 // 256 * 256, 256)
+    n_src = max(2, min(n_copies, (2 << 30) // half + 1))
+    srcs = [torch.empty(half, dtype=torch.uint8, device="cuda").fill_(i & 0xFF) for i in range(n_src)]
+    dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for i in range(4):
+        dsts[i % 2].copy_(srcs[i % n_src])
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e-3 * 2.4e9))
+    a.record()
+    for i in range(n_copies):
+        dsts[i % 2].copy_(srcs[(i + 4) % n_src])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n_copies
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return 2 * half / (us * 1e-6) / 1e9
+
+
 class Workload:
     """Device-resident inputs of one workload and its step function."""
 
     def __init__(self, name, ring_size, torch, mb, synth):
+        import dataclasses
         self.name = name
         self.cfg = WORKLOADS[name]
-        self.shape = synth.CONFIGS[self.cfg]
+        self.shape = dataclasses.replace(synth.CONFIGS[self.cfg], **WORKLOAD_SHAPE.get(name, {}))
+        self.opts_kw = WORKLOAD_OPTS.get(name, {})
+        self.opts = mb.forward_opts(**self.opts_kw) if self.opts_kw else None
         self.torch, self.mb, self.synth = torch, mb, synth
         shp = self.shape
         self.T, self.H, self.E, self.K, self.F = shp.tokens, shp.hidden, shp.n_experts, shp.top_k, shp.ffn
         self.stack = self.cfg == 3
-        log(f"workload {name}: {synth.CONFIG_NAMES[self.cfg]}")
+        self.label = synth.CONFIG_NAMES[self.cfg]
+        if self.opts_kw.get("act_quant"):
+            self.label = self.label.replace("int4", "W8A8 (int8 row-scaled weights, int8 activations)")
+        log(f"workload {name}: {self.label}")
         t0 = time.time()
         if self.stack:
             self.layers = []
@@ -164,6 +205,7 @@ class Workload:
     def call(self, i, l, ids_out=None, opts=None):
         """Layer call l of step i."""
         mb = self.mb
+        opts = self.opts if opts is None else opts
         if self.stack:
             mb.layer_forward(self.layers[l], self.x0 if l == 0 else self.xin, self.y, self.ws,
                              res=self.res0 if l == 0 else self.res_l, topk_ids=ids_out, c_layer=self.c_layers[l],
@@ -229,7 +271,7 @@ def stage_times(wl, n_steps):
     c = 0
     for i in range(n_steps):
         for l in range(wl.calls_per_step):
-            opts = mb.forward_opts(events={st: ev[st][c] for st in ev})
+            opts = mb.forward_opts(events={st: ev[st][c] for st in ev}, **wl.opts_kw)
             wl.call(i, l, opts=opts)
             c += 1
     torch.cuda.synchronize()
@@ -266,19 +308,38 @@ def measure(wl, K_steps, warmup, reps, prof_steps):
     # expert rows)
     fused_down = T <= 8 and not wl.stack
     prefill = T > 16
-    # the SwiGLU rows between the two kernels: bf16 hi + lo (4 bytes an
-    # element) for decode calls, one fp16 plane (2 bytes) for prefill
-    act_b = 2 if prefill else 4
-    gateup_bytes = U * gu_bytes + sh_gu + T * H * 2 + (T * K * F + T * Fs) * act_b
-    down_out = T * H * 4 if fused_down else (T * K + (T if Fs else 0)) * H * 4
-    down_bytes = U * dn_bytes + sh_dn + (T * K * F + T * Fs) * act_b + down_out
+    w8a8 = bool(wl.opts_kw.get("act_quant"))
+    rows = T * K + (T if Fs else 0)
+    if w8a8:
+        # int8 x rows in, fp32 SwiGLU rows out; int8 SwiGLU rows in, fp32 rows out
+        gateup_bytes = U * gu_bytes + sh_gu + T * H + rows * F * 4
+        down_bytes = U * dn_bytes + sh_dn + rows * F + rows * H * 4
+    else:
+        # the SwiGLU rows between the two kernels: bf16 hi + lo (4 bytes an
+        # element) for decode calls, one fp16 plane (2 bytes) for prefill
+        act_b = 2 if prefill else 4
+        gateup_bytes = U * gu_bytes + sh_gu + T * H * 2 + (T * K * F + T * Fs) * act_b
+        down_out = T * H * 4 if fused_down else (T * K + (T if Fs else 0)) * H * 4
+        down_bytes = U * dn_bytes + sh_dn + (T * K * F + T * Fs) * act_b + down_out
     kern = {"gateup": (gateup_bytes, stage_us["gateup"]), "down": (down_bytes, stage_us["down"])}
     dom = max(kern, key=lambda k: kern[k][1])
     dom_bytes, dom_us = kern[dom]
     kernel_name = {("gateup", False): "gateup_mfma_kernel",
                    ("down", False): "down_combine_kernel" if fused_down else "down_mfma_kernel",
                    ("gateup", True): "gateup_gemm128_kernel", ("down", True): "down_gemm_kernel"}[(dom, prefill)]
-    if prefill:
+    if w8a8:
+        kernel_name = "w8a8_gemm_kernel<true>" if dom == "gateup" else "w8a8_gemm_kernel<false>"
+        # int8 weights: the weight stream bounds these GEMMs (the int8 matrix
+        # work is a fifth of the weight-stream time at the peaks); the
+        # matrix-core fraction is reported beside it
+        ops = {"gateup": 2.0 * rows * 2 * H * F, "down": 2.0 * rows * H * F}[dom]
+        achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, kernel_name),
+                    "kernel": kernel_name, "kernel_us": dom_us, "kernel_bytes": dom_bytes, "kernel_int8_ops": ops,
+                    "int8_mfma_frac": ops / (dom_us * 1e-6) / 1e12 / INT8_PEAK_TOPS, "stage_us": stage_us,
+                    "copy_ceiling_gbs": copy_ceiling_gbs(torch, dom_bytes)}
+    elif prefill:
         # useful matrix-core work of the dominant grouped GEMM: every routed
         # and shared row through gate+up (2 H F each, 2 flops a product) or
         # down (H F), padding not counted
@@ -293,7 +354,8 @@ def measure(wl, K_steps, warmup, reps, prof_steps):
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, kernel_name),
-                    "kernel": kernel_name, "kernel_us": dom_us, "kernel_bytes": dom_bytes, "stage_us": stage_us}
+                    "kernel": kernel_name, "kernel_us": dom_us, "kernel_bytes": dom_bytes, "stage_us": stage_us,
+                    "copy_ceiling_gbs": copy_ceiling_gbs(torch, dom_bytes)}
     # whole-layer algorithmic bytes (router + unique experts + shared + x + y)
     layer_bytes = E * H * 4 + U * (gu_bytes + dn_bytes) + sh_gu + sh_dn + T * H * 2 + T * H * 4
     layer_ms = ms_per_step / wl.calls_per_step
@@ -302,7 +364,7 @@ def measure(wl, K_steps, warmup, reps, prof_steps):
         f"{gateup_bytes / (stage_us['gateup'] * 1e-6) / 1e9:.0f} GB/s; down {stage_us['down']:.2f} us -> "
         f"{down_bytes / (stage_us['down'] * 1e-6) / 1e9:.0f} GB/s; layer {layer_bytes / 1e6:.2f} MB -> "
         f"{layer_bytes / (layer_ms * 1e-3) / 1e9:.0f} GB/s")
-    config = {"workload": wl.synth.CONFIG_NAMES[wl.cfg], "tokens": T, "hidden": H, "experts": E, "top_k": K,
+    config = {"workload": wl.label, "tokens": T, "hidden": H, "experts": E, "top_k": K,
               "ffn": F, "shared_ffn": Fs, "layers_per_step": wl.calls_per_step,
               "distinct_layer_instances": len(wl.layers), "unique_experts_per_call": U,
               "layer_bytes": layer_bytes, "layer_us": layer_ms * 1e3,
@@ -310,7 +372,8 @@ def measure(wl, K_steps, warmup, reps, prof_steps):
     if wl.stack:
         config["stack_tokens_per_s"] = T / (ms_per_step * 1e-3)
     return {"value": tokens_per_s, "ms_per_step": ms_per_step, "ms_per_step_reps": per_rep,
-            "dtype": "int4-weights/bf16-act/f32-acc" if fmt == 2 else "int8-weights/bf16-act/f32-acc",
+            "dtype": ("int8-weights/int8-act/i32-acc" if w8a8 else
+                      "int4-weights/bf16-act/f32-acc" if fmt == 2 else "int8-weights/bf16-act/f32-acc"),
             "config": config, "roofline": roofline}
 
 
@@ -358,19 +421,29 @@ def main():
     ap.add_argument("--prof-steps", type=int, default=5, help="profiled steps after the timed repetitions")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="batch16-stack-int4")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="leave out the nested prefill-chunk measurement of the default line")
+                    help="leave out the nested prefill-chunk measurements (int4, and int8 W8A8) of the default line")
     ap.add_argument("--ring", type=int, default=40, help="distinct layer instances (decode workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (20 times), the known-size reference for "
                          "the HBM byte counters, and exit")
+    ap.add_argument("--copy-sweep", action="store_true",
+                    help="only time the plain device copy over a range of sizes (the streaming rate one launch of "
+                         "each size reaches) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the library runs on one GPU (expert-parallel sharding is a "
               "design note only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_sweep:
+        import torch
+        for mib in (4, 8, 16, 36, 64, 128, 256, 1024):
+            g = copy_ceiling_gbs(torch, mib << 20)
+            print(json.dumps({"copy_traffic_mib": mib, "GBps": g}), flush=True)
+        return
 
     if args.calibrate_copy_mib:
         import torch
@@ -393,14 +466,18 @@ def main():
     res = measure(wl, args.steps, args.warmup, args.reps, args.prof_steps)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seconds)
 
-    nested = None
+    nested = {}
     if args.workload == "batch16-stack-int4" and not args.no_prefill:
-        pf = Workload("prefill-int4", args.ring, torch, mb, synth)
-        r = measure(pf, args.steps, args.warmup, args.reps, args.prof_steps)
-        nested = {"metric": METRIC, "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
-                  "ms_per_step_reps": r["ms_per_step_reps"], "steps": args.steps, "dtype": r["dtype"],
-                  "config": r["config"], "roofline": r["roofline"]}
-        del pf
+        del wl  # frees the stack's 18 GB before the prefill layers are made
+        torch.cuda.empty_cache()
+        for key, name in (("prefill", "prefill-int4"), ("prefill_w8a8", "prefill-int8-w8a8")):
+            pf = Workload(name, args.ring, torch, mb, synth)
+            r = measure(pf, args.steps, args.warmup, args.reps, args.prof_steps)
+            nested[key] = {"metric": METRIC, "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+                           "ms_per_step_reps": r["ms_per_step_reps"], "steps": args.steps, "dtype": r["dtype"],
+                           "config": r["config"], "roofline": r["roofline"]}
+            del pf
+            torch.cuda.empty_cache()
 
     out = {
         "metric": METRIC,
@@ -421,8 +498,7 @@ def main():
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
     }
-    if nested is not None:
-        out["prefill"] = nested
+    out.update(nested)
     print(json.dumps(out), flush=True)
 
 
