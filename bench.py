@@ -9,9 +9,13 @@ stack of 40 distinct int4 layers with the residual epilogue between layers
 expert popularity; 18.3 GB of weights resident), the largest single-GPU
 workload.  The same line carries the 2048-token int4 prefill chunk as a
 nested object ("prefill") with its own roofline against the matrix-core
-peak.  Other primary workloads: --workload decode-int8 | mtp-verify-int4 |
-prefill-int4 | tiny-int8 (decode workloads rotate over a ring of 40 layer
-instances so that no call finds its weights in the 256 MB last-level cache).
+peak, and the same chunk in the W8A8 variant (int8 weights, int8
+activations: "prefill_w8a8") against the HBM peak.  Other primary workloads:
+--workload decode-int8 | mtp-verify-int4 | prefill-int4 | prefill-int8-w8a8
+| tiny-int8 (decode workloads rotate over a ring of 40 layer instances so
+that no call finds its weights in the 256 MB last-level cache).  Each HBM
+roofline also carries the rate a plain device copy of the same traffic
+reaches in one launch (copy_ceiling_gbs).
 
 Timing: W warm-up steps, then R repetitions (default 5) of K steps each,
 every repetition launched on one stream behind a bounded spin kernel long
@@ -116,12 +120,11 @@ def copy_ceiling_gbs(torch, traffic_bytes, n_copies=60):
     the given number of bytes in one launch (half read, half written): the
     streaming rate one launch of that size reaches, the practical ceiling
     beside the 8 TB/s peak for a kernel of the same traffic.  The copies
-    rotate over at least 2 GiB of buffers so that none starts from data the
-    256 MB last-level cache still holds (for the larger sizes, where the
-    pool holds fewer buffers than copies, a source comes round again only
-    after 2 GiB of other sources)."""
+    rotate over a pool of buffers so that none starts from data the
+    256 MB last-level cache still holds: the sources together hold at least
+    1 GiB, and one comes round again only after all the others."""
     half = max(int(traffic_bytes) // 2 // 256 * 256, 256)
-    n_src = max(2, min(n_copies, (2 << 30) // half + 1))
+    n_src = max(2, min(512, (1 << 30) // half + 1))
     srcs = [torch.empty(half, dtype=torch.uint8, device="cuda").fill_(i & 0xFF) for i in range(n_src)]
     dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(2)]
     for i in range(4):
