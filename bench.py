@@ -265,7 +265,7 @@ def stage_times(wl, n_steps):
     stream = torch.cuda.current_stream()
     n_calls = n_steps * wl.calls_per_step
     ev = {st: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n_calls)] for st in ("gateup", "down")}
+               for _ in range(n_calls)] for st in ("route", "gateup", "down")}
     for st in ev:  # torch creates the HIP event at its first record
         for a_, b_ in ev[st]:
             a_.record(stream)

@@ -266,15 +266,31 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
       const int i = tid + b * blockDim.x;
       xv[b] = i < T * pieces ? reinterpret_cast<const uint4 *>(a.x)[i] : make_uint4(0, 0, 0, 0);
     }
+    // the x rows go to LDS while the partial logits are in flight
+    auto stage_xv = [&]() {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i = tid + b * blockDim.x;
+        if (i < T * pieces) {
+          const int t = i / pieces, k = i - t * pieces;
+          uint4 o = xv[b];
+          if constexpr (kInt4) {
+            const u32x4_t pp = pair_permute(xv[b]);
+            o = make_uint4(pp.x, pp.y, pp.z, pp.w);
+          }
+          xs_lds[t * xstride + k] = o;
+        }
+      }
+    };
     // every block routes the batch (the last block, which has the fewest
     // items, also publishes it)
     const int npl = (a.route.E + 63) / 64;
     if (npl <= 1)
-      route_in_block_small<1>(a.route, L, blockIdx.x == gridDim.x - 1);
+      route_in_block_small<1>(a.route, L, blockIdx.x == gridDim.x - 1, stage_xv);
     else if (npl <= 2)
-      route_in_block_small<2>(a.route, L, blockIdx.x == gridDim.x - 1);
+      route_in_block_small<2>(a.route, L, blockIdx.x == gridDim.x - 1, stage_xv);
     else
-      route_in_block_small<4>(a.route, L, blockIdx.x == gridDim.x - 1);  // E <= 256 on this path
+      route_in_block_small<4>(a.route, L, blockIdx.x == gridDim.x - 1, stage_xv);  // E <= 256 on this path
     U = L.n_active;
   } else {
     U = routed_units(a);
@@ -311,19 +327,6 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
       tab[tid][3] = f0;
 #pragma unroll
       for (int m = 0; m < 16; ++m) toks[tid][m] = m < nn ? (e < 0 ? m : L.row_tok[r0 + m]) : 0;
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = tid + b * blockDim.x;
-      if (i < T * pieces) {
-        const int t = i / pieces, k = i - t * pieces;
-        uint4 o = xv[b];
-        if constexpr (kInt4) {
-          const u32x4_t pp = pair_permute(xv[b]);
-          o = make_uint4(pp.x, pp.y, pp.z, pp.w);
-        }
-        xs_lds[t * xstride + k] = o;
-      }
     }
     if (T * pieces > 4 * static_cast<int>(blockDim.x)) {  // the rest of the rows
       for (int base = tid + 4 * blockDim.x; base < T * pieces; base += blockDim.x) {

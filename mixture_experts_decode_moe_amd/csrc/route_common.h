@@ -33,6 +33,20 @@ MOE_DEV uint32_t wave_max_u32(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
+// Wave-wide maximum left in every lane, on the vector unit only: row
+// maxima through DPP, then the four rows through the gfx950 permlane swaps
+// (no lane reads, so no round trip through scalar registers).
+MOE_DEV uint32_t wave_max_all_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max(static_cast<uint32_t>(p[0]), static_cast<uint32_t>(p[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(static_cast<uint32_t>(q[0]), static_cast<uint32_t>(q[1]));
+}
+
 // Wave-wide minimum (uniform result).
 MOE_DEV uint32_t wave_min_u32(uint32_t v) {
   v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
@@ -104,34 +118,34 @@ MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t reno
       cswap(1, 3);
       cswap(1, 2);
     }
-    float top_v = 0.f;
-    float my_v = 0.f;  // lane k keeps round k's value and index
+    // Each round: the maximum in every lane, the winning lane (the lowest
+    // expert among equal keys, rare), the winner's expert by one lane read,
+    // and the winner's list shifted with selects (no branch, no exec-mask
+    // copies); lane k keeps round k's key and expert.
+    uint32_t my_key = 0u;
     my_e = 0;
     for (int k = 0; k < K; ++k) {
-      const uint32_t m = wave_max_u32(key[0]);
-      const uint64_t hit = __ballot(key[0] == m);
-      int sel;
-      if (__popcll(hit) == 1) {
-        sel = __builtin_amdgcn_readlane(idx[0], __builtin_ctzll(hit));
-      } else {
-        sel = static_cast<int>(wave_min_u32(key[0] == m ? static_cast<uint32_t>(idx[0]) : 0xFFFFFFFFu));
+      const uint32_t m = wave_max_all_u32(key[0]);
+      bool win = key[0] == m;
+      uint64_t hit = __ballot(win);
+      if (__popcll(hit) != 1) {
+        const uint32_t lo = wave_min_u32(win ? static_cast<uint32_t>(idx[0]) : 0xFFFFFFFFu);
+        win = win && static_cast<uint32_t>(idx[0]) == lo;
+        hit = __ballot(win);
       }
-      if ((sel & 63) == lane) {  // the winner drops its first pair
+      const int sel = __builtin_amdgcn_readlane(idx[0], __builtin_ctzll(hit));
 #pragma unroll
-        for (int j = 0; j + 1 < NPL; ++j) {
-          key[j] = key[j + 1];
-          idx[j] = idx[j + 1];
-        }
-        key[NPL - 1] = 0u;
+      for (int j = 0; j + 1 < NPL; ++j) {
+        key[j] = win ? key[j + 1] : key[j];
+        idx[j] = win ? idx[j + 1] : idx[j];
       }
-      const float sel_v = key_float(m);
-      if (k == 0) top_v = sel_v;
-      if (lane == k) {
-        my_v = sel_v;
-        my_e = sel;
-      }
+      key[NPL - 1] = win ? 0u : key[NPL - 1];
+      const bool mine = lane == k;
+      my_key = mine ? m : my_key;
+      my_e = mine ? sel : my_e;
     }
-    my_w = topk_weight<NPL>(v, E, K, renorm, my_v, top_v);
+    const float top_v = key_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(my_key, 0)));
+    my_w = topk_weight<NPL>(v, E, K, renorm, key_float(my_key), top_v);
     return;
   }
   uint32_t key[NPL];  // 0 = used or absent
@@ -381,8 +395,15 @@ MOE_DEV int wave_incl_sum(int x) {
 // then places pairs (route_small_rows).  The phases are separated by block
 // barriers, so a caller can start work that needs only the active list
 // before the rows are placed.  Results are identical to route_in_block's.
-template <int NPL>
-MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish) {
+// `stage` runs once per wave, after the wave's first partial-logit
+// requests are out and before they are used (the gate/up kernel stages its
+// x rows there, so their wait overlaps the partials' round trip).
+struct NoStage {
+  MOE_DEV void operator()() const {}
+};
+
+template <int NPL, class Stage = NoStage>
+MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish, const Stage &stage = Stage()) {
   static_assert(NPL <= 4, "E <= 256");
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -390,6 +411,11 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
   const int T = a.T, E = a.E, S = a.S, K = a.K, Ep = a.Ep;
   const int mwords = (E + 31) / 32;  // <= 8
   const int N = a.tail_skip > 0 ? min(a.tail_skip, K) : 0;
+  // the bias (when there is one) requested with the first partials
+  float bias[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) bias[j] = a.router_bias ? a.router_bias[min(lane + 64 * j, E - 1)] : 0.f;
+  bool staged = false;
   for (int t = wave; t < T; t += nw) {
     const float *__restrict__ part = a.part;
     float acc[NPL];
@@ -407,6 +433,10 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
           const int sl = min(s0 + q, S - 1);
           pv[j][q] = part[(static_cast<size_t>(sl) * T + t) * Ep + ex];
         }
+      if (!staged) {
+        stage();
+        staged = true;
+      }
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
 #pragma unroll
@@ -416,7 +446,7 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int ex = lane + 64 * j;
-      const float sum = acc[j] + (a.router_bias && ex < E ? a.router_bias[ex] : 0.f);
+      const float sum = acc[j] + (a.router_bias && ex < E ? bias[j] : 0.f);
       v[j] = (ex < E && sum == sum) ? sum : -INFINITY;  // NaN never outranks a number
       if (publish && a.logits && ex < E) a.logits[static_cast<size_t>(t) * E + ex] = sum;
     }
@@ -444,6 +474,7 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
       if (publish && lane == 0) a.gate[t] = gv;
     }
   }
+  if (!staged) stage();
 }
 
 // Wave 0 only, after route_small_topk and a block barrier.
@@ -519,9 +550,9 @@ MOE_DEV void route_small_rows(const RouteFusedArgs &a, RouteLds &L, bool publish
   }
 }
 
-template <int NPL>
-MOE_DEV void route_in_block_small(const RouteFusedArgs &a, RouteLds &L, bool publish) {
-  route_small_topk<NPL>(a, L, publish);
+template <int NPL, class Stage = NoStage>
+MOE_DEV void route_in_block_small(const RouteFusedArgs &a, RouteLds &L, bool publish, const Stage &stage = Stage()) {
+  route_small_topk<NPL>(a, L, publish, stage);
   lds_barrier();
   if ((threadIdx.x >> 6) == 0) route_small_scan(a, L, publish);
   lds_barrier();

@@ -103,26 +103,30 @@ def test_prefill_repeated_calls_one_workspace(mb):
         assert np.array_equal(again["y"], first["y"]), f"call {rep + 2}: bits differ from the first call"
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_small_batch_one_launch_down_combine(mb, cfg):
-    """Batches of up to eight tokens run the down projection and the combine
-    as one launch, larger ones as two; a token's output must carry the same
-    bits either way (int8 and int4), and match the oracle."""
+    """Decode batches of up to eight tokens without the normalised residual
+    copy run the down projection and the combine as one launch; larger
+    batches, and calls that ask for the normalised copy, take two.  A
+    token's output and residual sum must carry the same bits either way
+    (int8 and int4), and match the oracle."""
     import parity_util as pu
-    shape = _shape(cfg, tokens=12, correlated_sigma=0.0, seed=70 + cfg)
+    shape = _shape(cfg, tokens=16, correlated_sigma=0.0, seed=70 + cfg, **({"layers": 1} if cfg == 3 else {}))
     layer = synth.make_layer(shape)
     x = synth.make_x(shape)
+    r = synth.make_x(shape, seed=170 + cfg)
     dl = mb.layer_to_device(layer)
-    say(f"one-launch down+combine cfg{cfg}: T=12 reference")
-    full = pu.run_layer(dl, pu.dev_u16(x), 12, with_logits=False)
-    for T in (1, 2, 5, 8):
+    say(f"one-launch down+combine cfg{cfg}: T=16 two-launch reference")
+    full = pu.run_layer(dl, pu.dev_u16(x), 16, residual=pu.dev_u16(r), normed=True, with_logits=False)
+    for T in (1, 2, 5, 8, 9, 12, 16):
         say(f"  T={T}")
-        part = pu.run_layer(dl, pu.dev_u16(x[:T]), T)
+        part = pu.run_layer(dl, pu.dev_u16(x[:T]), T, residual=pu.dev_u16(r[:T]), normed=False)
         assert np.array_equal(part["ids"], full["ids"][:T])
         assert np.array_equal(part["y"], full["y"][:T]), f"T={T}: bits differ from the two-launch path"
-        if T == 5:
+        assert np.array_equal(part["residual_out"], full["residual_out"][:T]), f"T={T}: residual sum differs"
+        if T in (5, 16):
             err, ties = pu.check_layer_against_oracle(layer, x[:T], part)
-            say(f"  T=5: rel err {err:.2e}, near ties {ties}")
+            say(f"  T={T}: rel err {err:.2e}, near ties {ties}")
 
 
 def test_small_batch_residual_without_norm(mb):
