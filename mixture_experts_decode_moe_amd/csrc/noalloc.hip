@@ -45,9 +45,10 @@ void *device_scratch(hipStream_t s) {
 extern "C" int moe_layer_forward_noalloc(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y,
                                          const moe_residual *res, int32_t *topk_ids, float *topk_w,
                                          const moe_forward_opts *opts, void *stream) {
-  const size_t need = moe_workspace_bytes(L, T);
-  // invalid layers and token counts: the same validation and status as the
-  // workspace entry point (nothing is launched)
+  const size_t need = T > 0 ? moe_workspace_bytes(L, T) : 0;
+  // invalid layers and token counts, and calls without tokens: the same
+  // validation and status as the workspace entry point, which launches
+  // nothing for them (and no device is touched)
   if (need == 0) return moe_layer_forward_ex(L, x_bf16, T, y, res, topk_ids, topk_w, nullptr, 0, opts, stream);
   if (need > kScratchBytes) return MOE_ERR_UNSUPPORTED;  // beyond the fixed scratch array
   hipStream_t s = static_cast<hipStream_t>(stream);
