@@ -72,7 +72,7 @@ MOE_DEV PfUnit pf_unit(const FfnArgs &a, int u) {
 // Fills pre[u] = first row tile of unit u (exclusive prefix of the row
 // tiles), pre[n_units] = total; returns the number of units.
 // NT threads (scratch holds NT / 64 ints).
-template <int NT = kPfThreads>
+template <int NT = kPfThreads, int ROWS = kPfRows>
 MOE_DEV int pf_tiles(const FfnArgs &a, int *pre, int *scratch) {
   const int n_units = (a.Fs > 0 ? 1 : 0) + routed_units(a);
   const int tid = threadIdx.x;
@@ -85,7 +85,7 @@ MOE_DEV int pf_tiles(const FfnArgs &a, int *pre, int *scratch) {
     int c = 0;
     if (u < n_units) {
       const PfUnit x = pf_unit(a, u);
-      c = x.n > 0 ? (x.n + kPfRows - 1) / kPfRows : 0;
+      c = x.n > 0 ? (x.n + ROWS - 1) / ROWS : 0;
     }
     cnt[i] = c;
     mine += c;
@@ -1248,12 +1248,18 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
 // (one rounded product), clamped to [-127, 127]; amax = 0 gives q = 0, d = 0.
 // Every decision in float32, as the reference statement of the variant.
 //
-// GEMM tiles.  An item is (unit, 64 rows, 128 output columns); each of the 4
-// waves owns 32 of the columns for all 64 rows (two 32x32 tiles along M;
-// gate/up: the gate and the up tile of its 32 SwiGLU columns).  Operands go
-// straight from global memory (through the caches) into registers: lane l
-// supplies row / column l % 32 and the 16 consecutive k of group l / 32 of
-// each 32-wide step, two steps requested ahead.
+// GEMM tiles.  An item is (unit, up to 128 rows, 128 output columns): with
+// 64 rows an expert on average (at most about 90 for uniform routing), one
+// item covers all of an expert's rows, so every weight is read once.  Each
+// of the 4 waves owns 32 of the columns for all the rows (four 32x32 tiles
+// along M; gate/up: the gate and the up tile of its 32 SwiGLU columns).
+// Operands go straight from global memory (through the caches) into
+// registers: lane l supplies row / column l % 32 and the 16 consecutive k
+// of group l / 32 of each 32-wide step, two steps requested ahead.  One
+// block per compute unit (the 128 accumulator registers of the gate/up
+// tiles leave room for one wave a SIMD; splitting the rows over 8 waves, two
+// a SIMD, measured slower: 361 against 288 us for the prefill chunk's
+// gate/up).
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
@@ -1309,6 +1315,9 @@ __global__ void __launch_bounds__(kQrThreads) quant_rows_kernel(const In *__rest
 }
 
 constexpr int kW8Cols = 128;  // output columns per item (gate/up: SwiGLU columns)
+constexpr int kW8Rows = 128;  // rows per item
+constexpr int kW8Threads = 256;      // 4 waves, one per 32-column group
+constexpr int kW8Mt = kW8Rows / 32;  // 32-row tiles per wave
 static int pf_grid(int items_upper);
 
 MOE_DEV i32x4_t load_i8x16(const int8_t *p) {
@@ -1321,34 +1330,36 @@ MOE_DEV i32x4_t load_i8x16(const int8_t *p) {
 // rows_out[row][h] = I dA[row] sd[h] w[row], the rows' quantised SwiGLU
 // rows against the down rows h.
 template <bool GATEUP>
-__global__ void __launch_bounds__(kPfThreads) w8a8_gemm_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(kW8Threads) w8a8_gemm_kernel(FfnArgs a) {
   __shared__ int pre[kPfMaxUnits + 1];
-  __shared__ int scratch[4];
-  __shared__ int rtok[kPfRows];    // GATEUP: token of each tile row; down: its act row
-  __shared__ float rscale[kPfRows];  // the row's activation scale (x weight for down)
+  __shared__ int scratch[kW8Threads / 64];
+  __shared__ int rtok[kW8Rows];      // GATEUP: token of each tile row; down: its act row
+  __shared__ float rscale[kW8Rows];  // the row's activation scale (x weight for down)
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int c = lane & 31, kg = lane >> 5;
   const int H = a.H, T = a.T;
-  const int K = GATEUP ? H : a.F;        // reduction
-  const int N = GATEUP ? a.F : H;        // output columns (SwiGLU columns for gate/up)
-  const int n_units = pf_tiles(a, pre, scratch);
+  const int K = GATEUP ? H : a.F;  // reduction
+  const int N = GATEUP ? a.F : H;  // output columns (SwiGLU columns for gate/up)
+  const int n_units = pf_tiles<kW8Threads, kW8Rows>(a, pre, scratch);
+  const int mg = 0, cw = wave;  // this wave's rows (all) and column group
   const int col_groups = N / kW8Cols;
   const int n_items = pre[n_units] * col_groups;
   const int steps = K / 32;
+  constexpr int NB = GATEUP ? 2 : 1;  // B tiles: gate and up, or down
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int j = item / col_groups;
     const int cg = item - j * col_groups;
     const int u = pf_find(pre, n_units, j);
     const PfUnit un = pf_unit(a, u);
-    const int m0 = (j - pre[u]) * kPfRows;  // first row of the tile inside the unit
-    const int rows = min(kPfRows, un.n - m0);
+    const int m0 = (j - pre[u]) * kW8Rows;  // first row of the tile inside the unit
+    const int rows = min(kW8Rows, un.n - m0);
     const bool shared = un.e < 0;
     const int e = shared ? 0 : un.e;
     lds_barrier();  // the previous item's readers of rtok / rscale are done
-    if (tid < kPfRows) {
+    if (tid < kW8Rows) {
       int t = 0;
       float sc = 0.f;
       if (tid < rows) {
@@ -1366,52 +1377,56 @@ __global__ void __launch_bounds__(kPfThreads) w8a8_gemm_kernel(FfnArgs a) {
       rscale[tid] = sc;
     }
     lds_barrier();
-    // this lane's A rows (two 32-row tiles) and B columns
-    const int8_t *ap[2];
+    // this lane's A rows (one per 32-row tile; rows past the tile's end read
+    // row 0 and multiply zeros) and B columns
+    const int8_t *ap[kW8Mt];
+    bool mv[kW8Mt];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int r = 32 * mt + c;
-      const int src = rtok[r < rows ? r : 0];
+    for (int mt = 0; mt < kW8Mt; ++mt) {
+      const int r = 32 * kW8Mt * mg + 32 * mt + c;
+      mv[mt] = r < rows;
+      const int src = rtok[mv[mt] ? r : 0];
       ap[mt] = (GATEUP ? a.qx + static_cast<size_t>(src) * H : a.qa + static_cast<size_t>(src) * a.F) + 16 * kg;
     }
-    const int col = cg * kW8Cols + 32 * wave + c;
-    const int8_t *bp0, *bp1;
+    const int col = cg * kW8Cols + 32 * cw + c;
+    const int8_t *bp[NB];
     if (GATEUP) {
       const int8_t *gq = static_cast<const int8_t *>(shared ? a.sgq : a.gq);
       const int8_t *uq = static_cast<const int8_t *>(shared ? a.suq : a.uq);
       const size_t row = static_cast<size_t>(e) * (shared ? a.Fs : a.F) + col;
-      bp0 = gq + row * H + 16 * kg;
-      bp1 = uq + row * H + 16 * kg;
+      bp[0] = gq + row * H + 16 * kg;
+      bp[NB - 1] = uq + row * H + 16 * kg;
     } else {
       const int8_t *dq = static_cast<const int8_t *>(shared ? a.sdq : a.dq);
-      bp0 = dq + (static_cast<size_t>(e) * H + col) * a.F + 16 * kg;
-      bp1 = bp0;
+      bp[0] = dq + (static_cast<size_t>(e) * H + col) * a.F + 16 * kg;
     }
-    const bool mv0 = c < rows, mv1 = 32 + c < rows;
-    i32x16_t acc[2][2];  // [B tile (gate, up)][M tile]
+    // this wave's row tiles that hold rows (wave-uniform; none: the wave
+    // only waits at the barriers)
+    const int mts = min(kW8Mt, max(0, (rows - 32 * kW8Mt * mg + 31) / 32));
+    i32x16_t acc[NB][kW8Mt];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < kW8Mt; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[b][mt][r] = 0;
     // two steps in flight: operands of step s + 2 requested before step s is multiplied
-    i32x4_t A0[3], A1[3], B0[3], B1[3];
+    i32x4_t A[3][kW8Mt], B[3][NB];
+    const i32x4_t z4 = {0, 0, 0, 0};
     auto load = [&](int s, int slot) __attribute__((always_inline)) {
       const int ks = min(s, steps - 1) * 32;  // past the end: re-request the last step
-      A0[slot] = load_i8x16(ap[0] + ks);
-      A1[slot] = load_i8x16(ap[1] + ks);
-      B0[slot] = load_i8x16(bp0 + ks);
-      if (GATEUP) B1[slot] = load_i8x16(bp1 + ks);
+#pragma unroll
+      for (int mt = 0; mt < kW8Mt; ++mt) A[slot][mt] = mt < mts ? load_i8x16(ap[mt] + ks) : z4;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) B[slot][b] = load_i8x16(bp[b] + ks);
     };
-    const i32x4_t z4 = {0, 0, 0, 0};
     auto step = [&](int slot) __attribute__((always_inline)) {
-      const i32x4_t a0 = mv0 ? A0[slot] : z4, a1 = mv1 ? A1[slot] : z4;
-      acc[0][0] = mfma_i8(a0, B0[slot], acc[0][0]);
-      acc[0][1] = mfma_i8(a1, B0[slot], acc[0][1]);
-      if (GATEUP) {
-        acc[1][0] = mfma_i8(a0, B1[slot], acc[1][0]);
-        acc[1][1] = mfma_i8(a1, B1[slot], acc[1][1]);
+#pragma unroll
+      for (int mt = 0; mt < kW8Mt; ++mt) {
+        if (mt >= mts) break;  // wave-uniform
+        const i32x4_t av = mv[mt] ? A[slot][mt] : z4;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][mt] = mfma_i8(av, B[slot][b], acc[b][mt]);
       }
     };
     load(0, 0);
@@ -1439,14 +1454,14 @@ __global__ void __launch_bounds__(kPfThreads) w8a8_gemm_kernel(FfnArgs a) {
       const size_t srow = static_cast<size_t>(e) * (shared ? a.Fs : a.F) + col;
       const float sg = gs[srow], su = us[srow];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < kW8Mt; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = 32 * mt + 8 * (r >> 2) + 4 * kg + (r & 3);
+          const int m = 32 * kW8Mt * mg + 32 * mt + 8 * (r >> 2) + 4 * kg + (r & 3);
           if (m < rows) {
             const float dxr = rscale[m];
             const float gv = static_cast<float>(acc[0][mt][r]) * dxr * sg;
-            const float uv = static_cast<float>(acc[1][mt][r]) * dxr * su;
+            const float uv = static_cast<float>(acc[NB - 1][mt][r]) * dxr * su;
             const int rr = m0 + m;
             const size_t arow = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(un.r0) + rr;
             a.act[arow * a.F + col] = gv / (1.f + expf(-gv)) * uv;
@@ -1455,10 +1470,10 @@ __global__ void __launch_bounds__(kPfThreads) w8a8_gemm_kernel(FfnArgs a) {
     } else {
       const float sd = static_cast<const float *>(shared ? a.sds : a.ds)[static_cast<size_t>(e) * H + col];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < kW8Mt; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = 32 * mt + 8 * (r >> 2) + 4 * kg + (r & 3);
+          const int m = 32 * kW8Mt * mg + 32 * mt + 8 * (r >> 2) + 4 * kg + (r & 3);
           if (m < rows) {
             const float v = static_cast<float>(acc[0][mt][r]) * rscale[m] * sd;
             a.rows_out[static_cast<size_t>(rtok[m]) * H + col] = v;
@@ -1466,6 +1481,16 @@ __global__ void __launch_bounds__(kPfThreads) w8a8_gemm_kernel(FfnArgs a) {
         }
     }
   }
+}
+
+// Blocks of a W8A8 GEMM launch: one per compute unit (fewer for fewer items).
+static int w8_grid(int items_upper) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  return items_upper < 1 ? 1 : (items_upper < cus ? items_upper : cus);
 }
 
 bool w8a8_ok(const FfnArgs &a) {
@@ -1482,15 +1507,15 @@ hipError_t launch_w8a8(const FfnArgs &a, hipStream_t s, const LaunchEvents &ev_g
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1);
-  const int tiles = (a.n_rows + kPfRows - 1) / kPfRows + units + (a.Fs > 0 ? (a.T + kPfRows - 1) / kPfRows : 0);
-  e = launch_kernel(w8a8_gemm_kernel<true>, dim3(pf_grid(tiles * (a.F / kW8Cols))), dim3(kPfThreads), 0, s, ev_gu, a);
+  const int tiles = (a.n_rows + kW8Rows - 1) / kW8Rows + units + (a.Fs > 0 ? (a.T + kW8Rows - 1) / kW8Rows : 0);
+  e = launch_kernel(w8a8_gemm_kernel<true>, dim3(w8_grid(tiles * (a.F / kW8Cols))), dim3(kW8Threads), 0, s, ev_gu, a);
   if (e != hipSuccess) return e;
   // every SwiGLU row (routed, then the shared expert's), quantised per row
   const int rows_all = a.n_rows + (a.Fs > 0 ? a.T : 0);
   quant_rows_kernel<float><<<rows_all, kQrThreads, 0, s>>>(a.act, a.F, a.qa, a.da);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_kernel(w8a8_gemm_kernel<false>, dim3(pf_grid(tiles * (a.H / kW8Cols))), dim3(kPfThreads), 0, s, ev_dn,
+  return launch_kernel(w8a8_gemm_kernel<false>, dim3(w8_grid(tiles * (a.H / kW8Cols))), dim3(kW8Threads), 0, s, ev_dn,
                        a);
 }
 
