@@ -29,6 +29,8 @@
 // enumerated once per block into an LDS table.
 #include <math.h>
 
+#include <utility>
+
 #include "mfma_common.h"
 
 namespace moe {
@@ -1248,18 +1250,17 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
 // (one rounded product), clamped to [-127, 127]; amax = 0 gives q = 0, d = 0.
 // Every decision in float32, as the reference statement of the variant.
 //
-// GEMM tiles.  An item is (unit, up to 128 rows, 128 output columns): with
-// 64 rows an expert on average (at most about 90 for uniform routing), one
-// item covers all of an expert's rows, so every weight is read once.  Each
-// of the 4 waves owns 32 of the columns for all the rows (four 32x32 tiles
-// along M; gate/up: the gate and the up tile of its 32 SwiGLU columns).
-// Operands go straight from global memory (through the caches) into
-// registers: lane l supplies row / column l % 32 and the 16 consecutive k
-// of group l / 32 of each 32-wide step, two steps requested ahead.  One
-// block per compute unit (the 128 accumulator registers of the gate/up
-// tiles leave room for one wave a SIMD; splitting the rows over 8 waves, two
-// a SIMD, measured slower: 361 against 288 us for the prefill chunk's
-// gate/up).
+// GEMM tiles.  An item is (unit, up to 128 rows, 128 SwiGLU columns for
+// gate/up, 256 output columns for down): with 64 rows an expert on average
+// (at most about 90 for uniform routing), one item covers all of an
+// expert's rows, so every weight is read once.  Both operands go from
+// global memory straight into LDS (direct loads, no registers), two k-steps
+// of 128 ahead, into three buffers each, as in gateup_gemm128_kernel: each
+// 128-byte row segment's eight 16-byte pieces are stored at slot
+// piece ^ (row & 7), so that the operand reads (32 rows at one piece) spread
+// over the banks, and every request covers whole 128-byte lines.  Each of
+// the 8 waves owns 32 output columns (gate/up: the gate and the up rows of
+// 16 SwiGLU columns) for all the item's rows, four 32x32 tiles along M.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
@@ -1314,176 +1315,231 @@ __global__ void __launch_bounds__(kQrThreads) quant_rows_kernel(const In *__rest
   if (tid == 0) d[row] = amax > 0.f ? amax / 127.f : 0.f;
 }
 
-constexpr int kW8Cols = 128;  // output columns per item (gate/up: SwiGLU columns)
 constexpr int kW8Rows = 128;  // rows per item
-constexpr int kW8Threads = 256;      // 4 waves, one per 32-column group
-constexpr int kW8Mt = kW8Rows / 32;  // 32-row tiles per wave
+constexpr int kW8Step = 128;  // k (bytes of an int8 row) per step
 static int pf_grid(int items_upper);
 
-MOE_DEV i32x4_t load_i8x16(const int8_t *p) {
-  const uint4 v = *reinterpret_cast<const uint4 *>(p);
-  return i32x4_t{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
+// step(IntC<0>), ..., step(IntC<KS - 1>) as straight-line code (the k loops
+// are unrolled whole: see gateup_gemm128_kernel)
+template <class Fn, int... S>
+MOE_DEV void unrolled_steps(std::integer_sequence<int, S...>, Fn &&step) {
+  (step(IntC<S>{}), ...);
 }
 
-// GATEUP: a[row][f] = silu(g) u with g = I_g dx[t] sg[f] (and u alike), the
-// rows' tokens' inputs against the gate and up rows f.  Otherwise (down):
-// rows_out[row][h] = I dA[row] sd[h] w[row], the rows' quantised SwiGLU
-// rows against the down rows h.
-template <bool GATEUP>
-__global__ void __launch_bounds__(kW8Threads) w8a8_gemm_kernel(FfnArgs a) {
-  __shared__ int pre[kPfMaxUnits + 1];
-  __shared__ int scratch[kW8Threads / 64];
-  __shared__ int rtok[kW8Rows];      // GATEUP: token of each tile row; down: its act row
-  __shared__ float rscale[kW8Rows];  // the row's activation scale (x weight for down)
+// The W8A8 GEMM.  GATEUP: a[row][f] = silu(g) u with g = I_g dx[t] sg[f]
+// (and u alike), the rows' tokens' quantised inputs against the gate and
+// up rows f; K = H.  Otherwise (down): rows_out[row][h] = I dA[row] w[row]
+// sd[h], the rows' quantised SwiGLU rows against the down rows h; K = F.
+// KS = K / 128 steps, unrolled.
+template <bool GATEUP, int KS>
+__global__ void __launch_bounds__(kGmThreads) w8a8_gemm_kernel(FfnArgs a) {
+  // three A buffers (128 rows x eight 16-byte pieces) and three weight
+  // buffers (256 rows x eight pieces): separate arrays, so that the
+  // compiler sees that the LDS reads of a step do not touch the buffers its
+  // direct loads are filling
+  __shared__ uint4 w8_a0[kW8Rows * 8], w8_a1[kW8Rows * 8], w8_a2[kW8Rows * 8];
+  __shared__ uint4 w8_b0[256 * 8], w8_b1[256 * 8], w8_b2[256 * 8];
+  __shared__ GmUnits units;
+  __shared__ int scratch[kGmThreads / 64];
+  __shared__ float rsc[kW8Rows];  // the row's activation scale (x routing weight for down)
+  __shared__ int arow[kW8Rows];   // down: the row's act row (= its output row)
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int c = lane & 31, kg = lane >> 5;
-  const int H = a.H, T = a.T;
-  const int K = GATEUP ? H : a.F;  // reduction
-  const int N = GATEUP ? a.F : H;  // output columns (SwiGLU columns for gate/up)
-  const int n_units = pf_tiles<kW8Threads, kW8Rows>(a, pre, scratch);
-  const int mg = 0, cw = wave;  // this wave's rows (all) and column group
-  const int col_groups = N / kW8Cols;
-  const int n_items = pre[n_units] * col_groups;
-  const int steps = K / 32;
-  constexpr int NB = GATEUP ? 2 : 1;  // B tiles: gate and up, or down
+  const int c = lane & 31, h = lane >> 5;
+  const int T = a.T;
+  const int K = kW8Step * KS;
+  const int n_units = gm_units<kW8Rows>(a, units, scratch);
+  const int NC = GATEUP ? 128 : 256;  // output columns of an item
+  const int col_groups = (GATEUP ? a.F : a.H) / NC;
+  const int n_items = units.pre[n_units] * col_groups;
+  auto abuf = [&](int b) __attribute__((always_inline)) { return b == 0 ? w8_a0 : b == 1 ? w8_a1 : w8_a2; };
+  auto bbuf = [&](int b) __attribute__((always_inline)) { return b == 0 ? w8_b0 : b == 1 ? w8_b1 : w8_b2; };
+  // this lane's operand row of the weight tile: gate/up: the gate (c < 16)
+  // or up (c >= 16) row of SwiGLU column 16 wave + c % 16; down: column
+  // 32 wave + c
+  const int Rm = GATEUP ? (c >= 16 ? 128 : 0) + 16 * wave + (c & 15) : 32 * wave + c;
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int j = item / col_groups;
     const int cg = item - j * col_groups;
-    const int u = pf_find(pre, n_units, j);
-    const PfUnit un = pf_unit(a, u);
-    const int m0 = (j - pre[u]) * kW8Rows;  // first row of the tile inside the unit
+    const int u = pf_find(units.pre, n_units, j);
+    const PfUnit un = gm_unit(units, u);
+    const int m0 = (j - units.pre[u]) * kW8Rows;
     const int rows = min(kW8Rows, un.n - m0);
     const bool shared = un.e < 0;
     const int e = shared ? 0 : un.e;
-    lds_barrier();  // the previous item's readers of rtok / rscale are done
+    lds_barrier();  // the previous item's readers of rsc / arow are done
     if (tid < kW8Rows) {
-      int t = 0;
       float sc = 0.f;
+      int ar = 0;
       if (tid < rows) {
         const int rr = un.r0 + m0 + tid;  // routed: row index; shared: token
         if (GATEUP) {
-          t = shared ? rr : (a.row_tok ? a.row_tok[rr] : rr);
+          int t = shared ? rr : (a.row_tok ? a.row_tok[rr] : rr);
           t = t < 0 ? 0 : (t >= T ? T - 1 : t);  // memory safety for malformed row lists
           sc = a.dx[t];
+          ar = t;
         } else {
-          t = shared ? a.n_rows + rr : rr;  // the row's act row (= its output row)
-          sc = a.da[t] * (shared || !a.row_w ? 1.f : a.row_w[rr]);
+          ar = shared ? a.n_rows + rr : rr;
+          sc = a.da[ar] * (shared || !a.row_w ? 1.f : a.row_w[rr]);
         }
       }
-      rtok[tid] = t;
-      rscale[tid] = sc;
+      rsc[tid] = sc;
+      arow[tid] = ar;  // gate/up: the row's token
     }
     lds_barrier();
-    // this lane's A rows (one per 32-row tile; rows past the tile's end read
-    // row 0 and multiply zeros) and B columns
-    const int8_t *ap[kW8Mt];
-    bool mv[kW8Mt];
-#pragma unroll
-    for (int mt = 0; mt < kW8Mt; ++mt) {
-      const int r = 32 * kW8Mt * mg + 32 * mt + c;
-      mv[mt] = r < rows;
-      const int src = rtok[mv[mt] ? r : 0];
-      ap[mt] = (GATEUP ? a.qx + static_cast<size_t>(src) * H : a.qa + static_cast<size_t>(src) * a.F) + 16 * kg;
-    }
-    const int col = cg * kW8Cols + 32 * cw + c;
-    const int8_t *bp[NB];
+    // Weight tile rows: instruction k of wave w fills rows 32 w + 8 k + l / 8
+    // (gate/up: 0-127 the gate rows of the item's SwiGLU columns, 128-255
+    // their up rows), slot l % 8, with piece slot ^ (row & 7).
+    gchar_t *bq;
+    uint32_t bbase;
     if (GATEUP) {
-      const int8_t *gq = static_cast<const int8_t *>(shared ? a.sgq : a.gq);
-      const int8_t *uq = static_cast<const int8_t *>(shared ? a.suq : a.uq);
-      const size_t row = static_cast<size_t>(e) * (shared ? a.Fs : a.F) + col;
-      bp[0] = gq + row * H + 16 * kg;
-      bp[NB - 1] = uq + row * H + 16 * kg;
+      const int F = shared ? a.Fs : a.F;
+      bq = uniform_gptr(wave < 4 ? (shared ? a.sgq : a.gq) : (shared ? a.suq : a.uq));
+      bbase = static_cast<uint32_t>(e * F + cg * 128);
     } else {
-      const int8_t *dq = static_cast<const int8_t *>(shared ? a.sdq : a.dq);
-      bp[0] = dq + (static_cast<size_t>(e) * H + col) * a.F + 16 * kg;
+      bq = uniform_gptr(shared ? a.sdq : a.dq);
+      bbase = static_cast<uint32_t>(e * a.H + cg * 256);
     }
-    // this wave's row tiles that hold rows (wave-uniform; none: the wave
-    // only waits at the barriers)
-    const int mts = min(kW8Mt, max(0, (rows - 32 * kW8Mt * mg + 31) / 32));
-    i32x16_t acc[NB][kW8Mt];
+    uint32_t boff[4];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int k = 0; k < 4; ++k) {
+      const int R = 32 * wave + 8 * k + (lane >> 3);
+      boff[k] = (bbase + static_cast<uint32_t>(GATEUP ? (R & 127) : R)) * K + 16 * ((lane & 7) ^ (R & 7));
+    }
+    // A rows: instruction i of wave w fills rows 8 (w + 8 i) + l / 8, slot l % 8;
+    // rows past the tile's end read the first row (their products land in
+    // accumulator rows that are never stored)
+    gchar_t *aq = uniform_gptr(GATEUP ? static_cast<const void *>(a.qx) : static_cast<const void *>(a.qa));
+    uint32_t aoff[2];
 #pragma unroll
-      for (int mt = 0; mt < kW8Mt; ++mt)
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * (wave + 8 * i) + (lane >> 3);
+      const int src = arow[r < rows ? r : 0];
+      aoff[i] = static_cast<uint32_t>(src) * K + 16 * ((lane & 7) ^ (r & 7));
+    }
+    auto load_step = [&](int s, auto msc) __attribute__((always_inline)) {
+      constexpr int MS = decltype(msc)::value;
+      const int b = s % 3;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][mt][r] = 0;
-    // two steps in flight: operands of step s + 2 requested before step s is multiplied
-    i32x4_t A[3][kW8Mt], B[3][NB];
-    const i32x4_t z4 = {0, 0, 0, 0};
-    auto load = [&](int s, int slot) __attribute__((always_inline)) {
-      const int ks = min(s, steps - 1) * 32;  // past the end: re-request the last step
+      for (int i = 0; i < (MS + 1) / 2; ++i)
+        __builtin_amdgcn_global_load_lds(aq + (aoff[i] + static_cast<uint32_t>(kW8Step) * s),
+                                         (__attribute__((address_space(3))) void *)(abuf(b) + 8 * 8 * (wave + 8 * i)),
+                                         16, 0, 0);
 #pragma unroll
-      for (int mt = 0; mt < kW8Mt; ++mt) A[slot][mt] = mt < mts ? load_i8x16(ap[mt] + ks) : z4;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) B[slot][b] = load_i8x16(bp[b] + ks);
+      for (int k = 0; k < 4; ++k)
+        __builtin_amdgcn_global_load_lds(bq + (boff[k] + static_cast<uint32_t>(kW8Step) * s),
+                                         (__attribute__((address_space(3))) void *)(bbuf(b) + 8 * (32 * wave + 8 * k)),
+                                         16, 0, 0);
     };
-    auto step = [&](int slot) __attribute__((always_inline)) {
+
+    i32x16_t acc[4];
 #pragma unroll
-      for (int mt = 0; mt < kW8Mt; ++mt) {
-        if (mt >= mts) break;  // wave-uniform
-        const i32x4_t av = mv[mt] ? A[slot][mt] : z4;
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b][mt] = mfma_i8(av, B[slot][b], acc[b][mt]);
-      }
-    };
-    load(0, 0);
-    load(1, 1);
-    int s = 0;
-    for (; s + 3 <= steps; s += 3) {  // slots by step modulo 3, constant inside the body
-      load(s + 2, 2);
-      step(0);
-      load(s + 3, 0);
-      step(1);
-      load(s + 4, 1);
-      step(2);
-    }
-    for (; s < steps; ++s) {  // the remaining (at most two) steps are in slots 0 and 1
-      if (s % 3 == 0) step(0); else if (s % 3 == 1) step(1); else step(2);
-      if (s + 2 < steps) {
-        if ((s + 2) % 3 == 0) load(s + 2, 0); else if ((s + 2) % 3 == 1) load(s + 2, 1); else load(s + 2, 2);
-      }
-    }
+      for (int r = 0; r < 16; ++r) acc[mt][r] = 0;
+    with_msub((rows + 31) >> 5, [&](auto msc) __attribute__((always_inline)) {
+      constexpr int MS = decltype(msc)::value;
+      constexpr int G = (MS + 1) / 2 + 4;  // requests a step
+      // steps 0 and 1; the wait leaves step 1's requests pending (the waits
+      // count requests in issue order, so each group is pinned)
+      load_step(0, msc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(1, msc);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
+      lds_barrier();
+      auto step = [&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int b = s % 3;
+        pin_u32(aoff[0]);
+        pin_u32(aoff[1]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pin_u32(boff[k]);
+        // two steps ahead (clamped: past the end it re-reads the last
+        // step, the same bytes into the same buffer)
+        load_step(s + 2 < KS ? s + 2 : KS - 1, msc);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint4 *brow = bbuf(b) + 8 * Rm;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          // k 32 t4 .. 32 t4 + 31 of the step: piece 2 t4 + h of the rows
+          const int pc = 2 * t4 + h;
+          const uint4 bv = brow[pc ^ (Rm & 7)];
+          const i32x4_t B = {static_cast<int>(bv.x), static_cast<int>(bv.y), static_cast<int>(bv.z),
+                             static_cast<int>(bv.w)};
+          uint4 Av[MS];
+#pragma unroll
+          for (int mt = 0; mt < MS; ++mt) Av[mt] = abuf(b)[8 * (32 * mt + c) + (pc ^ (c & 7))];
+#pragma unroll
+          for (int mt = 0; mt < MS; ++mt) {
+            const i32x4_t A = {static_cast<int>(Av[mt].x), static_cast<int>(Av[mt].y), static_cast<int>(Av[mt].z),
+                               static_cast<int>(Av[mt].w)};
+            acc[mt] = mfma_i8(A, B, acc[mt]);
+          }
+        }
+        // step s + 1 has landed once at most step s + 2's requests are pending
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
+        lds_barrier();
+      };
+      unrolled_steps(std::make_integer_sequence<int, KS>{}, step);
+    });
+    // the clamped requests still in flight write into the buffers: let them
+    // land before the next item's requests reuse them
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     // epilogue: result (m, n) of a 32x32 tile sits in lane n + 32 ((m / 4) % 2),
     // register 4 (m / 8) + m % 4
     if (GATEUP) {
-      const float *gs = static_cast<const float *>(shared ? a.sgs : a.gs);
-      const float *us = static_cast<const float *>(shared ? a.sus : a.us);
-      const size_t srow = static_cast<size_t>(e) * (shared ? a.Fs : a.F) + col;
-      const float sg = gs[srow], su = us[srow];
+      // scaled products; then register j swapped with j + 8 between the
+      // 16-lane halves of each 32-lane row: lanes c < 16 hold gate and up of
+      // value j, lanes c >= 16 those of value j + 8
+      const int F = shared ? a.Fs : a.F;
+      const size_t srow = static_cast<size_t>(e) * F + cg * 128 + 16 * wave + (c & 15);
+      const float sl = static_cast<const float *>(c >= 16 ? (shared ? a.sus : a.us) : (shared ? a.sgs : a.gs))[srow];
+      const int rbase = (c >= 16 ? 16 : 0) + 4 * h;
+      const int col = cg * 128 + 16 * wave + (c & 15);
 #pragma unroll
-      for (int mt = 0; mt < kW8Mt; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = 32 * kW8Mt * mg + 32 * mt + 8 * (r >> 2) + 4 * kg + (r & 3);
-          if (m < rows) {
-            const float dxr = rscale[m];
-            const float gv = static_cast<float>(acc[0][mt][r]) * dxr * sg;
-            const float uv = static_cast<float>(acc[NB - 1][mt][r]) * dxr * su;
-            const int rr = m0 + m;
-            const size_t arow = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(un.r0) + rr;
-            a.act[arow * a.F + col] = gv / (1.f + expf(-gv)) * uv;
+        for (int jj = 0; jj < 8; ++jj) {
+          const int rlo = 32 * mt + 8 * (jj >> 2) + 4 * h + (jj & 3);  // row of register jj
+          const int rhi = rlo + 16;                                    // row of register jj + 8
+          const float vlo = static_cast<float>(acc[mt][jj]) * rsc[rlo] * sl;
+          const float vhi = static_cast<float>(acc[mt][jj + 8]) * rsc[rhi] * sl;
+          const auto gu = __builtin_amdgcn_permlane16_swap(__float_as_uint(vlo), __float_as_uint(vhi), false, false);
+          const float gv = __uint_as_float(gu[0]), uv = __uint_as_float(gu[1]);
+          const int r = 32 * mt + 8 * (jj >> 2) + (jj & 3) + rbase;
+          if (r < rows) {
+            const int rr = m0 + r;
+            const size_t ar = shared ? static_cast<size_t>(a.n_rows) + rr : static_cast<size_t>(un.r0) + rr;
+            a.act[ar * a.F + col] = gv / (1.f + expf(-gv)) * uv;
           }
         }
     } else {
-      const float sd = static_cast<const float *>(shared ? a.sds : a.ds)[static_cast<size_t>(e) * H + col];
+      const int col = cg * 256 + 32 * wave + c;
+      const float sd = static_cast<const float *>(shared ? a.sds : a.ds)[static_cast<size_t>(e) * a.H + col];
 #pragma unroll
-      for (int mt = 0; mt < kW8Mt; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = 32 * kW8Mt * mg + 32 * mt + 8 * (r >> 2) + 4 * kg + (r & 3);
-          if (m < rows) {
-            const float v = static_cast<float>(acc[0][mt][r]) * rscale[m] * sd;
-            a.rows_out[static_cast<size_t>(rtok[m]) * H + col] = v;
-          }
+        for (int r16 = 0; r16 < 16; ++r16) {
+          const int m = 32 * mt + 8 * (r16 >> 2) + 4 * h + (r16 & 3);
+          if (m < rows) a.rows_out[static_cast<size_t>(arow[m]) * a.H + col] =
+              static_cast<float>(acc[mt][r16]) * rsc[m] * sd;
         }
     }
   }
 }
 
-// Blocks of a W8A8 GEMM launch: one per compute unit (fewer for fewer items).
+bool w8a8_ok(const FfnArgs &a) {
+  const int units = (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1);
+  auto steps_ok = [](int k) { return k == 2 * kW8Step || k == 4 * kW8Step || k == 8 * kW8Step || k == 16 * kW8Step; };
+  return a.fmt == MOE_W_INT8_ROW && (a.Fs == 0 || a.Fs == a.F) && steps_ok(a.H) && steps_ok(a.F) && a.H % 256 == 0 &&
+         units <= kGmMaxUnits && a.qx && a.dx && a.qa && a.da;
+}
+
+// Blocks of a W8A8 GEMM launch: one per compute unit (its LDS holds one
+// block), fewer for fewer items.
 static int w8_grid(int items_upper) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -1493,11 +1549,22 @@ static int w8_grid(int items_upper) {
   return items_upper < 1 ? 1 : (items_upper < cus ? items_upper : cus);
 }
 
-bool w8a8_ok(const FfnArgs &a) {
+template <bool GATEUP>
+static hipError_t launch_w8a8_gemm(const FfnArgs &a, hipStream_t s, const LaunchEvents &ev) {
   const int units = (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1);
-  return a.fmt == MOE_W_INT8_ROW && (a.Fs == 0 || a.Fs == a.F) && a.F % kW8Cols == 0 && a.H % kW8Cols == 0 &&
-         a.H <= kQrThreads * kQrMaxPer && a.F <= kQrThreads * kQrMaxPer && units <= kPfMaxUnits && a.qx && a.dx &&
-         a.qa && a.da;
+  const int tiles = (a.n_rows + kW8Rows - 1) / kW8Rows + units + (a.Fs > 0 ? (a.T + kW8Rows - 1) / kW8Rows : 0);
+  const int K = GATEUP ? a.H : a.F;
+  const int grid = w8_grid(tiles * (GATEUP ? a.F / 128 : a.H / 256));
+  switch (K / kW8Step) {
+    case 16:
+      return launch_kernel(w8a8_gemm_kernel<GATEUP, 16>, dim3(grid), dim3(kGmThreads), 0, s, ev, a);
+    case 8:
+      return launch_kernel(w8a8_gemm_kernel<GATEUP, 8>, dim3(grid), dim3(kGmThreads), 0, s, ev, a);
+    case 4:
+      return launch_kernel(w8a8_gemm_kernel<GATEUP, 4>, dim3(grid), dim3(kGmThreads), 0, s, ev, a);
+    default:
+      return launch_kernel(w8a8_gemm_kernel<GATEUP, 2>, dim3(grid), dim3(kGmThreads), 0, s, ev, a);
+  }
 }
 
 hipError_t launch_w8a8(const FfnArgs &a, hipStream_t s, const LaunchEvents &ev_gu, const LaunchEvents &ev_dn) {
@@ -1506,17 +1573,14 @@ hipError_t launch_w8a8(const FfnArgs &a, hipStream_t s, const LaunchEvents &ev_g
   quant_rows_kernel<uint16_t><<<a.T, kQrThreads, 0, s>>>(a.x, a.H, a.qx, a.dx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int units = (a.Fs > 0 ? 1 : 0) + (a.offsets ? a.max_units : 1);
-  const int tiles = (a.n_rows + kW8Rows - 1) / kW8Rows + units + (a.Fs > 0 ? (a.T + kW8Rows - 1) / kW8Rows : 0);
-  e = launch_kernel(w8a8_gemm_kernel<true>, dim3(w8_grid(tiles * (a.F / kW8Cols))), dim3(kW8Threads), 0, s, ev_gu, a);
+  e = launch_w8a8_gemm<true>(a, s, ev_gu);
   if (e != hipSuccess) return e;
   // every SwiGLU row (routed, then the shared expert's), quantised per row
   const int rows_all = a.n_rows + (a.Fs > 0 ? a.T : 0);
   quant_rows_kernel<float><<<rows_all, kQrThreads, 0, s>>>(a.act, a.F, a.qa, a.da);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_kernel(w8a8_gemm_kernel<false>, dim3(w8_grid(tiles * (a.H / kW8Cols))), dim3(kW8Threads), 0, s, ev_dn,
-                       a);
+  return launch_w8a8_gemm<false>(a, s, ev_dn);
 }
 
 // ----------------------------------------------------------------- launches
