@@ -120,8 +120,9 @@ size_t moe_workspace_bytes(const moe_layer *L, int32_t max_tokens);
  * the kernels keep zero between calls).  Enqueued on `stream`. */
 int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
-/* Bytes of workspace moe_route needs for T tokens when it is not given a
- * logits buffer (host, pure; 0 on invalid arguments). */
+/* Bytes of workspace moe_route needs for T tokens (host, pure; 0 on invalid
+ * arguments): the logits when the caller passes none, plus, for batches of
+ * more than 16 tokens, the router GEMM's partial sums. */
 size_t moe_route_workspace_bytes(const moe_layer *L, int32_t T);
 
 /* Router: logits[t][e] = sum_h Wr[e][h] * x[t][h] (+ bias[e]) in float32;
@@ -131,10 +132,12 @@ size_t moe_route_workspace_bytes(const moe_layer *L, int32_t T);
  * topk_w[t][k] = routing weights per L->renorm.
  * x_bf16 [T][H] bfloat16 bits (16-byte aligned); topk_ids int32 [T][K];
  * topk_w float [T][K]; logits float [T][E], or NULL when the caller does not
- * want them: they then pass through `ws`, which must hold
- * moe_route_workspace_bytes(L, T) bytes (ws is unused when logits is given
- * and may be NULL).  MOE_ERR_WORKSPACE if logits is NULL and ws is missing
- * or too small.  shared_gate float [T] or NULL: with L->shared_gate_w it
+ * want them.  ws (256-byte aligned, moe_route_workspace_bytes(L, T) bytes)
+ * holds the logits when logits is NULL and, for batches of more than 16
+ * tokens (whose logits are a matrix-core GEMM over slices of H, the slices
+ * added in order by the top-k kernel), the partial sums; for a batch of at
+ * most 16 tokens with logits given it is unused and may be NULL.
+ * MOE_ERR_WORKSPACE if ws is needed and missing, misaligned or too small.  shared_gate float [T] or NULL: with L->shared_gate_w it
  * receives sigmoid(shared_gate_w . x[t]) per token. */
 int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *topk_ids, float *topk_w,
               float *logits, float *shared_gate, void *ws, size_t ws_bytes, void *stream);

@@ -198,9 +198,14 @@ def route_workspace_bytes(layer: Layer, T: int) -> int:
 def route(layer: Layer, x_bf16: torch.Tensor, topk_ids, topk_w, logits=None, ws=None, stream=None,
           shared_gate=None):
     """Router + top-k (+ the shared gate's sigmoid into shared_gate [T]).
-    logits None: they pass through ws (see moe_route)."""
+    ws None: a workspace of route_workspace_bytes is allocated here when the
+    call needs one (see moe_route)."""
     c = layer.c()
     T = x_bf16.shape[0]
+    if ws is None:
+        need = int(_lib.moe_route_workspace_bytes(ctypes.byref(c), T))
+        if need and (logits is None or T > 16):
+            ws = torch.empty(need, dtype=torch.uint8, device=x_bf16.device)
     _check("moe_route", _lib.moe_route(ctypes.byref(c), _ptr(x_bf16), T, _ptr(topk_ids), _ptr(topk_w),
                                        _ptr(logits), _ptr(shared_gate), _ptr(ws), 0 if ws is None else ws.numel(),
                                        _stream(stream)))

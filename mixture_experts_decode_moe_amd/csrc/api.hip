@@ -113,6 +113,7 @@ struct LayerWs {
   float *gate;    // [T]: the shared expert's gate values
   int8_t *qx, *qa;  // W8A8: quantised x [T][H] and SwiGLU rows [rows][F]
   float *dx, *da;   // their per-row scales
+  float *rpart;     // the router GEMM's partial sums
   size_t bytes;
 };
 
@@ -150,6 +151,9 @@ LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
   w.dx = c.take<float>(T);
   w.qa = c.take<int8_t>((TK + (Fs ? T : 0)) * L->routed.ffn);
   w.da = c.take<float>(TK + (Fs ? T : 0));
+  // the router GEMM's partial sums of a prompt batch (either path may be
+  // forced at run time, so sized for the GEMM whenever T allows it)
+  w.rpart = c.take<float>(router_partial_floats(T, L->hidden, static_cast<int>(E), kPathPrefill));
   w.bytes = align_up(c.off, 256);
   return w;
 }
@@ -215,7 +219,10 @@ int moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
 
 size_t moe_route_workspace_bytes(const moe_layer *L, int32_t T) {
   if (check_layer(L) != MOE_OK || T < 0) return 0;
-  return align_up(static_cast<size_t>(T) * L->n_experts * sizeof(float), 256);
+  // the logits (when the caller passes none), then the router GEMM's
+  // partial sums (batches above kFusedTokens tokens)
+  return align_up(static_cast<size_t>(T) * L->n_experts * sizeof(float), 256) +
+         align_up(router_partial_floats(T, L->hidden, L->n_experts, kPathAuto) * sizeof(float), 256);
 }
 
 int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *topk_ids, float *topk_w, float *logits,
@@ -225,14 +232,19 @@ int moe_route(const moe_layer *L, const uint16_t *x_bf16, int32_t T, int32_t *to
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x_bf16 || !topk_ids || !topk_w || !aligned(x_bf16, 16)) return MOE_ERR_INVALID_ARG;
-  if (!logits) {
-    // the logits pass between the two kernels through the caller's workspace
-    if (!ws || !aligned(ws, 16) || ws_bytes < moe_route_workspace_bytes(L, T)) return MOE_ERR_WORKSPACE;
-    logits = static_cast<float *>(ws);
+  // the workspace: the logits when the caller passes none, then the router
+  // GEMM's partial sums when the batch takes the GEMM
+  const size_t logit_bytes = align_up(static_cast<size_t>(T) * L->n_experts * sizeof(float), 256);
+  const size_t part_floats = router_partial_floats(T, L->hidden, L->n_experts, kPathAuto);
+  if (!logits || part_floats) {
+    if (!ws || !aligned(ws, 256) || ws_bytes < moe_route_workspace_bytes(L, T)) return MOE_ERR_WORKSPACE;
+    if (!logits) logits = static_cast<float *>(ws);
   }
+  float *part = part_floats ? reinterpret_cast<float *>(static_cast<char *>(ws) + logit_bytes) : nullptr;
   const bool gate = L->shared_gate_w && shared_gate;
   RouteArgs a{L->router_w, L->router_bias, x_bf16, T, L->hidden, L->n_experts, L->top_k, L->renorm, logits,
-              topk_ids, topk_w, nullptr, kPathAuto, gate ? L->shared_gate_w : nullptr, gate ? shared_gate : nullptr};
+              topk_ids, topk_w, nullptr, kPathAuto, gate ? L->shared_gate_w : nullptr, gate ? shared_gate : nullptr,
+              part};
   hipError_t e = launch_router_logits(a, as_stream(stream));
   if (e == hipSuccess) e = launch_topk(a, as_stream(stream));
   return hip_status(e);
@@ -460,8 +472,11 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
     e = xa.route_here ? launch_route_partial(fa, s) : launch_route_fused(fa, s);
   } else {
     // (prompt batches: tail-skip leaves them untouched)
-    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, w.logits, ids, tw, w.x16, path,
-                 L->shared_gate_w, w.gate};
+    // (the router GEMM's slices are added by the top-k kernel, which then
+    // has no logits to write for the layer)
+    float *lg = router_partial_floats(T, H, E, path) ? nullptr : w.logits;
+    RouteArgs ra{L->router_w, L->router_bias, x_bf16, T, H, E, K, L->renorm, lg, ids, tw, w.x16, path,
+                 L->shared_gate_w, w.gate, w.rpart};
     if (router_writes_x16(ra)) {
       xa.x16 = w.x16;
       xa.queue = w.control;

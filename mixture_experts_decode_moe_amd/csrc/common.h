@@ -109,8 +109,12 @@ struct RouteArgs {
   int32_t path;   // PathSel: kPathPrefill takes the matrix-core router GEMM at any T
   const float *gate_w;  // [H] or NULL: the shared expert's gate row
   float *gate;          // [T] (with gate_w): sigmoid of the gate row's product with x
+  float *part;          // the router GEMM's partial sums: router_partial_floats(T, H, E, path) floats
 };
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s);
+// floats of partial sums the router GEMM needs for this call (0: the call
+// takes the partial-logit router kernel and needs none)
+size_t router_partial_floats(int T, int H, int E, int path);
 // whether launch_router_logits writes x16 (when given) for this call
 bool router_writes_x16(const RouteArgs &a);
 hipError_t launch_topk(const RouteArgs &a, hipStream_t s);

@@ -29,8 +29,6 @@
 // enumerated once per block into an LDS table.
 #include <math.h>
 
-#include <utility>
-
 #include "mfma_common.h"
 
 namespace moe {
@@ -452,16 +450,6 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 
 typedef __attribute__((address_space(1))) const u32x2_t gu2_t;
 
-// An empty volatile statement on a 32-bit offset in registers: the
-// addresses derived from it are then computed where they are used rather
-// than hoisted out of the k loop and kept live (which spills, and a spill
-// reload waits for every load).
-MOE_DEV void pin_u32(uint32_t &v) { __asm__ volatile("" : "+v"(v)); }
-
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
 
 template <class Fn>
 MOE_DEV void with_msub(int msub, Fn &&fn) {
@@ -489,10 +477,6 @@ MOE_DEV void with_msub2(int msub, Fn &&fn) {
     fn(IntC<2>{});
 }
 
-// s_waitcnt immediate that waits until at most n (< 64) vector memory
-// requests are outstanding and leaves the other counters alone (GFX9
-// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // 32x32 output tiles (v_mfma_f32_32x32x16_f16, twice the rate of the 16x16
 // shape on this chip): lane l holds row l % 32 of A and column l % 32 of B
@@ -1318,13 +1302,6 @@ __global__ void __launch_bounds__(kQrThreads) quant_rows_kernel(const In *__rest
 constexpr int kW8Rows = 128;  // rows per item
 constexpr int kW8Step = 128;  // k (bytes of an int8 row) per step
 static int pf_grid(int items_upper);
-
-// step(IntC<0>), ..., step(IntC<KS - 1>) as straight-line code (the k loops
-// are unrolled whole: see gateup_gemm128_kernel)
-template <class Fn, int... S>
-MOE_DEV void unrolled_steps(std::integer_sequence<int, S...>, Fn &&step) {
-  (step(IntC<S>{}), ...);
-}
 
 // The W8A8 GEMM.  GATEUP: a[row][f] = silu(g) u with g = I_g dx[t] sg[f]
 // (and u alike), the rows' tokens' quantised inputs against the gate and

@@ -4,6 +4,8 @@
 // expert_mfma.hip.
 #pragma once
 
+#include <utility>
+
 #include "expert_common.h"
 
 namespace moe {
@@ -199,6 +201,30 @@ MOE_DEV uint4 load16_g(gchar_t *p) {
   const u32x4_t v = *reinterpret_cast<gu32x4_t *>(p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// An empty volatile statement on a 32-bit offset in registers: the
+// addresses derived from it are then computed where they are used rather
+// than hoisted out of the k loop and kept live (which spills, and a spill
+// reload waits for every load).
+MOE_DEV void pin_u32(uint32_t &v) { __asm__ volatile("" : "+v"(v)); }
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// step(IntC<0>), ..., step(IntC<KS - 1>) as straight-line code (k loops
+// with direct loads into LDS are unrolled whole: with a loop back-edge the
+// compiler waits for every outstanding load there)
+template <class Fn, int... S>
+MOE_DEV void unrolled_steps(std::integer_sequence<int, S...>, Fn &&step) {
+  (step(IntC<S>{}), ...);
+}
+
+// s_waitcnt immediate that waits until at most n (< 64) vector memory
+// requests are outstanding and leaves the other counters alone (GFX9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 MOE_DEV uint4 load_stream16_g(gchar_t *p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t *>(p));

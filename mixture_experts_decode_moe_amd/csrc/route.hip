@@ -142,14 +142,19 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float *__restr
 // 8 significant bits, mid: the remainder cut likewise, lo: the last 8 bits),
 // so three v_mfma_f32_32x32x16_bf16 per 16-wide k-step form every product
 // exactly and accumulate it in fp32, as an fp32 dot product does (in another
-// order).  A block owns 32 tokens x 64 experts with 8 waves: wave w takes
-// expert tile w & 1 over the quarter w >> 1 of the reduction dimension, its
-// operands straight from global memory (lane l: token / expert l % 32, the
-// 8 consecutive k of group l / 32), and the four quarters' sums are added in
-// LDS in quarter order.  moe_route and the layer use this kernel alike for
-// such batches.
-constexpr int kRmTok = 32, kRmExp = 64, kRmK = 64;
-constexpr int kRmThreads = 512;
+// order).  The reduction is split into kRgSlices slices: a block owns 64
+// tokens x 64 experts over one slice and writes its partial sums; the
+// top-k kernel adds the slices in order (then the bias), so a weight row is
+// read by T / 64 blocks and the x rows by E / 64.  Both operands go from
+// global memory straight into LDS by direct loads, one 64-wide k-step ahead
+// in two buffers; the block then splits the step's weights once into three
+// bf16 planes in LDS (no wave splits a weight another wave splits too).
+// Each of the 4 waves owns one 32x32 tile (tokens 32 (w & 1), experts
+// 32 (w >> 1)); the 72 KB of LDS let two blocks share a compute unit, so one
+// block's loads overlap the other's matrix work.  moe_route and the layer
+// use this kernel alike for such batches.
+constexpr int kRgTok = 64, kRgExp = 64, kRgStep = 64, kRgSlices = 4;
+constexpr int kRgThreads = 256;
 
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rf32x16_t __attribute__((ext_vector_type(16)));
@@ -182,94 +187,144 @@ MOE_DEV rf32x16_t mfma32_bf16(const u32x4_t &a, const u32x4_t &b, const rf32x16_
                                                  c, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__restrict__ wr,
-                                                                 const float *__restrict__ bias,
+// part[slice][t][e] = sum of x[t][k] w[e][k] over the slice's k (no bias);
+// the blocks of expert block 0 also write x in fp16, pair-permuted (the
+// prefill expert GEMMs' operand form).  SPS = steps of kRgStep per slice.
+template <int SPS>
+__global__ void __launch_bounds__(kRgThreads) router_gemm_kernel(const float *__restrict__ wr,
                                                                  const uint16_t *__restrict__ x, int32_t T,
-                                                                 int32_t H, int32_t E, float *__restrict__ logits,
+                                                                 int32_t H, int32_t E, float *__restrict__ part,
                                                                  uint16_t *__restrict__ x16) {
-  __shared__ rf32x16_t part[8][64];  // each wave's sums: [wave][lane]
+  // raw step operands, two buffers: x rows [64][8 pieces of 8 bf16] and
+  // weight rows [64][16 pieces of 4 fp32]; the split weights [3][64][8]
+  __shared__ uint4 rg_x0[kRgTok * 8], rg_x1[kRgTok * 8];
+  __shared__ uint4 rg_w0[kRgExp * 16], rg_w1[kRgExp * 16];
+  __shared__ uint4 rg_p[3][kRgExp * 8];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int c = lane & 31, g = lane >> 5;
-  const int et = wave & 1, kq = wave >> 1;  // expert tile, quarter of the reduction
-  const int t0 = blockIdx.y * kRmTok;
-  const int e0 = blockIdx.x * kRmExp + 32 * et;
-  const int t = t0 + c, e = e0 + c;
-  const bool tv = t < T, ev = e < E;
-  const int Hq = H >> 2;  // a multiple of 16
-  const int k0 = kq * Hq + 8 * g;
-  // rows past T or E read row 0: their sums land in outputs never stored
-  const uint4 *xp = reinterpret_cast<const uint4 *>(x + static_cast<size_t>(tv ? t : 0) * H + k0);
-  const float4 *wp = reinterpret_cast<const float4 *>(wr + static_cast<size_t>(ev ? e : 0) * H + k0);
-  // the first expert tile's waves also write x in fp16, pair-permuted (the
-  // prefill expert GEMMs' operand form): quarter kq of the token rows by the
-  // blocks of expert-tile column kq % gridDim.x, so that the writes are
-  // spread over the columns
-  uint16_t *x16p = (x16 && et == 0 && tv && static_cast<int>(blockIdx.x) == kq % static_cast<int>(gridDim.x))
-                       ? x16 + static_cast<size_t>(t) * H + k0
-                       : nullptr;
+  const int tt = wave & 1, eq = wave >> 1;  // this wave's token tile and expert tile
+  const int t0 = blockIdx.x * kRgTok, e0 = blockIdx.y * kRgExp;
+  const int slice = blockIdx.z;
+  const int k0 = slice * SPS * kRgStep;
+  auto xbuf = [&](int b) __attribute__((always_inline)) { return b == 0 ? rg_x0 : rg_x1; };
+  auto wbuf = [&](int b) __attribute__((always_inline)) { return b == 0 ? rg_w0 : rg_w1; };
+  // direct loads: instruction i of wave w fills x rows 8 (4 i + w) + l / 8,
+  // slot l % 8 holding piece slot ^ (row & 7), and weight rows
+  // 4 (4 w + i) + l / 16, slot l % 16 holding piece slot ^ (row & 15).  Rows
+  // past T or E read row 0: their sums land in outputs never stored.
+  gchar_t *xg = uniform_gptr(x);
+  gchar_t *wg = uniform_gptr(wr);
+  uint32_t xoff[2], woff[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (4 * i + wave) + (lane >> 3);
+    xoff[i] = (static_cast<uint32_t>(t0 + r < T ? t0 + r : 0) * H + k0) * 2 + 16 * ((lane & 7) ^ (r & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * (4 * wave + i) + (lane >> 4);
+    woff[i] = (static_cast<uint32_t>(e0 + r < E ? e0 + r : 0) * H + k0) * 4 + 16 * ((lane & 15) ^ (r & 15));
+  }
+  auto load_step = [&](int s) __attribute__((always_inline)) {
+    const int b = s & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(xg + (xoff[i] + static_cast<uint32_t>(2 * kRgStep) * s),
+                                       (__attribute__((address_space(3))) void *)(xbuf(b) + 64 * (4 * i + wave)), 16,
+                                       0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(wg + (woff[i] + static_cast<uint32_t>(4 * kRgStep) * s),
+                                       (__attribute__((address_space(3))) void *)(wbuf(b) + 64 * (4 * wave + i)), 16,
+                                       0, 0);
+  };
+  // the block's split of a step's weights: thread (row tid / 4, quarter
+  // tid % 4) splits k 16 q .. 16 q + 15 of its row into the planes' pieces
+  // 2 q and 2 q + 1 (slot piece ^ (row & 7))
+  auto split_step = [&](int b) __attribute__((always_inline)) {
+    const int r = tid >> 2, q = tid & 3;
+    const uint4 *src = wbuf(b) + 16 * r;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int pc = 4 * q + 2 * hh;  // fp32 pieces pc, pc + 1: k 8 (2 q + hh) .. + 7
+      const uint4 a0 = src[pc ^ (r & 15)], a1 = src[(pc + 1) ^ (r & 15)];
+      u32x4_t ph, pm, pl;
+      split3(make_float4(__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w)),
+             make_float4(__uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)),
+             ph, pm, pl);
+      const int slot = (2 * q + hh) ^ (r & 7);
+      rg_p[0][8 * r + slot] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+      rg_p[1][8 * r + slot] = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+      rg_p[2][8 * r + slot] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+    }
+  };
+  // the fp16 copy of x: thread (row 8 (4 i + w) + l / 8, slot l % 8) writes
+  // the piece it loaded (blocks of expert block 0 only)
+  const bool write16 = x16 && blockIdx.y == 0;
   rf32x16_t acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  const int steps = Hq / 16;
-  // two 16-wide steps per round, the next three rounds' operands in flight
-  uint4 xa[4][2];
-  float4 wa[4][2][2];
-  auto load = [&](int r, int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int s = min(2 * r + u, steps - 1);  // clamped: past the end it re-reads the last step
-      xa[slot][u] = xp[2 * s];
-      wa[slot][u][0] = wp[4 * s];
-      wa[slot][u][1] = wp[4 * s + 1];
-    }
-  };
-  auto compute = [&](int r, int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint4 xv = xa[slot][u];
-      const u32x4_t A = {xv.x, xv.y, xv.z, xv.w};
-      if (x16p) {
-        const u32x4_t pp = pair_permute(xv);
-        *reinterpret_cast<uint4 *>(x16p + 16 * (2 * r + u)) =
-            make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y), bf16x2_to_f16x2(pp.z), bf16x2_to_f16x2(pp.w));
-      }
-      u32x4_t bh, bm, bl;
-      split3(wa[slot][u][0], wa[slot][u][1], bh, bm, bl);
-      acc = mfma32_bf16(A, bh, acc);
-      acc = mfma32_bf16(A, bm, acc);
-      acc = mfma32_bf16(A, bl, acc);
-    }
-  };
-  // steps is a multiple of 8 (H % 512 == 0): whole groups of four rounds,
-  // no matrix-core instruction under a branch
-  const int rounds = steps >> 1;
-  load(0, 0);
-  load(1, 1);
-  load(2, 2);
-  for (int r = 0; r < rounds; r += 4) {
-    load(r + 3, 3);
-    compute(r, 0);
-    load(r + 4, 0);
-    compute(r + 1, 1);
-    load(r + 5, 1);
-    compute(r + 2, 2);
-    load(r + 6, 2);
-    compute(r + 3, 3);
-  }
-  part[wave][lane] = acc;
+  const int ar = 32 * tt + c, er = 32 * eq + c;  // this lane's x row and weight row
+  load_step(0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (SPS > 1) load_step(1);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(SPS > 1 ? 6 : 0));
   lds_barrier();
-  // waves 0 and 1 add the four quarters of their expert tile in order
-  if (kq == 0 && ev) {
-    rf32x16_t v = part[et][lane];
+  split_step(0);
+  lds_barrier();
+  auto step = [&](auto sc) __attribute__((always_inline)) {
+    constexpr int s = decltype(sc)::value;
+    constexpr int b = s & 1;
+    if (write16) {
+      // this thread's landed x pieces, in fp16 operand order
 #pragma unroll
-    for (int q = 1; q < 4; ++q) v += part[2 * q + et][lane];
-    const float b = bias ? bias[e] : 0.f;
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * (4 * i + wave) + (lane >> 3);
+        if (t0 + r < T) {
+          const int pcs = (lane & 7) ^ (r & 7);
+          const uint4 v = xbuf(b)[64 * (4 * i + wave) + lane];
+          const u32x4_t pp = pair_permute(v);
+          *reinterpret_cast<uint4 *>(x16 + static_cast<size_t>(t0 + r) * H + k0 + kRgStep * s + 8 * pcs) =
+              make_uint4(bf16x2_to_f16x2(pp.x), bf16x2_to_f16x2(pp.y), bf16x2_to_f16x2(pp.z),
+                         bf16x2_to_f16x2(pp.w));
+        }
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kRgStep / 16; ++kk) {
+      const int pc = 2 * kk + g;  // the lane's 8 k of the 16-wide step
+      const uint4 av = xbuf(b)[8 * ar + (pc ^ (ar & 7))];
+      const u32x4_t A = {av.x, av.y, av.z, av.w};
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        const uint4 bv = rg_p[pl][8 * er + (pc ^ (er & 7))];
+        const u32x4_t B = {bv.x, bv.y, bv.z, bv.w};
+        acc = mfma32_bf16(A, B, acc);
+      }
+    }
+    if constexpr (s + 1 < SPS) {
+      lds_barrier();  // every wave is done with the planes and with buffer b
+      if constexpr (s + 2 < SPS) load_step(s + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      // step s + 1 has landed once at most step s + 2's six requests are pending
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(s + 2 < SPS ? 6 : 0));
+      lds_barrier();
+      split_step(b ^ 1);
+      lds_barrier();
+    }
+  };
+  unrolled_steps(std::make_integer_sequence<int, SPS>{}, step);
+  // result (m, n) of the 32x32 tile sits in lane n + 32 ((m / 4) % 2),
+  // register 4 (m / 8) + m % 4
+  const int e = e0 + er;
+  if (e < E) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int tt = t0 + (j & 3) + 8 * (j >> 2) + 4 * g;
-      if (tt < T) logits[static_cast<size_t>(tt) * E + e] = v[j] + b;
+      const int t = t0 + 32 * tt + 8 * (j >> 2) + 4 * g + (j & 3);
+      if (t < T) part[(static_cast<size_t>(slice) * T + t) * E + e] = acc[j];
     }
   }
 }
@@ -279,12 +334,17 @@ __global__ void __launch_bounds__(kRmThreads) router_mfma_kernel(const float *__
 // also forms its token's shared gate logit, lane l summing elements
 // l, l + 64, ... and the wave adding the lanes in a fixed order, and writes
 // its sigmoid to gate[t].
+//
+// The logits come either whole (S = 1, bias already added) or as S partial
+// sums [S][T][E] from the router GEMM, added here in slice order and then
+// the bias; logits_out (or NULL) then receives them.
 template <int NPL>
-__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int32_t T, int32_t E,
-                                                   int32_t K, int32_t renorm, int32_t *__restrict__ ids,
-                                                   float *__restrict__ wout, const uint16_t *__restrict__ x,
-                                                   int32_t H, const float *__restrict__ gate_w,
-                                                   float *__restrict__ gate) {
+__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int32_t S,
+                                                   const float *__restrict__ bias, float *__restrict__ logits_out,
+                                                   int32_t T, int32_t E, int32_t K, int32_t renorm,
+                                                   int32_t *__restrict__ ids, float *__restrict__ wout,
+                                                   const uint16_t *__restrict__ x, int32_t H,
+                                                   const float *__restrict__ gate_w, float *__restrict__ gate) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
@@ -296,15 +356,26 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ log
     const float z = sum64(acc);
     if (lane == 0) gate[t] = 1.f / (1.f + expf(-z));
   }
-  const float *l = logits + static_cast<size_t>(t) * E;
   float v[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int e = lane + 64 * j;
     float val = -INFINITY;
     if (e < E) {
-      val = l[e];
-      if (val != val) val = -INFINITY;  // NaN never outranks a number
+      // every slice requested at once, then added in order
+      float pv[kRgSlices];
+#pragma unroll
+      for (int sl = 0; sl < kRgSlices; ++sl)
+        pv[sl] = sl < S ? logits[(static_cast<size_t>(sl) * T + t) * E + e] : 0.f;
+      float sum = pv[0];
+#pragma unroll
+      for (int sl = 1; sl < kRgSlices; ++sl)
+        if (sl < S) sum += pv[sl];
+      if (S > 1) {
+        if (bias) sum += bias[e];
+        if (logits_out) logits_out[static_cast<size_t>(t) * E + e] = sum;
+      }
+      val = sum == sum ? sum : -INFINITY;  // NaN never outranks a number
     }
     v[j] = val;
   }
@@ -378,17 +449,38 @@ hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-static bool router_mfma_ok(const RouteArgs &a) {
-  const bool many = a.path == kPathPrefill || (a.path == kPathAuto && a.T > kFusedTokens);
-  return many && a.H % (8 * kRmK) == 0;
+// Steps of the router GEMM per slice (H = kRgSlices * steps * kRgStep),
+// or 0 where the call takes the partial-logit router kernel.
+static int router_gemm_steps(int T, int H, int path) {
+  const bool many = path == kPathPrefill || (path == kPathAuto && T > kFusedTokens);
+  if (!many || H % (kRgSlices * kRgStep)) return 0;
+  const int sps = H / (kRgSlices * kRgStep);
+  return (sps == 2 || sps == 4 || sps == 8 || sps == 16) ? sps : 0;
+}
+
+static bool router_mfma_ok(const RouteArgs &a) { return router_gemm_steps(a.T, a.H, a.path) > 0; }
+
+size_t router_partial_floats(int T, int H, int E, int path) {
+  return router_gemm_steps(T, H, path) > 0 ? static_cast<size_t>(kRgSlices) * T * E : 0;
 }
 
 bool router_writes_x16(const RouteArgs &a) { return a.x16 != nullptr && router_mfma_ok(a); }
 
 hipError_t launch_router_logits(const RouteArgs &a, hipStream_t s) {
-  if (router_mfma_ok(a)) {
-    dim3 g((a.E + kRmExp - 1) / kRmExp, (a.T + kRmTok - 1) / kRmTok);
-    router_mfma_kernel<<<g, kRmThreads, 0, s>>>(a.router_w, a.router_bias, a.x, a.T, a.H, a.E, a.logits, a.x16);
+  const int sps = router_gemm_steps(a.T, a.H, a.path);
+  if (sps > 0) {
+    if (!a.part) return hipErrorInvalidValue;
+    dim3 g((a.T + kRgTok - 1) / kRgTok, (a.E + kRgExp - 1) / kRgExp, kRgSlices);
+#define MOE_RG(N) router_gemm_kernel<N><<<g, kRgThreads, 0, s>>>(a.router_w, a.x, a.T, a.H, a.E, a.part, a.x16)
+    if (sps == 2)
+      MOE_RG(2);
+    else if (sps == 4)
+      MOE_RG(4);
+    else if (sps == 8)
+      MOE_RG(8);
+    else
+      MOE_RG(16);
+#undef MOE_RG
     return hipGetLastError();
   }
   const int rows = a.E + (a.gate_w ? 1 : 0);  // the gate row rides with the router rows
@@ -403,9 +495,13 @@ hipError_t launch_topk(const RouteArgs &a, hipStream_t s) {
   dim3 grid((a.T + 3) / 4);
   const int npl = (a.E + 63) / 64;
   // the shared gate is formed here only when the router GEMM left it out
-  const float *gw = router_mfma_ok(a) ? a.gate_w : nullptr;
-#define MOE_TOPK(N) \
-  topk_kernel<N><<<grid, 256, 0, s>>>(a.logits, a.T, a.E, a.K, a.renorm, a.ids, a.w, a.x, a.H, gw, a.gate)
+  const bool gemm = router_mfma_ok(a);
+  const float *gw = gemm ? a.gate_w : nullptr;
+  const float *in = gemm ? a.part : a.logits;
+  const int S = gemm ? kRgSlices : 1;
+#define MOE_TOPK(N)                                                                                                  \
+  topk_kernel<N><<<grid, 256, 0, s>>>(in, S, a.router_bias, a.logits, a.T, a.E, a.K, a.renorm, a.ids, a.w, a.x, a.H, \
+                                      gw, a.gate)
   if (npl <= 1)
     MOE_TOPK(1);
   else if (npl <= 2)

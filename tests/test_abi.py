@@ -104,6 +104,10 @@ def test_other_entry_points_reject_bad_arguments(mb):
     assert lib.moe_route(ctypes.byref(L), p, 4, p, p, None, None, p, 16, None) == -3
     assert lib.moe_route_workspace_bytes(ctypes.byref(L), 4) >= 4 * 256 * 4
     assert lib.moe_route_workspace_bytes(ctypes.byref(L), -1) == 0
+    # batches above 16 tokens: the router GEMM's partial sums also pass
+    # through the workspace, so it is needed even with logits given
+    assert lib.moe_route_workspace_bytes(ctypes.byref(L), 64) >= 64 * 256 * 4 * 5
+    assert lib.moe_route(ctypes.byref(L), p, 64, p, p, p, None, None, 0, None) == -3
     assert lib.moe_permute(p, p, 4, 9, 8, p, p, p, p, p, p, p, p, 1 << 20, None) == -1  # K > E
     assert lib.moe_permute(p, p, 4, 2, 4096, p, p, p, p, p, p, p, p, 1 << 20, None) == -2
     assert lib.moe_permute(p, p, 4, 2, 8, p, p, p, p, p, p, p, None, 0, None) == -3
