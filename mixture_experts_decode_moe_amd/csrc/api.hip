@@ -100,7 +100,7 @@ int32_t effective_path(const moe_forward_opts *opts) {
 }
 
 struct LayerWs {
-  uint32_t *control;  // kControlBytes of words kept zero between calls; [0..1]: prefill gate/up item queue
+  uint32_t *control;  // kControlBytes of words kept zero between calls; [0..8]: prefill gate/up item queues
   float *part;        // fused routing: partial logits [S][T][E]
   float *logits;
   int32_t *ids;
@@ -434,6 +434,9 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
     if (!w8a8_ok(xa)) return MOE_ERR_UNSUPPORTED;
   }
   const bool decode_batch = T <= kFusedTokens && path != MOE_PATH_PREFILL && !w8a8;
+  // prompt batches on the prefill GEMM pair or the W8A8 GEMMs keep the
+  // expert rows in fp16 between the down projection and the combine
+  xa.rows_f16 = !decode_batch && !mfma_decode_ok(xa) && (w8a8 || down_rows_f16_ok(xa)) ? 1 : 0;
   if (decode_batch) {
     // decode batch: the router's partial logits; the top-k and the
     // permutation then run inside the gate/up kernel when it is the
@@ -533,9 +536,15 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
 
-  CombineArgs ca = combine_args(w.rows_out, w.inv_pos, T, K, H,
-                                has_shared ? w.rows_out + static_cast<size_t>(TK) * H : nullptr,
-                                L->shared_gate_w ? w.gate : nullptr, y, res);
+  // fp16 expert rows (prefill GEMM pair, W8A8): the shared expert's rows
+  // follow the routed ones in the same element size
+  const float *shared_rows =
+      !has_shared ? nullptr
+      : xa.rows_f16 ? reinterpret_cast<const float *>(reinterpret_cast<const uint16_t *>(w.rows_out) +
+                                                      static_cast<size_t>(TK) * H)
+                    : w.rows_out + static_cast<size_t>(TK) * H;
+  CombineArgs ca = combine_args(w.rows_out, w.inv_pos, T, K, H, shared_rows, L->shared_gate_w ? w.gate : nullptr, y, res);
+  ca.rows_f16 = xa.rows_f16;
   StageMark m(ev, MOE_STAGE_COMBINE, s);
   return hip_status(launch_combine(ca, s));
 }

@@ -23,9 +23,25 @@ MOE_DEV void add4(float4 &a, const float4 &b) {
   a.w += b.w;
 }
 
+// Four consecutive elements of an expert row: fp32, or fp16 (F16).
+template <bool F16>
+MOE_DEV float4 row4(const float *rows, size_t row, int H, int c) {
+  if constexpr (F16) {
+    const uint2 v = reinterpret_cast<const uint2 *>(reinterpret_cast<const _Float16 *>(rows) + row * H)[c];
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const h2_t a = __builtin_bit_cast(h2_t, v.x), b = __builtin_bit_cast(h2_t, v.y);
+    return make_float4(static_cast<float>(a[0]), static_cast<float>(a[1]), static_cast<float>(b[0]),
+                       static_cast<float>(b[1]));
+  } else {
+    return reinterpret_cast<const float4 *>(rows + row * H)[c];
+  }
+}
+
 // One block per token row.  With K <= kCombineSlots every row of a chunk is
 // requested at once (the slot rows are block-uniform, read through the
-// scalar cache), then added in slot order.
+// scalar cache), then added in slot order.  F16: the rows (and the shared
+// expert's) are fp16.
+template <bool F16>
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
   __shared__ float wave_sq[kCombineThreads / 64];
   const int t = blockIdx.x;
@@ -45,7 +61,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
 #pragma unroll
       for (int k = 0; k < kCombineSlots; ++k) {
         const int row = k < K ? inv[k] : -1;
-        const float4 x = reinterpret_cast<const float4 *>(a.rows_out + static_cast<size_t>(row < 0 ? 0 : row) * a.H)[c];
+        const float4 x = row4<F16>(a.rows_out, static_cast<size_t>(row < 0 ? 0 : row), a.H, c);
         v[k] = row >= 0 ? x : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
@@ -54,12 +70,12 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
     } else {
       for (int k = 0; k < K; ++k) {
         const int row = inv[k];
-        if (row >= 0) add4(acc, reinterpret_cast<const float4 *>(a.rows_out + static_cast<size_t>(row) * a.H)[c]);
+        if (row >= 0) add4(acc, row4<F16>(a.rows_out, static_cast<size_t>(row), a.H, c));
       }
     }
     const size_t o4 = static_cast<size_t>(t) * n4 + c;
     if (a.shared_out) {
-      const float4 sv = reinterpret_cast<const float4 *>(a.shared_out)[o4];
+      const float4 sv = row4<F16>(a.shared_out, static_cast<size_t>(t), a.H, c);
       if (a.shared_gate) {
         // the shared expert's row scaled by its gate, fused into the sum
         const float g = a.shared_gate[t];
@@ -113,7 +129,10 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  combine_kernel<<<a.T, kCombineThreads, 0, s>>>(a);
+  if (a.rows_f16)
+    combine_kernel<true><<<a.T, kCombineThreads, 0, s>>>(a);
+  else
+    combine_kernel<false><<<a.T, kCombineThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

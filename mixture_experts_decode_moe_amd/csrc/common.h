@@ -176,10 +176,11 @@ struct FfnArgs {
   const int32_t *row_tok;   // NULL: row r reads token r
   const float *row_w;       // NULL: weight 1
   float *act;               // [n_rows*F + T*Fs]
-  float *rows_out;          // [n_rows + (Fs ? T : 0)][H]
+  float *rows_out;          // [n_rows + (Fs ? T : 0)][H], fp32 or (rows_f16) fp16
+  int32_t rows_f16;         // 1: the down kernel writes rows_out in fp16 (prefill GEMM pair and W8A8 only)
   int32_t max_units;        // upper bound of routed units (grid sizing)
   const int32_t *units;     // [max_units] int4 (expert, first row, rows, 0) or NULL
-  uint32_t *queue;          // NULL, or two words, zero between calls: the prefill gate/up item queue
+  uint32_t *queue;          // NULL, or nine words, zero between calls: the prefill gate/up item queues
   // decode layer calls (E <= 256): the gate/up kernel routes the batch
   // itself from the router's partial logits and its last block publishes
   // the routing (the offsets, active, n_active, row_tok and row_w above
@@ -199,6 +200,9 @@ struct FfnArgs {
 hipError_t launch_gateup(const FfnArgs &a, hipStream_t s);
 bool mfma_decode_ok(const FfnArgs &a);  // the decode matrix-core kernels take this call
 hipError_t launch_down(const FfnArgs &a, hipStream_t s);
+// the prefill family's down launch for this call can write fp16 rows
+// (rows_f16); the caller checks mfma_decode_ok first
+bool down_rows_f16_ok(const FfnArgs &a);
 
 // Down projection and combine in one launch (decode layer calls of a few
 // tokens after the matrix-core gate/up kernel has published the routing).
@@ -221,7 +225,7 @@ hipError_t launch_w8a8(const FfnArgs &a, hipStream_t s, const LaunchEvents &ev_g
 hipError_t launch_down_combine(const DownCombineArgs &d, hipStream_t s);
 
 struct CombineArgs {
-  const float *rows_out;
+  const float *rows_out;        // fp32 rows, or fp16 rows with rows_f16 (shared_out alike)
   const int32_t *inv_pos;
   int32_t T, K, H;
   const float *shared_out;      // [T][H] or NULL
@@ -231,6 +235,7 @@ struct CombineArgs {
   uint16_t *residual_out;       // NULL: no residual epilogue
   uint16_t *normed_out;         // NULL: no normalised copy
   float eps;
+  int32_t rows_f16;
 };
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 

@@ -675,7 +675,11 @@ static hipError_t launch_down_mfma_f(const FfnArgs &a, hipStream_t s) {
   int jw, ks;
   split_k(a.F, block_k(FMT), kDnMaxWaves, jw, ks);
   const int tiles = a.H / 64;
-  const int grid = mfma_grid((a.Fs > 0 ? tiles : 0) + a.max_units * tiles);
+  // blocks loop over items: four a compute unit cover a decode call's items
+  // in one round without thousands of blocks that find none
+  const int items = (a.Fs > 0 ? tiles : 0) + a.max_units * tiles;
+  const int cap = 4 * cu_count();
+  const int grid = mfma_grid(items < cap ? items : cap);
   if (jw == 1)
     return launch_kernel(down_mfma_kernel<FMT, 1>, dim3(grid), dim3(64 * ks), 0, s, a.ev, a);
   else if (jw == 2)

@@ -754,14 +754,15 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
 
 // ------------------------------------------------ gate/up, 128-row items
 // The layer's gate/up GEMM once its router GEMM has written x in fp16
-// operand form (a.x16), with the workspace's item queue (a.queue: two words
-// that are zero between calls).  An item is (unit, up to 128 rows, 128
+// operand form (a.x16), with the workspace's item queues (a.queue: nine
+// words that are zero between calls).  An item is (unit, up to 128 rows, 128
 // SwiGLU columns), so that an expert's rows (64 on average for a prefill
 // chunk, rarely above 128) share one pass over its weights: each weight is
 // dequantized once per expert instead of once per 64 rows, and a step
 // carries up to four 32-row tiles of matrix work per dequantized chunk.
-// Blocks take items from the queue (the shared expert's, the largest,
-// first), so that they finish together although items differ in size.
+// Blocks take items from their XCD's queue (the shared expert's, the
+// largest, first), so that they finish together although items differ in
+// size.
 // The x rows and the weight chunks go from global memory straight into LDS
 // (no registers), two steps ahead, into three buffers each: each x row's
 // sixteen 16-byte pieces are stored at slot piece ^ (row & 15), each weight
@@ -770,6 +771,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
 // LDS bank once.  The weight loads cover 64 contiguous bytes of 16 rows
 // each, half the cache lines per request of per-lane register loads.
 constexpr int kG2Rows = 128;
+constexpr int kG2Queues = 8;  // item queues, one per XCD; the grid is a multiple of this
 
 // The unit table of a layer call for the 128-row gate/up kernel: the shared
 // expert first, then the experts with rows (offsets[e + 1] > offsets[e]) in
@@ -860,19 +862,26 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
   const int H = 128 * KS;
   const int n_units = gm_units_from_offsets(a, units, scratch, class_cnt);
   const int col_tiles = a.F / 128;
-  const int n_items = units.pre[n_units] * col_tiles;
+  // XCD-aware queues: block b runs on XCD b mod 8 and takes items from
+  // queue b mod 8, which holds the row tiles j = b mod 8 (mod 8), each row
+  // tile's column tiles in a row, so that the column tiles of a row tile run
+  // at about the same time on one XCD and share its L2 for their x rows
+  const int xq = blockIdx.x & (kG2Queues - 1);
+  const int row_tiles = units.pre[n_units];
+  const int n_items = (row_tiles > xq ? (row_tiles - xq + kG2Queues - 1) / kG2Queues : 0) * col_tiles;
   auto abuf = [&](int b, int r) __attribute__((always_inline)) {
     return (b == 0 ? g2_a0 : b == 1 ? g2_a1 : g2_a2) + r * 16;
   };
   auto bbuf = [&](int b) __attribute__((always_inline)) { return b == 0 ? g2_b0 : b == 1 ? g2_b1 : g2_b2; };
 
   for (;;) {
-    if (tid == 0) next_item = static_cast<int>(atomicAdd(&a.queue[0], 1u));
+    if (tid == 0) next_item = static_cast<int>(atomicAdd(&a.queue[xq], 1u));
     lds_barrier();
     const int item = next_item;
     if (item >= n_items) break;
-    const int j = item / col_tiles;
-    const int ct = item - j * col_tiles;
+    const int jl = item / col_tiles;
+    const int ct = item - jl * col_tiles;
+    const int j = kG2Queues * jl + xq;
     const int u = pf_find(units.pre, n_units, j);
     const PfUnit un = gm_unit(units, u);
     const int m0 = (j - units.pre[u]) * kG2Rows;
@@ -1059,9 +1068,9 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
   // the last block out leaves the queue words zero for the next call
   if (tid == 0) {
     __threadfence();
-    if (atomicAdd(&a.queue[1], 1u) == gridDim.x - 1) {
-      atomicExch(&a.queue[0], 0u);
-      atomicExch(&a.queue[1], 0u);
+    if (atomicAdd(&a.queue[kG2Queues], 1u) == gridDim.x - 1) {
+#pragma unroll
+      for (int q = 0; q <= kG2Queues; ++q) atomicExch(&a.queue[q], 0u);
     }
   }
 }
@@ -1074,7 +1083,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
 // columns (16 rows of 64 contiguous bytes a request, blocks swizzled by
 // row); the block scales are register loads.  The products leave the
 // accumulators directly (32 lanes: 32 consecutive columns of one row).
-template <int KS>
+template <int KS, bool F16>
 __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
   static_assert(KS == 4, "four k-steps");
   __shared__ uint4 dn_a0[kPfRows * 16], dn_a1[kPfRows * 16];
@@ -1200,17 +1209,30 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
       step(IntC<3>{});
     });
     // rows of the tile times their routing weights, straight to the output
-    // rows: register jj of lane (c, h) is row 32 mt + (jj & 3) + 8 (jj >> 2) + 4 h
+    // rows (fp32, or rounded once to fp16 with rows_f16): register jj of
+    // lane (c, h) is row 32 mt + (jj & 3) + 8 (jj >> 2) + 4 h
     {
       const int orow0 = shared ? a.n_rows + m0 : un.r0 + m0;
-      float *op = a.rows_out + static_cast<size_t>(orow0 + 4 * h) * H + hcol;
+      const size_t o0 = static_cast<size_t>(orow0 + 4 * h) * H + hcol;
+      if constexpr (F16) {
+        _Float16 *op = reinterpret_cast<_Float16 *>(a.rows_out) + o0;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const int R = 32 * mt + (jj & 3) + 8 * (jj >> 2);
-          if (R + 4 * h < rows) op[R * H] = acc[mt][jj] * wrow[R + 4 * h];
-        }
+          for (int jj = 0; jj < 16; ++jj) {
+            const int R = 32 * mt + (jj & 3) + 8 * (jj >> 2);
+            if (R + 4 * h < rows) op[R * H] = static_cast<_Float16>(acc[mt][jj] * wrow[R + 4 * h]);
+          }
+      } else {
+        float *op = a.rows_out + o0;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int R = 32 * mt + (jj & 3) + 8 * (jj >> 2);
+            if (R + 4 * h < rows) op[R * H] = acc[mt][jj] * wrow[R + 4 * h];
+          }
+      }
     }
     lds_barrier();  // the next item's tiles and row weights reuse the memory
   }
@@ -1496,13 +1518,20 @@ __global__ void __launch_bounds__(kGmThreads) w8a8_gemm_kernel(FfnArgs a) {
     } else {
       const int col = cg * 256 + 32 * wave + c;
       const float sd = static_cast<const float *>(shared ? a.sds : a.ds)[static_cast<size_t>(e) * a.H + col];
+      _Float16 *o16 = reinterpret_cast<_Float16 *>(a.rows_out);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r16 = 0; r16 < 16; ++r16) {
           const int m = 32 * mt + 8 * (r16 >> 2) + 4 * h + (r16 & 3);
-          if (m < rows) a.rows_out[static_cast<size_t>(arow[m]) * a.H + col] =
-              static_cast<float>(acc[mt][r16]) * rsc[m] * sd;
+          const float v = static_cast<float>(acc[mt][r16]) * rsc[m] * sd;
+          const size_t o = static_cast<size_t>(arow[m]) * a.H + col;
+          if (m < rows) {
+            if (a.rows_f16)
+              o16[o] = static_cast<_Float16>(v);  // rounded once (rows_f16)
+            else
+              a.rows_out[o] = v;
+          }
         }
     }
   }
@@ -1614,7 +1643,9 @@ hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    return launch_kernel(gateup_gemm128_kernel<16>, dim3(cus), dim3(kGmThreads), 0, s, a.ev, a);
+    // every queue needs blocks: a multiple of kG2Queues
+    const int grid = (cus + kG2Queues - 1) / kG2Queues * kG2Queues;
+    return launch_kernel(gateup_gemm128_kernel<16>, dim3(grid), dim3(kGmThreads), 0, s, a.ev, a);
   }
   if (gm_pair_ok(a)) {
     return launch_kernel(gateup_gemm_kernel<16>, dim3(gm_grid(pf_tiles_upper(a) * (a.F / 128), 1)), dim3(kGmThreads), 0,
@@ -1624,10 +1655,13 @@ hipError_t launch_gateup_prefill(const FfnArgs &a, hipStream_t s) {
                        s, a.ev, a);
 }
 
+bool down_rows_f16_ok(const FfnArgs &a) { return prefill_ok(a) && gm_pair_ok(a); }
+
 hipError_t launch_down_prefill(const FfnArgs &a, hipStream_t s) {
   if (gm_pair_ok(a)) {
-    return launch_kernel(down_gemm_kernel<4>, dim3(gm_grid(pf_tiles_upper(a) * (a.H / 256), 2)), dim3(kGmThreads), 0, s, a.ev,
-                         a);
+    const dim3 grid(gm_grid(pf_tiles_upper(a) * (a.H / 256), 2));
+    if (a.rows_f16) return launch_kernel(down_gemm_kernel<4, true>, grid, dim3(kGmThreads), 0, s, a.ev, a);
+    return launch_kernel(down_gemm_kernel<4, false>, grid, dim3(kGmThreads), 0, s, a.ev, a);
   }
   return launch_kernel(down_prefill_kernel, dim3(pf_grid(pf_tiles_upper(a) * (a.H / kPfCols))), dim3(kPfThreads), 0,
                        s, a.ev, a);
