@@ -144,6 +144,35 @@ def copy_ceiling_gbs(torch, traffic_bytes, n_copies=60):
     return 2 * half / (us * 1e-6) / 1e9
 
 
+def read_ceiling_gbs(torch, mb, nbytes, n_reads=40):
+    """Read rate (GB/s) of the library's plain read-stream kernel
+    (moe_calib_read) reading the given number of bytes in one launch: the
+    achievable rate of a kernel that only streams that many bytes, beside
+    the 8 TB/s peak.  The sources rotate over at least 1 GiB so that none is
+    still in the 256 MB last-level cache; median of n_reads launches."""
+    n = max(int(nbytes) // 256 * 256, 256)
+    n_src = max(2, min(512, (1 << 30) // n + 1))
+    srcs = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i & 0xFF) for i in range(n_src)]
+    torch.cuda.synchronize()
+    for i in range(3):
+        mb.calib_read(srcs[i % n_src], n)
+    ms = sorted(mb.calib_read(srcs[(i + 3) % n_src], n) for i in range(n_reads))
+    del srcs
+    torch.cuda.empty_cache()
+    return n / (ms[len(ms) // 2] * 1e-3) / 1e9
+
+
+def mfma_achievable_tflops(mb, kind):
+    """Issue rate (TFLOP/s, or TOP/s for int8) of the library's pure matrix-core
+    kernel (moe_calib_mfma): kind 0 fp16 32x32x16, 2 int8 32x32x32; the best
+    of three launches of about a millisecond."""
+    best = 0.0
+    for _ in range(3):
+        ms, ops = mb.calib_mfma(kind, 10000)
+        best = max(best, ops / (ms * 1e-3) / 1e12)
+    return best
+
+
 class Workload:
     """Device-resident inputs of one workload and its step function."""
 
@@ -258,9 +287,12 @@ def time_steps(wl, K_steps, reps, host_ms):
     return out
 
 
-def stage_times(wl, n_steps):
+def stage_times(wl, n_steps, host_ms):
     """Mean kernel durations (us) of the gate/up and down stages over n_steps
-    profiled steps (events requested per call, outside the timed region)."""
+    profiled steps (events requested per call, outside the timed region).
+    As in the timed repetitions, the calls are queued behind a spin kernel
+    first, so that the GPU runs them back to back rather than each on an
+    idle device."""
     torch, mb = wl.torch, wl.mb
     stream = torch.cuda.current_stream()
     n_calls = n_steps * wl.calls_per_step
@@ -270,19 +302,20 @@ def stage_times(wl, n_steps):
         for a_, b_ in ev[st]:
             a_.record(stream)
             b_.record(stream)
+    opts = [mb.forward_opts(events={st: ev[st][c] for st in ev}, **wl.opts_kw) for c in range(n_calls)]
     torch.cuda.synchronize()
+    torch.cuda._sleep(int((1.5 * host_ms * n_steps + 10.0) * 1e-3 * 2.4e9))
     c = 0
     for i in range(n_steps):
         for l in range(wl.calls_per_step):
-            opts = mb.forward_opts(events={st: ev[st][c] for st in ev}, **wl.opts_kw)
-            wl.call(i, l, opts=opts)
+            wl.call(i, l, opts=opts[c])
             c += 1
     torch.cuda.synchronize()
     return {st: float(np.mean([hip_elapsed_ms(a_, b_) for a_, b_ in ev[st]])) * 1e3 for st in ev}
 
 
 def measure(wl, K_steps, warmup, reps, prof_steps):
-    torch = wl.torch
+    torch, mb = wl.torch, wl.mb
     shp = wl.shape
     T, H, E, K, F = wl.T, wl.H, wl.E, wl.K, wl.F
     torch.cuda.synchronize()
@@ -293,7 +326,8 @@ def measure(wl, K_steps, warmup, reps, prof_steps):
     torch.cuda.synchronize()
     per_rep = time_steps(wl, K_steps, reps, host_ms)
     ms_per_step = float(np.median(per_rep))
-    stage_us = stage_times(wl, prof_steps)
+    # single-call steps: at least 20 profiled calls
+    stage_us = stage_times(wl, prof_steps if wl.calls_per_step > 1 else max(prof_steps, 20), host_ms)
     U = wl.unique_experts()
     log(f"  host enqueue {host_ms:.3f} ms/step; repetitions (ms/step): "
         + ", ".join(f"{v:.4f}" for v in per_rep) + "; stage means: "
@@ -314,15 +348,17 @@ def measure(wl, K_steps, warmup, reps, prof_steps):
     w8a8 = bool(wl.opts_kw.get("act_quant"))
     rows = T * K + (T if Fs else 0)
     if w8a8:
-        # int8 x rows in, fp32 SwiGLU rows out; int8 SwiGLU rows in, fp32 rows out
+        # int8 x rows in, fp32 SwiGLU rows out; int8 SwiGLU rows in, fp16 rows out
         gateup_bytes = U * gu_bytes + sh_gu + T * H + rows * F * 4
-        down_bytes = U * dn_bytes + sh_dn + rows * F + rows * H * 4
+        down_bytes = U * dn_bytes + sh_dn + rows * F + rows * H * 2
     else:
         # the SwiGLU rows between the two kernels: bf16 hi + lo (4 bytes an
         # element) for decode calls, one fp16 plane (2 bytes) for prefill
         act_b = 2 if prefill else 4
         gateup_bytes = U * gu_bytes + sh_gu + T * H * 2 + (T * K * F + T * Fs) * act_b
-        down_out = T * H * 4 if fused_down else (T * K + (T if Fs else 0)) * H * 4
+        # expert output rows: fp32 from the decode kernels, fp16 from the
+        # prefill GEMMs; the one-launch down + combine writes y instead
+        down_out = T * H * 4 if fused_down else (T * K + (T if Fs else 0)) * H * (2 if prefill else 4)
         down_bytes = U * dn_bytes + sh_dn + (T * K * F + T * Fs) * act_b + down_out
     kern = {"gateup": (gateup_bytes, stage_us["gateup"]), "down": (down_bytes, stage_us["down"])}
     dom = max(kern, key=lambda k: kern[k][1])
@@ -337,11 +373,15 @@ def measure(wl, K_steps, warmup, reps, prof_steps):
         # matrix-core fraction is reported beside it
         ops = {"gateup": 2.0 * rows * 2 * H * F, "down": 2.0 * rows * H * F}[dom]
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+        int8_ach = mfma_achievable_tflops(mb, 2)
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, kernel_name),
                     "kernel": kernel_name, "kernel_us": dom_us, "kernel_bytes": dom_bytes, "kernel_int8_ops": ops,
-                    "int8_mfma_frac": ops / (dom_us * 1e-6) / 1e12 / INT8_PEAK_TOPS, "stage_us": stage_us,
-                    "copy_ceiling_gbs": copy_ceiling_gbs(torch, dom_bytes)}
+                    "int8_mfma_frac": ops / (dom_us * 1e-6) / 1e12 / INT8_PEAK_TOPS,
+                    "int8_achievable_tops": int8_ach,
+                    "int8_frac_of_achievable": ops / (dom_us * 1e-6) / 1e12 / int8_ach, "stage_us": stage_us,
+                    "copy_ceiling_gbs": copy_ceiling_gbs(torch, dom_bytes),
+                    "read_ceiling_gbs": read_ceiling_gbs(torch, mb, dom_bytes)}
     elif prefill:
         # useful matrix-core work of the dominant grouped GEMM: every routed
         # and shared row through gate+up (2 H F each, 2 flops a product) or
@@ -349,16 +389,19 @@ def measure(wl, K_steps, warmup, reps, prof_steps):
         rows = T * K + (T if Fs else 0)
         flops = {"gateup": 2.0 * rows * 2 * H * F, "down": 2.0 * rows * H * F}[dom]
         achieved = flops / (dom_us * 1e-6) / 1e12
+        f16_ach = mfma_achievable_tflops(mb, 0)
         roofline = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": measured_traffic(wl.name, kernel_name),
                     "kernel": kernel_name, "kernel_us": dom_us, "kernel_flops": flops, "kernel_bytes": dom_bytes,
+                    "mfma_achievable_tflops": f16_ach, "frac_of_achievable": achieved / f16_ach,
                     "stage_us": stage_us}
     else:
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, kernel_name),
                     "kernel": kernel_name, "kernel_us": dom_us, "kernel_bytes": dom_bytes, "stage_us": stage_us,
-                    "copy_ceiling_gbs": copy_ceiling_gbs(torch, dom_bytes)}
+                    "copy_ceiling_gbs": copy_ceiling_gbs(torch, dom_bytes),
+                    "read_ceiling_gbs": read_ceiling_gbs(torch, mb, dom_bytes)}
     # whole-layer algorithmic bytes (router + unique experts + shared + x + y)
     layer_bytes = E * H * 4 + U * (gu_bytes + dn_bytes) + sh_gu + sh_dn + T * H * 2 + T * H * 4
     layer_ms = ms_per_step / wl.calls_per_step
@@ -432,8 +475,8 @@ def main():
                     help="only run a plain device copy of this many MiB (20 times), the known-size reference for "
                          "the HBM byte counters, and exit")
     ap.add_argument("--copy-sweep", action="store_true",
-                    help="only time the plain device copy over a range of sizes (the streaming rate one launch of "
-                         "each size reaches) and exit")
+                    help="only time the plain device copy and the library's read-stream kernel over a range of "
+                         "sizes (the streaming rates one launch of each size reaches) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -443,9 +486,11 @@ def main():
 
     if args.copy_sweep:
         import torch
+        from mixture_experts_decode_moe_amd import binding as mb
         for mib in (4, 8, 16, 36, 64, 128, 256, 1024):
             g = copy_ceiling_gbs(torch, mib << 20)
-            print(json.dumps({"copy_traffic_mib": mib, "GBps": g}), flush=True)
+            r = read_ceiling_gbs(torch, mb, mib << 20)
+            print(json.dumps({"copy_traffic_mib": mib, "GBps": g, "read_GBps": r}), flush=True)
         return
 
     if args.calibrate_copy_mib:

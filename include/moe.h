@@ -291,6 +291,31 @@ int moe_layer_forward_noalloc(const moe_layer *L, const uint16_t *x_bf16, int32_
                               const moe_residual *res, int32_t *topk_ids, float *topk_w,
                               const moe_forward_opts *opts, void *stream);
 
+/* ---- Measurement helpers (not on the layer path) ----
+ *
+ * The achievable ceilings the expert kernels are compared with, measured on
+ * the current device.  Each makes its launches on `stream` between two HIP
+ * events it creates, waits for the second (host-blocking) and touches no
+ * caller memory except what it is given to read.  Errors:
+ * MOE_ERR_INVALID_ARG for arguments outside the stated ranges, MOE_ERR_HIP
+ * for a failed launch or event. */
+
+/* Matrix-core issue rate: 4 blocks a compute unit of 4 waves, each wave
+ * issuing `iters` x 4 independent MFMAs from registers (no memory traffic):
+ * kind 0 v_mfma_f32_32x32x16_f16, 1 v_mfma_f32_32x32x16_bf16,
+ * 2 v_mfma_i32_32x32x32_i8.  One untimed launch precedes the timed one.
+ * *ms receives the timed launch's duration and *ops the operations it
+ * performed (2 per multiply-add).  1 <= iters <= 2^24. */
+int moe_calib_mfma(int32_t kind, int32_t iters, float *ms, double *ops, void *stream);
+
+/* HBM read rate: one launch that reads the `bytes` bytes at device address
+ * `src` once (16-byte aligned, bytes a nonzero multiple of 16) with eight
+ * 16-byte loads in flight per thread, at most one 1024-thread block a
+ * compute unit.  *ms receives the launch's duration.  The rate is a ceiling
+ * only when `src` is not already in the last-level cache: callers rotate
+ * over buffers larger than it. */
+int moe_calib_read(const void *src, size_t bytes, float *ms, void *stream);
+
 /* Static text for a status code (host). */
 const char *moe_status_string(int status);
 

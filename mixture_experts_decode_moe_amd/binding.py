@@ -76,6 +76,9 @@ _SIGS = {
     "moe_layer_forward_ex": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _PO, _vp], ctypes.c_int),
     "moe_layer_forward_noalloc": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _PO, _vp], ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_calib_mfma": ([_i32, _i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double), _vp],
+                       ctypes.c_int),
+    "moe_calib_read": ([_vp, _sz, ctypes.POINTER(ctypes.c_float), _vp], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -290,6 +293,23 @@ def layer_forward_noalloc(layer: Layer, x_bf16, y, res: MoeResidual | None = Non
     _check("moe_layer_forward_noalloc", _lib.moe_layer_forward_noalloc(
         ctypes.byref(c), _ptr(x_bf16), T, _ptr(y), ctypes.byref(res) if res is not None else None,
         _ptr(topk_ids), _ptr(topk_w), ctypes.byref(opts) if opts is not None else None, _stream(stream)))
+
+
+def calib_mfma(kind: int, iters: int, stream=None):
+    """moe_calib_mfma: (ms, operations) of one launch of the matrix-core
+    issue-rate kernel (kind 0 fp16, 1 bf16, 2 int8)."""
+    ms, ops = ctypes.c_float(), ctypes.c_double()
+    _check("moe_calib_mfma", _lib.moe_calib_mfma(kind, iters, ctypes.byref(ms), ctypes.byref(ops), _stream(stream)))
+    return ms.value, ops.value
+
+
+def calib_read(buf: torch.Tensor, nbytes: int, stream=None) -> float:
+    """moe_calib_read: ms of one launch reading the first nbytes of buf."""
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    ms = ctypes.c_float()
+    _check("moe_calib_read", _lib.moe_calib_read(_ptr(buf), nbytes, ctypes.byref(ms), _stream(stream)))
+    return ms.value
 
 
 def raw_lib():

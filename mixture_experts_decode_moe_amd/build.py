@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "expert_decode.hip", "expert_mfma.hip", "expert_prefill.hip", "down_combine.hip", "combine.hip", "noalloc.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "expert_decode.hip", "expert_mfma.hip", "expert_prefill.hip", "down_combine.hip", "combine.hip", "noalloc.hip", "calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

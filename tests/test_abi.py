@@ -122,6 +122,21 @@ def test_other_entry_points_reject_bad_arguments(mb):
     assert lib.moe_workspace_init(None, 0, None) == -3
 
 
+def test_calibration_helpers_reject_bad_arguments(mb):
+    """The measurement helpers check their arguments before touching a
+    device."""
+    lib = mb.raw_lib()
+    ms, ops = ctypes.c_float(), ctypes.c_double()
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.moe_calib_mfma(3, 10, ctypes.byref(ms), ctypes.byref(ops), None) == -1
+    assert lib.moe_calib_mfma(0, 0, ctypes.byref(ms), ctypes.byref(ops), None) == -1
+    assert lib.moe_calib_mfma(0, 10, None, ctypes.byref(ops), None) == -1
+    assert lib.moe_calib_read(None, 1 << 20, ctypes.byref(ms), None) == -1
+    assert lib.moe_calib_read(p, 0, ctypes.byref(ms), None) == -1
+    assert lib.moe_calib_read(p, 1000, ctypes.byref(ms), None) == -1  # not a multiple of 16
+    assert lib.moe_calib_read(ctypes.c_void_p((1 << 20) + 8), 1 << 20, ctypes.byref(ms), None) == -1
+
+
 def test_forward_options_are_validated(mb):
     """Per-call options: an unknown path or a nonzero reserved word is
     rejected before anything is launched; all-zero options are the

@@ -176,3 +176,24 @@ def test_expert_ffn_and_combine(mb, cfg, tokens):
     assert np.abs(r_ref.astype(np.int32) - pu.host_u16(r_out).astype(np.int32)).max() <= 1
     n_ref = oracle.rmsnorm(pu.host_u16(r_out))
     assert np.abs(n_ref.astype(np.int32) - pu.host_u16(normed).astype(np.int32)).max() <= 1
+
+
+def test_calibration_helpers(mb):
+    """The ceilings the roofline figures are compared with: the matrix-core
+    issue kernel and the read-stream kernel run, and their rates sit below
+    the data-sheet peaks (2516.6 TFLOP/s fp16, 5033 TOP/s int8, 8000 GB/s)
+    and above a tenth of them."""
+    import torch
+    for kind, peak in ((0, 2516.6), (1, 2516.6), (2, 5033.2)):
+        ms, ops = mb.calib_mfma(kind, 2000)
+        rate = ops / (ms * 1e-3) / 1e12
+        say(f"matrix cores kind {kind}: {rate:.0f} of {peak}")
+        assert 0.1 * peak < rate <= 1.02 * peak
+    # 1 GiB filled, then its first 512 MiB read (the 256 MB last-level
+    # cache holds at most the end of the fill)
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    torch.cuda.synchronize()
+    ms = mb.calib_read(buf, 512 << 20)
+    gbs = (512 << 20) / (ms * 1e-3) / 1e9
+    say(f"read 512 MiB: {gbs:.0f} GB/s")
+    assert 800 < gbs <= 8000 * 1.02
