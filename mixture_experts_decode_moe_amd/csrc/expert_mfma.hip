@@ -155,35 +155,57 @@ MOE_DEV GuPtrs gu_ptrs(const FfnArgs &a) {
   return p;
 }
 
-// Loads this lane's part of item (e, f0): lanes n < 8 the gate row f0 + n,
-// lanes n >= 8 the up row f0 + n - 8 (e < 0: the shared expert).
+// This lane's weight and scale bases and its fixed byte offsets, set once
+// per block: lanes n < 8 read gate rows, lanes n >= 8 up rows; the routed
+// and the shared expert's matrices.  Offsets from these bases fit 32 bits
+// (mfma_decode_ok checks the matrix sizes).
+struct GuLane {
+  gchar_t *q_r, *q_s, *s_r, *s_s;  // weights / scales, routed and shared
+  uint32_t w_off;                  // this lane's bytes within a row: 64 (wave JW) + 16 g
+  uint32_t n7;                     // the lane's row within the item's gate or up rows
+};
+
 template <int FMT, int JW>
-MOE_DEV void gu_load(const FfnArgs &a, const GuPtrs &P, int e, int f0, int wave, int n, int g,
-                     GuWeights<FMT, JW> &w) {
+MOE_DEV GuLane gu_lane(const GuPtrs &P, int wave, int n, int g) {
+  const bool up = n >= 8;
+  GuLane L;
+  L.q_r = up ? P.uq : P.gq;
+  L.q_s = up ? P.suq : P.sgq;
+  L.s_r = up ? P.us : P.gs;
+  L.s_s = up ? P.sus : P.sgs;
+  L.w_off = 64u * static_cast<uint32_t>(wave * JW) + 16u * static_cast<uint32_t>(g);
+  L.n7 = static_cast<uint32_t>(n & 7);
+  return L;
+}
+
+// Loads this lane's part of item (e, f0) (e < 0: the shared expert); e and
+// f0 are wave-uniform.  Row f0 + n7 of the gate or up matrix: JW 16-byte
+// chunks at w_off + 64 jj, and the chunks' block scales (int4) or the row
+// scale (int8).
+template <int FMT, int JW>
+MOE_DEV void gu_load(const FfnArgs &a, const GuLane &L, int e, int f0, GuWeights<FMT, JW> &w) {
   using Fm = MfmaFmt<FMT>;
   const bool shared = e < 0;
-  const bool up = n >= 8;
-  const int F = shared ? a.Fs : a.F;
-  const size_t row = static_cast<size_t>(shared ? 0 : e) * F + f0 + (n & 7);
-  gchar_t *gq = shared ? P.sgq : P.gq, *uq = shared ? P.suq : P.uq;
-  gchar_t *gs = shared ? P.sgs : P.gs, *us = shared ? P.sus : P.us;
-  gchar_t *q = up ? uq : gq;
-  gchar_t *sc = up ? us : gs;
-  const int nblk = a.H / Fm::kBlockK;
-  gchar_t *p = q + row * nblk * 16;
+  const uint32_t F = static_cast<uint32_t>(shared ? a.Fs : a.F);
+  const uint32_t nblk = static_cast<uint32_t>(a.H / Fm::kBlockK);
+  const uint32_t row = (shared ? 0u : static_cast<uint32_t>(e)) * F + static_cast<uint32_t>(f0) + L.n7;
+  gchar_t *q = shared ? L.q_s : L.q_r;
+  gchar_t *sc = shared ? L.s_s : L.s_r;
+  const uint32_t woff = row * (nblk * 16u) + L.w_off;
 #pragma unroll
-  for (int jj = 0; jj < JW; ++jj) w.w[jj] = load_stream16_g(p + 16 * (4 * (wave * JW + jj) + g));
+  for (int jj = 0; jj < JW; ++jj) w.w[jj] = load_stream16_g(q + (woff + 64u * jj));
   if constexpr (FMT == MOE_W_INT4_B32) {
-    gu32_t *sp = reinterpret_cast<gu32_t *>(sc + row * nblk * 2);
+    // the four fp16 scales of each chunk: 8 bytes at 8 (wave JW + jj)
+    const uint32_t soff = row * (nblk * 2u) + (L.w_off & ~63u) / 8u;
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
-      const int j = wave * JW + jj;
-      w.s[jj][0] = sp[2 * j];
-      w.s[jj][1] = sp[2 * j + 1];
+      const u32x2_t sv = *reinterpret_cast<gu2_t *>(sc + (soff + 8u * jj));
+      w.s[jj][0] = sv.x;
+      w.s[jj][1] = sv.y;
     }
     w.rs = 1.f;
   } else {
-    w.rs = reinterpret_cast<gf32_t *>(sc)[row];
+    w.rs = *reinterpret_cast<gf32_t *>(sc + row * 4u);
   }
 }
 
@@ -216,7 +238,7 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   constexpr bool kInt4 = FMT == MOE_W_INT4_B32;
   extern __shared__ uint4 xs_lds[];  // [T][H/8 + 1] 16-byte pieces of x
   __shared__ f32x4_t red[kGuGroup][kGuMaxWaves][64];  // partial tiles of a group of items
-  __shared__ int tab[kGuTable][4];   // e, r0, n (<= 16), f0
+  __shared__ __attribute__((aligned(16))) int tab[kGuTable][4];  // e, r0, n (<= 16), f0
   __shared__ int toks[kGuTable][16];
   __shared__ uint32_t act_st[NI][16][8];  // SwiGLU outputs of a chunk: bf16 hi | lo << 16
   const int tid = threadIdx.x;
@@ -372,14 +394,22 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   // is issued first (unconditionally: a missing item re-requests the
   // chunk's first item, already in flight), so the wait before each item
   // leaves the later items' loads in flight.
-  const GuPtrs P = gu_ptrs(a);
+  const GuLane GL = gu_lane<FMT, JW>(gu_ptrs(a), wave, n, g);
   for (int c0 = 0; c0 < my_items; c0 += NI) {
     GuWeights<FMT, JW> w[NI];
+    // the chunk's item records first (one LDS read each, all in flight
+    // together), made wave-uniform, then every weight request
+    int te[NI], tf[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int it = c0 + i < my_items ? c0 + i : c0;
-      gu_load<FMT, JW>(a, P, tab[it][0], tab[it][3], wave, n, g, w[i]);
+      const int4 rec = *reinterpret_cast<const int4 *>(tab[it]);
+      te[i] = rec.x;
+      tf[i] = rec.w;
     }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      gu_load<FMT, JW>(a, GL, __builtin_amdgcn_readfirstlane(te[i]), __builtin_amdgcn_readfirstlane(tf[i]), w[i]);
     // groups of kGuGroup items: every wave's partial tiles of the group go to
     // LDS, then one pass adds them and applies SwiGLU (two barriers a group)
 #pragma unroll
@@ -623,7 +653,10 @@ bool mfma_decode_ok(const FfnArgs &a) {
   // every unit's rows are among the n_rows routed rows, and with distinct
   // experts per token a unit has at most T rows
   const bool rows16 = a.n_rows <= 16 || a.distinct_ids;
-  return a.path != kPathPrefill && rows16 && (a.fmt == MOE_W_INT4_B32 || a.fmt == MOE_W_INT8_ROW) &&
+  // the gate/up kernel addresses weights and scales with 32-bit offsets
+  const uint64_t mat_bytes = static_cast<uint64_t>(a.n_experts > 0 ? a.n_experts : 1) * a.F * a.H;
+  const bool off32 = mat_bytes < (1ull << 32) && static_cast<uint64_t>(a.Fs) * a.H < (1ull << 32);
+  return a.path != kPathPrefill && rows16 && off32 && (a.fmt == MOE_W_INT4_B32 || a.fmt == MOE_W_INT8_ROW) &&
          a.T <= kFusedTokens && lds <= 160 * 1024 &&
          (a.Fs == 0 || a.Fs == a.F) && split_k(a.H, block_k(a.fmt), kGuMaxWaves, jw, ks) &&
          split_k(a.F, block_k(a.fmt), kDnMaxWaves, jw, ks);

@@ -448,7 +448,6 @@ __global__ void __launch_bounds__(kPfThreads) down_prefill_kernel(FfnArgs a) {
 // result read by a VALU instruction right after the branch without the
 // wait states the matrix core needs, and those reads saw stale registers.)
 
-typedef __attribute__((address_space(1))) const u32x2_t gu2_t;
 
 
 template <class Fn>

@@ -188,6 +188,7 @@ struct MfmaFmt<MOE_W_INT8_ROW> {
 typedef __attribute__((address_space(1))) const char gchar_t;
 typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
 typedef __attribute__((address_space(1))) const uint32_t gu32_t;
+typedef __attribute__((address_space(1))) const u32x2_t gu2_t;
 typedef __attribute__((address_space(1))) const float gf32_t;
 
 MOE_DEV gchar_t *uniform_gptr(const void *p) {
