@@ -772,6 +772,10 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm_kernel(FfnArgs a) {
 constexpr int kG2Rows = 128;
 constexpr int kG2Queues = 8;  // item queues, one per XCD; the grid is a multiple of this
 
+// Requests one k-step's loads issue in gateup_gemm128_kernel: the A tiles
+// (ms) and two weight chunks.
+constexpr int g2_requests(int, int ms) { return ms + 2; }
+
 // The unit table of a layer call for the 128-row gate/up kernel: the shared
 // expert first, then the experts with rows (offsets[e + 1] > offsets[e]) in
 // index order, from one read of the offsets (no dependent reads of the
@@ -929,9 +933,15 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
       }
       xoff[i] = static_cast<uint32_t>(t) * (2 * H) + 16 * ((lane & 15) ^ (r & 15));
     }
-    // the requests of step s into buffer s % 3: its A tiles (MS), its weight
-    // chunks (2 direct loads), its block scales (1 register load)
-    u32x2_t bs[3];
+    // the item's block scales, requested first: lane half h holds those of
+    // steps 8 h .. 8 h + 7 (64 of its row's 128 bytes); a step takes the
+    // holder half's words with one lane swap.  (Register loads of a step's
+    // scales beside its direct loads cost about a seventh of the kernel.)
+    u32x4_t sreg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sreg[i] = *reinterpret_cast<gu32x4_t *>(wsc + (soff + 64u * h + 16u * i));
+    // the requests of step s into buffer s % 3: its A tiles (MS) and its
+    // weight chunks (2 direct loads)
     auto load_step = [&](int s, auto msc) __attribute__((always_inline)) {
       constexpr int MS = decltype(msc)::value;
       const int b = s % 3;
@@ -945,7 +955,6 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
         __builtin_amdgcn_global_load_lds(bq + (boff[k] + 64u * s),
                                          (__attribute__((address_space(3))) void *)(bbuf(b) + (32 * wave + 16 * k) * 4),
                                          16, 0, 0);
-      bs[b] = *reinterpret_cast<gu2_t *>(wsc + (soff + 8u * s));
     };
 
     f32x16_t acc[4];
@@ -953,14 +962,13 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
     for (int mt = 0; mt < 4; ++mt) acc[mt] = zero16();
     with_msub((rows + 31) >> 5, [&](auto msc) __attribute__((always_inline)) {
       constexpr int MS = decltype(msc)::value;
-      constexpr int G = MS + 3;  // requests a step
       // steps 0 and 1; the wait leaves step 1's requests pending (the waits
       // count requests in issue order, so each group is pinned)
       load_step(0, msc);
       __builtin_amdgcn_sched_barrier(0);
       load_step(1, msc);
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(g2_requests(1, MS)));
       lds_barrier();
       auto step = [&](auto sc) __attribute__((always_inline)) {
         constexpr int s = decltype(sc)::value;
@@ -970,18 +978,24 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
         for (int i = 0; i < 4; ++i) pin_u32(xoff[i]);
 #pragma unroll
         for (int k = 0; k < 2; ++k) pin_u32(boff[k]);
-        // two steps ahead (clamped: past the end it re-reads the last step
-        // into a buffer no later step reads)
-        load_step(s + 2 < KS ? s + 2 : KS - 1, msc);
+        // two steps ahead (clamped: past the end it re-reads the last step,
+        // the same bytes into the same buffer)
+        constexpr int ahead = s + 2 < KS ? s + 2 : KS - 1;
+        load_step(ahead, msc);
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t *brow = reinterpret_cast<const uint32_t *>(bbuf(b) + Rm * 4);
         const int rsw = (Rm >> 2) & 3;
+        const u32x4_t &sq = sreg[(s & 7) >> 1];
+        const auto sw01 = __builtin_amdgcn_permlane32_swap((s & 1) ? sq.z : sq.x, (s & 1) ? sq.z : sq.x, false, false);
+        const auto sw23 = __builtin_amdgcn_permlane32_swap((s & 1) ? sq.w : sq.y, (s & 1) ? sq.w : sq.y, false, false);
+        // [0]: the lower half's word in every lane, [1]: the upper half's
+        const uint32_t s01 = s < 8 ? sw01[0] : sw01[1], s23 = s < 8 ? sw23[0] : sw23[1];
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) {
           // k 16 t8 .. 16 t8 + 15 of the step: block t8 / 2, word 2 (t8 % 2) + h
           const int p = t8 >> 1;
           const uint32_t w = brow[4 * (p ^ rsw) + 2 * (t8 & 1) + h];
-          const u32x4_t B = dequant_f16_pairs(w, bs[b].x, bs[b].y, p);
+          const u32x4_t B = dequant_f16_pairs(w, s01, s23, p);
           const int slot = (2 * t8 + h) ^ (c & 15);
           uint4 Av[MS];
 #pragma unroll
@@ -993,7 +1007,7 @@ __global__ void __launch_bounds__(kGmThreads, 2) gateup_gemm128_kernel(FfnArgs a
           }
         }
         // step s + 1 has landed once at most step s + 2's requests are pending
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(g2_requests(ahead, MS)));
         lds_barrier();
       };
       step(IntC<0>{});
@@ -1150,7 +1164,9 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
       const int r = tid < rows ? tid : 0;
       wrow[tid] = shared || !a.row_w ? 1.f : a.row_w[un.r0 + m0 + r];
     }
-    u32x2_t bs[2];
+    // the item's block scales, requested first: lane half h holds those of
+    // steps 2 h and 2 h + 1 (16 of its row's 32 bytes), taken by a lane swap
+    const u32x4_t sreg = *reinterpret_cast<gu32x4_t *>(dsc + (soff + 16u * h));
     auto load_step = [&](int s) __attribute__((always_inline)) {
       const int b = s & 1;
 #pragma unroll
@@ -1163,7 +1179,6 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
         __builtin_amdgcn_global_load_lds(dq + (boff[k] + 64u * s),
                                          (__attribute__((address_space(3))) void *)(bbuf(b) + (32 * wave + 16 * k) * 4),
                                          16, 0, 0);
-      bs[b] = *reinterpret_cast<gu2_t *>(dsc + (soff + 8u * s));
     };
 
     f32x16_t acc[2];
@@ -1186,7 +1201,11 @@ __global__ void __launch_bounds__(kGmThreads, 4) down_gemm_kernel(FfnArgs a) {
         for (int t8 = 0; t8 < 8; ++t8) {
           const int p = t8 >> 1;
           const uint32_t w = brow[4 * (p ^ rsw) + 2 * (t8 & 1) + h];
-          const u32x4_t B = dequant_f16_pairs(w, bs[b].x, bs[b].y, p);
+          const auto sw01 = __builtin_amdgcn_permlane32_swap((s & 1) ? sreg.z : sreg.x, (s & 1) ? sreg.z : sreg.x,
+                                                             false, false);
+          const auto sw23 = __builtin_amdgcn_permlane32_swap((s & 1) ? sreg.w : sreg.y, (s & 1) ? sreg.w : sreg.y,
+                                                             false, false);
+          const u32x4_t B = dequant_f16_pairs(w, s < 2 ? sw01[0] : sw01[1], s < 2 ? sw23[0] : sw23[1], p);
           const int slot = (2 * t8 + h) ^ (c & 15);
           uint4 Av[MS];
 #pragma unroll
