@@ -7,7 +7,8 @@ resident in HBM.  Default workload: the 16-request decode batch through a
 stack of 40 distinct int4 layers with the residual epilogue between layers
 (16 tokens, H=2048, 256 experts, top-8, F=512 + a shared expert, Zipf(1.1)
 expert popularity; 18.3 GB of weights resident), the largest single-GPU
-workload.  The same line carries the 2048-token int4 prefill chunk as a
+workload, run as one moe_stack_forward call a step.  The same line carries
+the 2048-token int4 prefill chunk as a
 nested object ("prefill") with its own roofline against the matrix-core
 peak, and the same chunk in the W8A8 variant (int8 weights, int8
 activations: "prefill_w8a8") against the HBM peak.  Other primary workloads:
@@ -15,16 +16,18 @@ activations: "prefill_w8a8") against the HBM peak.  Other primary workloads:
 | tiny-int8 (decode workloads rotate over a ring of 40 layer instances so
 that no call finds its weights in the 256 MB last-level cache).  Each HBM
 roofline also carries the rate a plain device copy of the same traffic
-reaches in one launch (copy_ceiling_gbs).
+reaches in one launch (copy_ceiling_gbs) and the rate of a plain read-only
+launch of the same bytes (read_ceiling_gbs); the prefill roofline also
+carries the rate of a pure matrix-core kernel (mfma_achievable_tflops).
 
 Timing: W warm-up steps, then R repetitions (default 5) of K steps each,
 every repetition launched on one stream behind a bounded spin kernel long
 enough for the host to enqueue all K steps first (so the GPU runs them back
 to back), bracketed by synchronisation and HIP events; ms_per_step is the
 median repetition.  No profiling happens inside the timed repetitions.
-Afterwards a separate pass of a few steps asks the library (per-call
-options) for HIP events at the start and end of the gate/up and down
-kernels; the slower of the two is the dominant kernel, and its mean
+Afterwards a separate pass of a few steps (the stack as separate
+moe_layer_forward calls) asks the library (per-call options) for HIP events
+at the start and end of the gate/up and down kernels; the slower of the two is the dominant kernel, and its mean
 duration over that pass gives the roofline figure.  The CPU oracle is timed
 on a bounded sample of the same workload on the host cores.  Prints one JSON
 line.
@@ -223,6 +226,7 @@ class Workload:
         torch.cuda.synchronize()
         log(f"  inputs resident in {time.time() - t0:.1f} s")
         self.c_layers = [dl.c() for dl in self.layers]
+        self.c_stack = mb.stack_arrays(self.c_layers) if self.stack else None
         self.ws = mb.make_workspace(self.layers[0], self.T)
         self.y = torch.empty((self.T, self.H), dtype=torch.float32, device="cuda")
         if self.stack:
@@ -248,6 +252,12 @@ class Workload:
                              opts=opts)
 
     def step(self, i):
+        if self.stack:
+            # one moe_stack_forward call: the 40 layers chained by the
+            # residual stream, each layer's combine also forming the next
+            # layer's router product
+            self.mb.stack_forward(self.c_stack, self.x0, self.x0, self.r_buf, self.xin, self.y, self.ws)
+            return
         for l in range(self.calls_per_step):
             self.call(i, l)
 

@@ -267,6 +267,37 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
                          int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, const moe_forward_opts *opts,
                          void *stream);
 
+/* A stack of layers joined by the residual stream (the MoE steps of a
+ * batch of requests passing through the model's layers one after another:
+ * "Qwen3.6-35B-A3B: pictures, several requests at once and speed", Several
+ * requests at once; "qwen36: CUDA VRAM expert tier", Placement: 40 layers of
+ * 256 experts, top-8).  With x_0 = x_bf16 and r_0 = residual_in, for
+ * l = 0 .. n_layers - 1:
+ *   y = layer l applied to x_l (as moe_layer_forward),
+ *   r_(l+1) = bf16(r_l + y), x_(l+1) = bf16(RMSNorm(r_(l+1))),
+ * the residual epilogue of moe_residual with eps.  On return residual_out
+ * holds r_n, normed_out x_n and y the last layer's y; topk_ids / topk_w (or
+ * NULL) receive the last layer's routing.  Results are those of n_layers
+ * moe_layer_forward calls chained the same way, up to the summation order
+ * of the router products (each layer's combine also forms the next layer's
+ * router product, so the routing launch of every layer after the first is
+ * saved): selections agree except where two router logits are within
+ * float32 rounding of each other.
+ *
+ * layers: n_layers >= 1 host structs of one shape (hidden, experts, top-k,
+ * renorm, routed and shared formats and widths, shared gate present or
+ * not), each valid for moe_layer_forward.  x_bf16, residual_in,
+ * residual_out, normed_out: bf16 [T][H], 16-byte aligned; residual_in may
+ * equal residual_out and x_bf16 may equal normed_out (the stack updates
+ * them in place).  ws: moe_workspace_bytes(&layers[0], T) bytes as for
+ * moe_layer_forward (it also holds a second residual buffer).  Errors are
+ * those of moe_layer_forward, and MOE_ERR_INVALID_ARG for layers of
+ * different shapes or missing residual buffers; on an error partway the
+ * outputs hold an intermediate layer's state. */
+int moe_stack_forward(const moe_layer *layers, int32_t n_layers, const uint16_t *x_bf16, int32_t T,
+                      const uint16_t *residual_in, uint16_t *residual_out, uint16_t *normed_out, float eps, float *y,
+                      int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
 /* Bytes of the device array moe_layer_forward_noalloc uses as its
  * workspace (one array per GPU the library runs on). */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)

@@ -75,6 +75,8 @@ _SIGS = {
     "moe_layer_forward": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_layer_forward_ex": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _vp, _sz, _PO, _vp], ctypes.c_int),
     "moe_layer_forward_noalloc": ([_PL, _vp, _i32, _vp, _PR, _vp, _vp, _PO, _vp], ctypes.c_int),
+    "moe_stack_forward": ([_PL, _i32, _vp, _i32, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp],
+                          ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_calib_mfma": ([_i32, _i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double), _vp],
                        ctypes.c_int),
@@ -293,6 +295,23 @@ def layer_forward_noalloc(layer: Layer, x_bf16, y, res: MoeResidual | None = Non
     _check("moe_layer_forward_noalloc", _lib.moe_layer_forward_noalloc(
         ctypes.byref(c), _ptr(x_bf16), T, _ptr(y), ctypes.byref(res) if res is not None else None,
         _ptr(topk_ids), _ptr(topk_w), ctypes.byref(opts) if opts is not None else None, _stream(stream)))
+
+
+def stack_arrays(layers) -> ctypes.Array:
+    """A contiguous host array of the layers' C structs (for stack_forward)."""
+    arr = (MoeLayer * len(layers))()
+    for i, l in enumerate(layers):
+        arr[i] = l if isinstance(l, MoeLayer) else l.c()
+    return arr
+
+
+def stack_forward(c_layers, x_bf16, residual_in, residual_out, normed_out, y, ws, eps=1e-6, topk_ids=None,
+                  topk_w=None, stream=None):
+    """moe_stack_forward over a stack_arrays() array of layers."""
+    T = x_bf16.shape[0]
+    _check("moe_stack_forward", _lib.moe_stack_forward(
+        c_layers, len(c_layers), _ptr(x_bf16), T, _ptr(residual_in), _ptr(residual_out), _ptr(normed_out), eps,
+        _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def calib_mfma(kind: int, iters: int, stream=None):

@@ -114,6 +114,7 @@ struct LayerWs {
   int8_t *qx, *qa;  // W8A8: quantised x [T][H] and SwiGLU rows [rows][F]
   float *dx, *da;   // their per-row scales
   float *rpart;     // the router GEMM's partial sums
+  uint16_t *rstack;  // [T][H] bf16: the other residual buffer of a stack call
   size_t bytes;
 };
 
@@ -154,6 +155,7 @@ LayerWs carve_layer(const moe_layer *L, int32_t T, void *base) {
   // the router GEMM's partial sums of a prompt batch (either path may be
   // forced at run time, so sized for the GEMM whenever T allows it)
   w.rpart = c.take<float>(router_partial_floats(T, L->hidden, static_cast<int>(E), kPathPrefill));
+  w.rstack = c.take<uint16_t>(static_cast<size_t>(T) * L->hidden);
   w.bytes = align_up(c.off, 256);
   return w;
 }
@@ -369,9 +371,21 @@ int moe_combine(const float *rows_out, const int32_t *inv_pos, int32_t T, int32_
       launch_combine(combine_args(rows_out, inv_pos, T, K, H, shared_out, shared_gate, y, res), as_stream(stream)));
 }
 
-int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
-                         int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, const moe_forward_opts *opts,
-                         void *stream) {
+namespace {
+
+// How a layer call of moe_stack_forward links to its neighbours: its router
+// product is already in the workspace (written by the previous call's
+// combine), and/or its combine also forms the next layer's router product.
+struct StackLink {
+  bool route_ready = false;
+  const moe_layer *next = nullptr;
+  bool *fused = nullptr;  // set when the call did form the next layer's product
+};
+
+int layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
+                  int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, const moe_forward_opts *opts,
+                  void *stream, const StackLink &link) {
+  if (link.fused) *link.fused = false;
   int rc = check_layer(L);
   if (rc != MOE_OK) return rc;
   if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -470,9 +484,18 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
     fa.tail_skip = opts ? opts->tail_skip : 0;
     xa.route_here = (mfma_decode_ok(xa) && E <= 256) ? 1 : 0;
     if (xa.route_here) xa.units = w.units;  // published by the gate/up kernel's routing
-    xa.route = fa;
-    StageMark m(ev, MOE_STAGE_ROUTE, s);
-    e = xa.route_here ? launch_route_partial(fa, s) : launch_route_fused(fa, s);
+    if (xa.route_here && link.route_ready) {
+      // the previous layer's combine wrote this call's whole router product
+      // (one slice): the gate/up kernel's routing reads it as it is
+      fa.S = 1;
+      fa.Hs = H;
+      xa.route = fa;
+      e = hipSuccess;
+    } else {
+      xa.route = fa;
+      StageMark m(ev, MOE_STAGE_ROUTE, s);
+      e = xa.route_here ? launch_route_partial(fa, s) : launch_route_fused(fa, s);
+    }
   } else {
     // (prompt batches: tail-skip leaves them untouched)
     // (the router GEMM's slices are added by the top-k kernel, which then
@@ -546,7 +569,74 @@ int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, 
   CombineArgs ca = combine_args(w.rows_out, w.inv_pos, T, K, H, shared_rows, L->shared_gate_w ? w.gate : nullptr, y, res);
   ca.rows_f16 = xa.rows_f16;
   StageMark m(ev, MOE_STAGE_COMBINE, s);
+  // (the combine's blocks of one token all read the residual and one writes
+  // it, so the fused form needs distinct residual buffers)
+  if (link.next && xa.route_here && !xa.rows_f16 && res && res->normed_out && res->residual_in != res->residual_out &&
+      combine_route_ok(H)) {
+    // the next layer's router product, from the normalised row this
+    // combine forms, into the workspace's partial-logit area
+    const moe_layer *N = link.next;
+    CombineRouteArgs cr{ca, N->router_w, N->shared_gate_w, N->n_experts, router_rows(N), w.part};
+    e = launch_combine_route(cr, s);
+    if (e == hipSuccess && link.fused) *link.fused = true;
+    return hip_status(e);
+  }
   return hip_status(launch_combine(ca, s));
+}
+
+// Layers a stack call can chain: the shapes that decide the workspace carve
+// and the decode kernels' choice are equal.
+bool same_shape(const moe_layer *a, const moe_layer *b) {
+  auto ex_eq = [](const moe_experts &p, const moe_experts &q) {
+    return p.n_experts == q.n_experts && p.fmt == q.fmt && p.ffn == q.ffn;
+  };
+  return a->hidden == b->hidden && a->n_experts == b->n_experts && a->top_k == b->top_k && a->renorm == b->renorm &&
+         ex_eq(a->routed, b->routed) && ex_eq(a->shared, b->shared) &&
+         (a->shared_gate_w != nullptr) == (b->shared_gate_w != nullptr);
+}
+
+}  // namespace
+
+int moe_layer_forward_ex(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,
+                         int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, const moe_forward_opts *opts,
+                         void *stream) {
+  return layer_forward(L, x_bf16, T, y, res, topk_ids, topk_w, ws, ws_bytes, opts, stream, StackLink{});
+}
+
+int moe_stack_forward(const moe_layer *layers, int32_t n_layers, const uint16_t *x_bf16, int32_t T,
+                      const uint16_t *residual_in, uint16_t *residual_out, uint16_t *normed_out, float eps, float *y,
+                      int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  if (!layers || n_layers <= 0 || T < 0) return MOE_ERR_INVALID_ARG;
+  if (!residual_in || !residual_out || !normed_out || !(eps >= 0.f)) return MOE_ERR_INVALID_ARG;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const int rc = check_layer(&layers[l]);
+    if (rc != MOE_OK) return rc;
+    if (l > 0 && !same_shape(&layers[0], &layers[l])) return MOE_ERR_INVALID_ARG;
+  }
+  if (T == 0) return MOE_OK;
+  // every call checks the workspace, the buffers and their alignment itself
+  if (!ws || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  const LayerWs w = carve_layer(&layers[0], T, ws);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  // residual buffers: layer l reads R_l and writes R_(l+1), R_0 = residual_in,
+  // R_n = residual_out, and the others alternate between residual_out and
+  // the workspace's copy so that a layer reads and writes different ones
+  auto rbuf = [&](int32_t l) -> uint16_t * { return (n_layers - l) % 2 == 0 ? residual_out : w.rstack; };
+  bool ready = false;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    moe_residual res{l == 0 ? residual_in : rbuf(l), rbuf(l + 1), normed_out, eps, 0};
+    const bool last = l + 1 == n_layers;
+    bool fused = false;
+    StackLink link;
+    link.route_ready = ready;
+    link.next = last ? nullptr : &layers[l + 1];
+    link.fused = &fused;
+    const int rc = layer_forward(&layers[l], l == 0 ? x_bf16 : normed_out, T, y, &res, last ? topk_ids : nullptr,
+                                 last ? topk_w : nullptr, ws, ws_bytes, nullptr, stream, link);
+    if (rc != MOE_OK) return rc;
+    ready = fused;
+  }
+  return MOE_OK;
 }
 
 int moe_layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *y, const moe_residual *res,

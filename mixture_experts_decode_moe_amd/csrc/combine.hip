@@ -37,94 +37,220 @@ MOE_DEV float4 row4(const float *rows, size_t row, int H, int c) {
   }
 }
 
-// One block per token row.  With K <= kCombineSlots every row of a chunk is
-// requested at once (the slot rows are block-uniform, read through the
-// scalar cache), then added in slot order.  F16: the rows (and the shared
-// expert's) are fp16.
+// Chunk c (four elements) of token t's row: the routed rows in slot order
+// (with K <= kCombineSlots every row is requested at once; the slot rows are
+// block-uniform, read through the scalar cache), then the shared expert's
+// row (scaled by its gate).  combine_load issues the chunk's loads;
+// combine_finish writes y and, with residual_out, the residual sum
+// r' = bf16(r + y), whose fp32 values go to r4 and squares into sq; `store`
+// false computes without writing (the combine + router kernel's other
+// blocks).  Split so that a caller can issue other loads between the two.
+struct CombineLoads {
+  float4 v[kCombineSlots];  // the slot rows (K <= kCombineSlots)
+  float4 sv;                // the shared expert's row
+  uint2 xv;                 // the residual
+};
+
+template <bool F16>
+MOE_DEV void combine_load(const CombineArgs &a, int t, int c, CombineLoads &L) {
+  const int n4 = a.H / 4;
+  const int K = a.K;
+  const int32_t *inv = a.inv_pos + static_cast<size_t>(t) * K;
+  const size_t o4 = static_cast<size_t>(t) * n4 + c;
+  if (K <= kCombineSlots) {
+#pragma unroll
+    for (int k = 0; k < kCombineSlots; ++k) {
+      const int row = k < K ? inv[k] : -1;
+      const float4 x = row4<F16>(a.rows_out, static_cast<size_t>(row < 0 ? 0 : row), a.H, c);
+      L.v[k] = row >= 0 ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  L.sv = a.shared_out ? row4<F16>(a.shared_out, static_cast<size_t>(t), a.H, c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  L.xv = a.residual_out ? reinterpret_cast<const uint2 *>(a.residual_in)[o4] : make_uint2(0u, 0u);
+}
+
+template <bool F16>
+MOE_DEV void combine_finish(const CombineArgs &a, int t, int c, const CombineLoads &L, bool store, float4 &r4,
+                            float &sq) {
+  const int n4 = a.H / 4;
+  const int K = a.K;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (K <= kCombineSlots) {
+#pragma unroll
+    for (int k = 0; k < kCombineSlots; ++k)
+      if (k < K) add4(acc, L.v[k]);
+  } else {
+    const int32_t *inv = a.inv_pos + static_cast<size_t>(t) * K;
+    for (int k = 0; k < K; ++k) {
+      const int row = inv[k];
+      if (row >= 0) add4(acc, row4<F16>(a.rows_out, static_cast<size_t>(row), a.H, c));
+    }
+  }
+  const size_t o4 = static_cast<size_t>(t) * n4 + c;
+  if (a.shared_out) {
+    if (a.shared_gate) {
+      // the shared expert's row scaled by its gate, fused into the sum
+      const float g = a.shared_gate[t];
+      acc.x = fmaf(g, L.sv.x, acc.x);
+      acc.y = fmaf(g, L.sv.y, acc.y);
+      acc.z = fmaf(g, L.sv.z, acc.z);
+      acc.w = fmaf(g, L.sv.w, acc.w);
+    } else {
+      add4(acc, L.sv);
+    }
+  }
+  if (store) reinterpret_cast<float4 *>(a.y)[o4] = acc;
+  if (a.residual_out) {
+    const uint16_t b0 = f32_to_bf16_rne(bf16_lo(L.xv.x) + acc.x);
+    const uint16_t b1 = f32_to_bf16_rne(bf16_hi(L.xv.x) + acc.y);
+    const uint16_t b2 = f32_to_bf16_rne(bf16_lo(L.xv.y) + acc.z);
+    const uint16_t b3 = f32_to_bf16_rne(bf16_hi(L.xv.y) + acc.w);
+    if (store)
+      reinterpret_cast<uint2 *>(a.residual_out)[o4] =
+          make_uint2(static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16),
+                     static_cast<uint32_t>(b2) | (static_cast<uint32_t>(b3) << 16));
+    r4 = make_float4(bf16_to_f32(b0), bf16_to_f32(b1), bf16_to_f32(b2), bf16_to_f32(b3));
+    sq = fmaf(r4.x, r4.x, sq);
+    sq = fmaf(r4.y, r4.y, sq);
+    sq = fmaf(r4.z, r4.z, sq);
+    sq = fmaf(r4.w, r4.w, sq);
+  }
+}
+
+// 1 / sqrt(mean(r'^2) + eps) of the block's row: wave sums, then the waves
+// in order (every thread of the block calls it).
+MOE_DEV float row_inv_rms(float sq, float *wave_sq, int H, float eps) {
+  sq = sum64(sq);
+  if ((threadIdx.x & 63) == 0) wave_sq[threadIdx.x >> 6] = sq;
+  lds_barrier();
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) total += wave_sq[w];
+  return 1.f / sqrtf(total / static_cast<float>(H) + eps);
+}
+
+// bf16(r' * inv_rms) of four elements, packed.
+MOE_DEV uint2 normed4(const float4 &r, float inv_rms) {
+  const uint16_t b0 = f32_to_bf16_rne(r.x * inv_rms);
+  const uint16_t b1 = f32_to_bf16_rne(r.y * inv_rms);
+  const uint16_t b2 = f32_to_bf16_rne(r.z * inv_rms);
+  const uint16_t b3 = f32_to_bf16_rne(r.w * inv_rms);
+  return make_uint2(static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16),
+                    static_cast<uint32_t>(b2) | (static_cast<uint32_t>(b3) << 16));
+}
+
+// One block per token row.  F16: the rows (and the shared expert's) are fp16.
 template <bool F16>
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
   __shared__ float wave_sq[kCombineThreads / 64];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int n4 = a.H / 4;
-  const int K = a.K;
-  const int32_t *inv = a.inv_pos + static_cast<size_t>(t) * K;
   float4 r[kCombineChunks];
   float sq = 0.f;
 #pragma unroll
   for (int i = 0; i < kCombineChunks; ++i) {
     const int c = tid + kCombineThreads * i;
     if (c >= n4) break;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (K <= kCombineSlots) {
-      float4 v[kCombineSlots];
-#pragma unroll
-      for (int k = 0; k < kCombineSlots; ++k) {
-        const int row = k < K ? inv[k] : -1;
-        const float4 x = row4<F16>(a.rows_out, static_cast<size_t>(row < 0 ? 0 : row), a.H, c);
-        v[k] = row >= 0 ? x : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int k = 0; k < kCombineSlots; ++k)
-        if (k < K) add4(acc, v[k]);
-    } else {
-      for (int k = 0; k < K; ++k) {
-        const int row = inv[k];
-        if (row >= 0) add4(acc, row4<F16>(a.rows_out, static_cast<size_t>(row), a.H, c));
-      }
-    }
-    const size_t o4 = static_cast<size_t>(t) * n4 + c;
-    if (a.shared_out) {
-      const float4 sv = row4<F16>(a.shared_out, static_cast<size_t>(t), a.H, c);
-      if (a.shared_gate) {
-        // the shared expert's row scaled by its gate, fused into the sum
-        const float g = a.shared_gate[t];
-        acc.x = fmaf(g, sv.x, acc.x);
-        acc.y = fmaf(g, sv.y, acc.y);
-        acc.z = fmaf(g, sv.z, acc.z);
-        acc.w = fmaf(g, sv.w, acc.w);
-      } else {
-        add4(acc, sv);
-      }
-    }
-    reinterpret_cast<float4 *>(a.y)[o4] = acc;
-    if (a.residual_out) {
-      const uint2 xv = reinterpret_cast<const uint2 *>(a.residual_in)[o4];
-      const uint16_t b0 = f32_to_bf16_rne(bf16_lo(xv.x) + acc.x);
-      const uint16_t b1 = f32_to_bf16_rne(bf16_hi(xv.x) + acc.y);
-      const uint16_t b2 = f32_to_bf16_rne(bf16_lo(xv.y) + acc.z);
-      const uint16_t b3 = f32_to_bf16_rne(bf16_hi(xv.y) + acc.w);
-      reinterpret_cast<uint2 *>(a.residual_out)[o4] =
-          make_uint2(static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16),
-                     static_cast<uint32_t>(b2) | (static_cast<uint32_t>(b3) << 16));
-      r[i] = make_float4(bf16_to_f32(b0), bf16_to_f32(b1), bf16_to_f32(b2), bf16_to_f32(b3));
-      sq = fmaf(r[i].x, r[i].x, sq);
-      sq = fmaf(r[i].y, r[i].y, sq);
-      sq = fmaf(r[i].z, r[i].z, sq);
-      sq = fmaf(r[i].w, r[i].w, sq);
-    }
+    CombineLoads L;
+    combine_load<F16>(a, t, c, L);
+    combine_finish<F16>(a, t, c, L, true, r[i], sq);
   }
   if (!a.normed_out) return;
-  sq = sum64(sq);
-  if ((tid & 63) == 0) wave_sq[tid >> 6] = sq;
-  lds_barrier();
-  float total = 0.f;
-#pragma unroll
-  for (int w = 0; w < kCombineThreads / 64; ++w) total += wave_sq[w];
-  const float inv_rms = 1.f / sqrtf(total / static_cast<float>(a.H) + a.eps);
+  const float inv_rms = row_inv_rms(sq, wave_sq, a.H, a.eps);
 #pragma unroll
   for (int i = 0; i < kCombineChunks; ++i) {
     const int c = tid + kCombineThreads * i;
     if (c >= n4) break;
-    const size_t o4 = static_cast<size_t>(t) * n4 + c;
-    const uint16_t b0 = f32_to_bf16_rne(r[i].x * inv_rms);
-    const uint16_t b1 = f32_to_bf16_rne(r[i].y * inv_rms);
-    const uint16_t b2 = f32_to_bf16_rne(r[i].z * inv_rms);
-    const uint16_t b3 = f32_to_bf16_rne(r[i].w * inv_rms);
-    reinterpret_cast<uint2 *>(a.normed_out)[o4] =
-        make_uint2(static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16),
-                   static_cast<uint32_t>(b2) | (static_cast<uint32_t>(b3) << 16));
+    reinterpret_cast<uint2 *>(a.normed_out)[static_cast<size_t>(t) * n4 + c] = normed4(r[i], inv_rms);
   }
+}
+
+// The last step of a stack layer fused with the first of the next: block
+// (t, g) forms token t's combine, residual sum and normalised row exactly as
+// combine_kernel does (group 0 writes them), then multiplies the normalised
+// row by rows 16 g .. 16 g + 15 of the next layer's router product (the
+// router rows, then the shared gate row as row E) and writes those products
+// for the next layer's routing.  Each thread holds four columns (H <= 2048).
+// The expert rows are requested first and the router rows after them, so
+// the combine waits only for its own loads while the router rows arrive.
+// A product is summed over a thread's four columns in order, then over the
+// wave by a transposed reduction (lane halves exchange half of the sixteen
+// sums, then 16-lane rows exchange half of the rest, then each 16-lane row
+// adds its four sums), then over the waves in order.
+constexpr int kCrRows = 16;
+
+__global__ void __launch_bounds__(kCombineThreads) combine_route_kernel(CombineRouteArgs a) {
+  __shared__ float wave_sq[kCombineThreads / 64];
+  __shared__ float wave_dot[kCombineThreads / 64][kCrRows];
+  const int t = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const CombineArgs &c = a.c;
+  const int n4 = c.H / 4;
+  const bool mine = tid < n4;
+  const int col = mine ? tid : 0;
+  CombineLoads L;
+  combine_load<false>(c, t, col, L);
+  float4 wv[kCrRows];
+#pragma unroll
+  for (int j = 0; j < kCrRows; ++j) {
+    const int row = g * kCrRows + j;
+    const float *wr = row < a.E ? a.router_w + static_cast<size_t>(row) * c.H : a.gate_w;
+    wv[j] = (mine && row < a.Ep) ? reinterpret_cast<const float4 *>(wr)[col] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float4 r4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float sq = 0.f;
+  if (mine) combine_finish<false>(c, t, col, L, g == 0, r4, sq);
+  const float inv_rms = row_inv_rms(sq, wave_sq, c.H, c.eps);
+  const uint2 nv = normed4(r4, inv_rms);
+  if (mine && g == 0) reinterpret_cast<uint2 *>(c.normed_out)[static_cast<size_t>(t) * n4 + col] = nv;
+  const float x0 = bf16_lo(nv.x), x1 = bf16_hi(nv.x), x2 = bf16_lo(nv.y), x3 = bf16_hi(nv.y);
+  float d[kCrRows];
+#pragma unroll
+  for (int j = 0; j < kCrRows; ++j) {
+    float v = wv[j].x * x0;
+    v = fmaf(wv[j].y, x1, v);
+    v = fmaf(wv[j].z, x2, v);
+    v = fmaf(wv[j].w, x3, v);
+    d[j] = mine ? v : 0.f;
+  }
+  // lane halves: afterwards d[j] (j < 8) is row j + 8 (lane / 32) over lanes l, l ^ 32
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(d[j]), __float_as_uint(d[8 + j]), false, false);
+    d[j] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  // 16-lane rows: d[j] (j < 4) is row j + 4 ((lane / 16) % 2) + 8 (lane / 32) over four lanes
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[j]), __float_as_uint(d[4 + j]), false, false);
+    d[j] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) d[j] = sum16(d[j]);
+  if ((lane & 15) == 0) {
+    const int r0 = 4 * ((lane >> 4) & 1) + 8 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wave_dot[wave][r0 + j] = d[j];
+  }
+  lds_barrier();
+  if (tid < kCrRows) {
+    const int row = g * kCrRows + tid;
+    float total = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCombineThreads / 64; ++w) total += wave_dot[w][tid];
+    if (row < a.Ep) a.logits[static_cast<size_t>(t) * a.Ep + row] = total;
+  }
+}
+
+bool combine_route_ok(int H) { return H % 256 == 0 && H / 4 <= kCombineThreads; }
+
+hipError_t launch_combine_route(const CombineRouteArgs &a, hipStream_t s) {
+  if (a.c.T == 0) return hipSuccess;
+  if (!combine_route_ok(a.c.H) || !a.c.normed_out || !a.c.residual_out) return hipErrorInvalidValue;
+  const dim3 grid(a.c.T, (a.Ep + kCrRows - 1) / kCrRows);
+  combine_route_kernel<<<grid, kCombineThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {

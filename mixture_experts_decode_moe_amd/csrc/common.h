@@ -239,6 +239,18 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
+// A stack layer's combine (with the residual sum and the normalised row)
+// fused with the next layer's router product.
+struct CombineRouteArgs {
+  CombineArgs c;          // residual_out and normed_out required; fp32 rows
+  const float *router_w;  // the next layer's router [E][H]
+  const float *gate_w;    // its shared gate row [H], or NULL
+  int32_t E, Ep;          // its experts; Ep = E (+ 1 with the gate row)
+  float *logits;          // [T][Ep]: the next layer's router products (no bias)
+};
+bool combine_route_ok(int H);
+hipError_t launch_combine_route(const CombineRouteArgs &a, hipStream_t s);
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
 // Launches a kernel; with profiling events (a caller's per-call request)

@@ -122,6 +122,27 @@ def test_other_entry_points_reject_bad_arguments(mb):
     assert lib.moe_workspace_init(None, 0, None) == -3
 
 
+def test_stack_forward_rejects_bad_arguments(mb):
+    """moe_stack_forward checks its layers, buffers and workspace before
+    launching anything."""
+    lib = mb.raw_lib()
+    p = ctypes.c_void_p(1 << 20)
+    arr = (mb.MoeLayer * 2)(_fake_layer(mb), _fake_layer(mb))
+    f = lib.moe_stack_forward
+    assert f(None, 2, p, 4, p, p, p, 1e-6, p, None, None, p, 1 << 30, None) == -1
+    assert f(arr, 0, p, 4, p, p, p, 1e-6, p, None, None, p, 1 << 30, None) == -1
+    assert f(arr, 2, p, 4, None, p, p, 1e-6, p, None, None, p, 1 << 30, None) == -1  # no residual_in
+    assert f(arr, 2, p, 4, p, p, None, 1e-6, p, None, None, p, 1 << 30, None) == -1  # no normed_out
+    assert f(arr, 2, p, 4, p, p, p, -1.0, p, None, None, p, 1 << 30, None) == -1  # eps < 0
+    assert f(arr, 2, p, 0, p, p, p, 1e-6, p, None, None, p, 1 << 30, None) == 0  # no tokens: nothing to do
+    assert f(arr, 2, p, 4, p, p, p, 1e-6, p, None, None, None, 0, None) == -3  # no workspace
+    assert f(arr, 2, p, 4, p, p, p, 1e-6, p, None, None, p, 16, None) == -3  # too small
+    other = _fake_layer(mb)
+    other.top_k = 4
+    arr2 = (mb.MoeLayer * 2)(_fake_layer(mb), other)
+    assert f(arr2, 2, p, 4, p, p, p, 1e-6, p, None, None, p, 1 << 30, None) == -1  # shapes differ
+
+
 def test_calibration_helpers_reject_bad_arguments(mb):
     """The measurement helpers check their arguments before touching a
     device."""
