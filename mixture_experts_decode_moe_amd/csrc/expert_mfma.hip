@@ -182,7 +182,7 @@ MOE_DEV GuLane gu_lane(const GuPtrs &P, int wave, int n, int g) {
 // f0 are wave-uniform.  Row f0 + n7 of the gate or up matrix: JW 16-byte
 // chunks at w_off + 64 jj, and the chunks' block scales (int4) or the row
 // scale (int8).
-template <int FMT, int JW>
+template <int FMT, int JW, bool SCALES = true>
 MOE_DEV void gu_load(const FfnArgs &a, const GuLane &L, int e, int f0, GuWeights<FMT, JW> &w) {
   using Fm = MfmaFmt<FMT>;
   const bool shared = e < 0;
@@ -194,7 +194,9 @@ MOE_DEV void gu_load(const FfnArgs &a, const GuLane &L, int e, int f0, GuWeights
   const uint32_t woff = row * (nblk * 16u) + L.w_off;
 #pragma unroll
   for (int jj = 0; jj < JW; ++jj) w.w[jj] = load_stream16_g(q + (woff + 64u * jj));
-  if constexpr (FMT == MOE_W_INT4_B32) {
+  if constexpr (FMT == MOE_W_INT4_B32 && !SCALES) {
+    w.rs = 1.f;  // the block scales come from LDS (gateup_mfma_kernel with SCL)
+  } else if constexpr (FMT == MOE_W_INT4_B32) {
     // the four fp16 scales of each chunk: 8 bytes at 8 (wave JW + jj)
     const uint32_t soff = row * (nblk * 2u) + (L.w_off & ~63u) / 8u;
 #pragma unroll
@@ -231,7 +233,14 @@ MOE_DEV void gu_item(const FfnArgs &a, int i, int tiles_r, int tiles_s, int &e, 
   }
 }
 
-template <int FMT, int JW, int NI>
+// SCL: the scales of a chunk's items are staged in LDS by direct loads,
+// instead of every wave requesting a few bytes of each of its items' 16
+// scale rows (which doubled the requests of the weight stream for an eighth
+// of its bytes).  int4 only (H = 2048, 16 waves, 8 items a chunk): wave w
+// loads the 128-byte block-scale rows of the gate or up half of item w / 2.
+// (The int8 row scales, one float a row, staged the same way by one wave
+// made that kernel slower: they are a sixty-fourth of its bytes.)
+template <int FMT, int JW, int NI, bool SCL>
 __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   using Fm = MfmaFmt<FMT>;
   using Vec = typename Fm::Vec;
@@ -241,6 +250,10 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) int tab[kGuTable][4];  // e, r0, n (<= 16), f0
   __shared__ int toks[kGuTable][16];
   __shared__ uint32_t act_st[NI][16][8];  // SwiGLU outputs of a chunk: bf16 hi | lo << 16
+  // SCL: item i's 16 scale rows of 8 pieces (16 bytes, 8 blocks each), the
+  // piece p of row r at slot p ^ (r & 7)
+  __shared__ uint4 sc_lds[SCL ? NI * 128 : 1];
+  static_assert(!SCL || (kInt4 && JW == 1 && NI == 8), "SCL: int4, H = 2048, 8 items a chunk");
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -407,9 +420,34 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
       te[i] = rec.x;
       tf[i] = rec.w;
     }
+    if constexpr (SCL) {
+      // wave w: scale rows 8 (w & 1) .. + 7 (gate: 0-7, up: 8-15) of item w / 2
+      // of the chunk, one 1 KB direct load; lane l row l / 8, piece
+      // (l % 8) ^ (row % 8) into slot l % 8
+      const int hi = wave >> 1, half = wave & 1;
+      const int it = c0 + hi < my_items ? c0 + hi : c0;
+      const int e = __builtin_amdgcn_readfirstlane(tab[it][0]);
+      const int f0 = __builtin_amdgcn_readfirstlane(tab[it][3]);
+      const bool shared = e < 0;
+      const uint32_t F = static_cast<uint32_t>(shared ? a.Fs : a.F);
+      const int r = lane >> 3;
+      const uint32_t row = (shared ? 0u : static_cast<uint32_t>(e)) * F + static_cast<uint32_t>(f0) + r;
+      gchar_t *sb = half ? (shared ? uniform_gptr(a.sus) : uniform_gptr(a.us))
+                         : (shared ? uniform_gptr(a.sgs) : uniform_gptr(a.gs));
+      __builtin_amdgcn_global_load_lds(sb + (row * 128u + 16u * static_cast<uint32_t>((lane & 7) ^ (r & 7))),
+                                       (__attribute__((address_space(3))) void *)(sc_lds + hi * 128 + half * 64),
+                                       16, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      gu_load<FMT, JW>(a, GL, __builtin_amdgcn_readfirstlane(te[i]), __builtin_amdgcn_readfirstlane(tf[i]), w[i]);
+      gu_load<FMT, JW, !SCL>(a, GL, __builtin_amdgcn_readfirstlane(te[i]), __builtin_amdgcn_readfirstlane(tf[i]),
+                             w[i]);
+    if constexpr (SCL) {
+      // a wave's scale load is older than its NI JW weight loads; once every
+      // wave's has landed the chunk's scales are in LDS
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI * JW));
+      lds_barrier();
+    }
     // groups of kGuGroup items: every wave's partial tiles of the group go to
     // LDS, then one pass adds them and applies SwiGLU (two barriers a group)
 #pragma unroll
@@ -422,6 +460,17 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
           const int nrows = tab[it][2];
 #pragma unroll
           for (int jj = 0; jj < JW; ++jj) xpose4(w[i].w[jj]);
+          if constexpr (SCL) {
+            // the scales of blocks 4 q .. 4 q + 3 of row n: half q % 2 of piece q / 2
+#pragma unroll
+            for (int jj = 0; jj < JW; ++jj) {
+              const int q = wave * JW + jj;
+              const uint2 sv =
+                  reinterpret_cast<const uint2 *>(sc_lds + i * 128 + n * 8 + ((q >> 1) ^ (n & 7)))[q & 1];
+              w[i].s[jj][0] = sv.x;
+              w[i].s[jj][1] = sv.y;
+            }
+          }
           const bool mv = n < nrows;
           const uint16_t *xrow = reinterpret_cast<const uint16_t *>(xs_lds + toks[it][n] * xstride);
           f32x4_t acc = zero4;
@@ -681,7 +730,7 @@ static hipError_t launch_gateup_mfma_t(const FfnArgs &a, int ks, hipStream_t s) 
   constexpr int D = FMT == MOE_W_INT4_B32 ? (JW == 1 ? 8 : 4) : (JW == 1 ? 8 : 4);
   const size_t lds = static_cast<size_t>(a.T) * (a.H / 8 + 1) * 16;
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_mfma_kernel<FMT, JW, D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_mfma_kernel<FMT, JW, D, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
@@ -691,7 +740,17 @@ static hipError_t launch_gateup_mfma_t(const FfnArgs &a, int ks, hipStream_t s) 
   const int cus = cu_count();
   int grid = (items + kGuTable - 1) / kGuTable;
   if (grid < cus) grid = items < cus ? (items < 1 ? 1 : items) : cus;
-  return launch_kernel(gateup_mfma_kernel<FMT, JW, D>, dim3(grid), dim3(64 * ks), lds, s, a.ev, a);
+  if constexpr (FMT == MOE_W_INT4_B32 && JW == 1 && D == 8) {
+    if (a.H == 2048 && ks == 16) {
+      if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_mfma_kernel<FMT, JW, D, true>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+      }
+      return launch_kernel(gateup_mfma_kernel<FMT, JW, D, true>, dim3(grid), dim3(64 * ks), lds, s, a.ev, a);
+    }
+  }
+  return launch_kernel(gateup_mfma_kernel<FMT, JW, D, false>, dim3(grid), dim3(64 * ks), lds, s, a.ev, a);
 }
 
 template <int FMT>
