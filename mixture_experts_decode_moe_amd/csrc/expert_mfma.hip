@@ -408,6 +408,12 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
   // chunk's first item, already in flight), so the wait before each item
   // leaves the later items' loads in flight.
   const GuLane GL = gu_lane<FMT, JW>(gu_ptrs(a), wave, n, g);
+  // the unit of the last item multiplied, its x row pointer and correction
+  // products (wave-uniform unit; kept across chunks)
+  constexpr bool kKeepCorr = kInt4 && JW == 1;
+  int run_e = -2;  // no unit (-1 is the shared expert)
+  const uint16_t *xrow = nullptr;
+  f32x4_t run_corr[kKeepCorr ? 4 : 1];
   for (int c0 = 0; c0 < my_items; c0 += NI) {
     GuWeights<FMT, JW> w[NI];
     // the chunk's item records first (one LDS read each, all in flight
@@ -457,7 +463,6 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
         const int i = g0 + j;
         const int it = c0 + i;
         if (i < NI && it < my_items) {
-          const int nrows = tab[it][2];
 #pragma unroll
           for (int jj = 0; jj < JW; ++jj) xpose4(w[i].w[jj]);
           if constexpr (SCL) {
@@ -471,18 +476,30 @@ __global__ void __launch_bounds__(1024) gateup_mfma_kernel(FfnArgs a) {
               w[i].s[jj][1] = sv.y;
             }
           }
-          const bool mv = n < nrows;
-          const uint16_t *xrow = reinterpret_cast<const uint16_t *>(xs_lds + toks[it][n] * xstride);
+          // Slots m >= nrows read token 0's row (a finite operand): their
+          // output rows are never read, and MFMA rows do not mix.  Items of
+          // one unit share their token rows, so the row pointer and (int4,
+          // one block-quad a wave) the correction products are formed once
+          // per run of items of the same unit.
+          const int e_i = __builtin_amdgcn_readfirstlane(te[i]);
+          if (e_i != run_e) {
+            run_e = e_i;
+            xrow = reinterpret_cast<const uint16_t *>(xs_lds + toks[it][n] * xstride);
+            if constexpr (kKeepCorr) {
+#pragma unroll
+              for (int p = 0; p < 4; ++p) run_corr[p] = Fm::mfma(Fm::a_plane(xrow, 4 * wave + p, g), cvec, zero4);
+            }
+          }
           f32x4_t acc = zero4;
 #pragma unroll
           for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
               // staged x is already in operand order
-              const Vec xa = mv ? Fm::a_plane(xrow, 4 * (wave * JW + jj) + p, g) : Fm::zero();
+              const Vec xa = Fm::a_plane(xrow, 4 * (wave * JW + jj) + p, g);
               if constexpr (kInt4) {
                 // per block: -136 * sum(x) as the accumulator input, then the scale
-                const f32x4_t c0v = Fm::mfma(xa, cvec, zero4);
+                const f32x4_t c0v = kKeepCorr ? run_corr[p] : Fm::mfma(xa, cvec, zero4);
                 const f32x4_t c = Fm::mfma(xa, Fm::b_w(word(w[i].w[jj], p)), c0v);
                 acc = fma4(scale4(w[i].s[jj][0], w[i].s[jj][1], p), c, acc);
               } else {
