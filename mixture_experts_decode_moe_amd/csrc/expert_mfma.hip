@@ -58,10 +58,10 @@ struct MUnit {
   bool shared;
 };
 
-// rec: the unit's (expert, first row, rows) record from the routing's unit
-// table, when the caller has read it already (nullptr: look it up)
-MOE_DEV bool mfma_unit(const FfnArgs &a, int item, int tiles_r, int tiles_s, int U, MUnit &u,
-                       const int4 *rec = nullptr) {
+// rec (with use_rec): the unit's (expert, first row, rows) record from the
+// routing's unit table, read by the caller already; else it is looked up
+MOE_DEV bool mfma_unit(const FfnArgs &a, int item, int tiles_r, int tiles_s, int U, MUnit &u, bool use_rec,
+                       int4 rec) {
   if (item < tiles_s) {
     u.shared = true;
     u.gq = a.sgq;
@@ -89,10 +89,10 @@ MOE_DEV bool mfma_unit(const FfnArgs &a, int item, int tiles_r, int tiles_s, int
   u.ds = a.ds;
   u.F = a.F;
   u.tile = i - k * tiles_r;
-  if (rec) {
-    u.e = rec->x;
-    u.r0 = rec->y;
-    u.n = rec->z;
+  if (use_rec) {
+    u.e = rec.x;
+    u.r0 = rec.y;
+    u.n = rec.z;
   } else if (a.offsets) {
     u.e = a.active[k];
     u.r0 = a.offsets[u.e];
@@ -591,7 +591,7 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
       rec = reinterpret_cast<const int4 *>(a.units)[min((item - tiles_s) / tiles, a.max_units - 1)];
     else
       rec = rec0;
-    if (!mfma_unit(a, item, tiles, tiles_s, U, u, a.units ? &rec : nullptr) || u.n <= 0) continue;
+    if (!mfma_unit(a, item, tiles, tiles_s, U, u, a.units != nullptr, rec) || u.n <= 0) continue;
     const int h0 = u.tile * 64;
     const int F = u.F;
     const int nblk = F / Fm::kBlockK;
@@ -618,28 +618,53 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
     // activation rows of the first 16 rows, requested before the weights are
     // waited for
     Vec ah[JW][4], al[JW][4];
+    // rows m >= u.n read the unit's first row: their output rows are never
+    // stored, and MFMA rows do not mix
     auto load_a = [&](int m0) {
       const int m = m0 + n;
-      const bool mv = m < u.n;
-      const uint16_t *hp = reinterpret_cast<const uint16_t *>(a.act + mrow_act(a, u, u.r0 + (mv ? m : 0)));
+      const uint16_t *hp = reinterpret_cast<const uint16_t *>(a.act + mrow_act(a, u, u.r0 + (m < u.n ? m : 0)));
       const uint16_t *lp = hp + F;  // lo plane follows the hi plane
 #pragma unroll
       for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int b = 4 * (wave * JW + jj) + p;
-          ah[jj][p] = mv ? Fm::a_plane(hp, b, g) : Fm::zero();
-          al[jj][p] = mv ? Fm::a_plane(lp, b, g) : Fm::zero();
+          ah[jj][p] = Fm::a_plane(hp, b, g);
+          al[jj][p] = Fm::a_plane(lp, b, g);
         }
     };
+    // the routing weights of the rows this lane stores (rows m0 + 4 g + i),
+    // requested with the act rows rather than after the products
+    float rw[4];
+    auto load_rw = [&](int m0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mm = min(m0 + 4 * g + i, u.n - 1);
+        rw[i] = u.shared || !a.row_w ? 1.f : a.row_w[u.r0 + mm];
+      }
+    };
     load_a(0);
+    load_rw(0);
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) xpose4(wd[jj][nt]);
 
     for (int m0 = 0; m0 < u.n; m0 += 16) {
-      if (m0 > 0) load_a(m0);
+      if (m0 > 0) {
+        load_a(m0);
+        load_rw(m0);
+      }
+      // the weight words are converted inside the loop (a unit rarely has
+      // more than 16 rows; hoisting the conversions would keep sixty-four
+      // more registers live and cut the blocks a compute unit holds)
+#pragma unroll
+      for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          asm volatile("" : "+v"(wd[jj][nt].x), "+v"(wd[jj][nt].y), "+v"(wd[jj][nt].z), "+v"(wd[jj][nt].w));
+          if constexpr (kInt4) asm volatile("" : "+v"(sd[jj][nt][0]), "+v"(sd[jj][nt][1]));
+        }
       f32x4_t acc[4] = {zero4, zero4, zero4, zero4};
 #pragma unroll
       for (int jj = 0; jj < JW; ++jj)
@@ -681,9 +706,8 @@ __global__ void __launch_bounds__(512) down_mfma_kernel(FfnArgs a) {
           const int mm = m0 + 4 * g + i;
           if (mm < u.n) {
             const int r = u.r0 + mm;
-            const float w = u.shared || !a.row_w ? 1.f : a.row_w[r];
             const int orow = u.shared ? a.n_rows + r : r;
-            a.rows_out[static_cast<size_t>(orow) * H + h] = v[i] * w;
+            a.rows_out[static_cast<size_t>(orow) * H + h] = v[i] * rw[i];
           }
         }
       }
