@@ -421,7 +421,19 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
     float acc[NPL];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 4) {
+    if (S == 1) {
+      // whole logits (the previous launch formed them): one request each
+      float pv[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) pv[j] = part[static_cast<size_t>(t) * Ep + min(lane + 64 * j, E - 1)];
+      if (!staged) {
+        stage();
+        staged = true;
+      }
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) acc[j] += pv[j];
+    }
+    for (int s0 = 0; S > 1 && s0 < S; s0 += 4) {
       // every request of the batch at once (clamped, unconditional), then
       // the slices added in order
       float pv[NPL][4];
