@@ -59,6 +59,20 @@ int check_layer(const moe_layer *L) {
 // gate row when there is one.
 int32_t router_rows(const moe_layer *L) { return L->n_experts + (L->shared_gate_w ? 1 : 0); }
 
+// Where a stack layer's fused combine + router launch leaves the next
+// layer's sorted expert groups for a T-token decode batch: after the whole
+// router product [T][Ep] in the partial-logit area (S slices of it), when
+// the next layer's routing can merge them and they fit; else NULL.
+uint2 *sorted_groups(const moe_layer *N, float *part, int32_t T) {
+  const int32_t E = N->n_experts, Ep = router_rows(N);
+  if (!route_sorted_ok(E, N->top_k, N->renorm) || T > kFusedTokens) return nullptr;
+  const int32_t S = N->hidden / route_fused_slice(N->hidden);
+  const size_t logit_floats = (static_cast<size_t>(T) * Ep + 3) & ~static_cast<size_t>(3);  // 16-byte aligned after
+  const size_t need = logit_floats + static_cast<size_t>(T) * route_sorted_groups(E) * kSortedKeep * 2;
+  if (need > static_cast<size_t>(S) * T * Ep) return nullptr;
+  return reinterpret_cast<uint2 *>(part + logit_floats);
+}
+
 constexpr size_t kControlBytes = 256;  // control words kept zero between calls
 
 // The profiling events a call asked for (moe_forward_opts), one pair per
@@ -489,6 +503,7 @@ int layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *
       // (one slice): the gate/up kernel's routing reads it as it is
       fa.S = 1;
       fa.Hs = H;
+      fa.sorted = sorted_groups(L, w.part, T);
       xa.route = fa;
       e = hipSuccess;
     } else {
@@ -576,7 +591,8 @@ int layer_forward(const moe_layer *L, const uint16_t *x_bf16, int32_t T, float *
     // the next layer's router product, from the normalised row this
     // combine forms, into the workspace's partial-logit area
     const moe_layer *N = link.next;
-    CombineRouteArgs cr{ca, N->router_w, N->shared_gate_w, N->n_experts, router_rows(N), w.part};
+    CombineRouteArgs cr{ca, N->router_w, N->shared_gate_w, N->n_experts, router_rows(N), w.part, N->router_bias,
+                        sorted_groups(N, w.part, T)};
     e = launch_combine_route(cr, s);
     if (e == hipSuccess && link.fused) *link.fused = true;
     return hip_status(e);

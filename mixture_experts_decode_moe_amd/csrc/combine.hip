@@ -240,8 +240,28 @@ __global__ void __launch_bounds__(kCombineThreads) combine_route_kernel(CombineR
 #pragma unroll
     for (int w = 0; w < kCombineThreads / 64; ++w) total += wave_dot[w][tid];
     if (row < a.Ep) a.logits[static_cast<size_t>(t) * a.Ep + row] = total;
+    if (a.sorted && g * kCrRows < a.E) {
+      // the group's experts in selection order: the biased logit as the
+      // routing forms it ((0 + product) + bias, NaN as -inf), ranked by
+      // (key desc, expert asc) among the group's 16 rows; the first
+      // kSortedKeep are written at their ranks
+      const bool ex = row < a.E;
+      const float v = (0.f + total) + (a.bias && ex ? a.bias[row] : 0.f);
+      const uint32_t key = ex ? float_key(v == v ? v : -INFINITY) : 0u;
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < kCrRows; ++j) {
+        const uint32_t kj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), j));
+        rank += (kj > key || (kj == key && j < tid)) ? 1 : 0;
+      }
+      if (rank < kSortedKeep)
+        a.sorted[(static_cast<size_t>(t) * route_sorted_groups(a.E) + g) * kSortedKeep + rank] =
+            make_uint2(key, static_cast<uint32_t>(row));
+    }
   }
 }
+
+static_assert(kCrRows == kSortedGroup, "a block's router rows are one sorted group");
 
 bool combine_route_ok(int H) { return H % 256 == 0 && H / 4 <= kCombineThreads; }
 

@@ -62,6 +62,15 @@ MOE_DEV float sum64(float v) {
 
 MOE_DEV int lane_id() { return __lane_id(); }
 
+// Order-preserving map of a float onto uint32 (NaN must be excluded).
+MOE_DEV uint32_t float_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+MOE_DEV float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Block barrier for data exchanged through LDS only.  __syncthreads() also
 // orders global memory at workgroup scope, which makes every wave wait for
 // all its outstanding global loads and stores (prefetches included); this
@@ -123,6 +132,22 @@ hipError_t launch_topk(const RouteArgs &a, hipStream_t s);
 // batch.
 constexpr int kFusedTokens = 16;    // largest T routed by the fused kernel
 constexpr int kFusedMaxChunks = 2;  // router slice <= 512 floats: float4 per lane
+// Decode routing from sorted expert groups.  The launch that forms a decode
+// batch's whole router product (the previous stack layer's combine) can
+// also write, for every token and every group of kSortedGroup experts, the
+// group's first kSortedKeep (key, expert) pairs in selection order (larger
+// biased logit first, the lower expert on equal logits, NaN as -inf; key =
+// float_key of the logit, 0 for rows past E).  Every selected expert is
+// among its group's first K, so with K <= kSortedKeep the gate/up kernel's
+// routing merges these lists instead of ranking all E logits.  Taken only
+// where the weights are a softmax over the K selected logits (renorm).
+constexpr int kSortedGroup = 16;
+constexpr int kSortedKeep = 8;
+__host__ __device__ inline bool route_sorted_ok(int E, int K, int renorm) {
+  return renorm == 1 && K >= 1 && K <= kSortedKeep && E >= K && E <= 256;
+}
+__host__ __device__ inline int route_sorted_groups(int E) { return (E + kSortedGroup - 1) / kSortedGroup; }
+
 struct RouteFusedArgs {
   const float *router_w;
   const float *router_bias;
@@ -140,6 +165,7 @@ struct RouteFusedArgs {
   float *gate;          // [T] (with gate_w): sigmoid of the gate logit, published with the routing
   int32_t Ep;           // row stride of part: E, or E + 1 with the gate row
   int32_t tail_skip;    // 0, or N: experts no token ranks among its first N are left out
+  const uint2 *sorted;  // [T][groups][kSortedKeep] (S = 1 only) or NULL: the logits' sorted groups
 };
 hipError_t launch_route_fused(const RouteFusedArgs &a, hipStream_t s);    // partials + selection
 hipError_t launch_route_partial(const RouteFusedArgs &a, hipStream_t s);  // partials only
@@ -247,6 +273,8 @@ struct CombineRouteArgs {
   const float *gate_w;    // its shared gate row [H], or NULL
   int32_t E, Ep;          // its experts; Ep = E (+ 1 with the gate row)
   float *logits;          // [T][Ep]: the next layer's router products (no bias)
+  const float *bias;      // its router bias [E] or NULL (used for the sorted groups)
+  uint2 *sorted;          // [T][groups][kSortedKeep] or NULL: the biased logits' sorted groups
 };
 bool combine_route_ok(int H);
 hipError_t launch_combine_route(const CombineRouteArgs &a, hipStream_t s);

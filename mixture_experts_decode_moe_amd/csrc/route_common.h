@@ -8,14 +8,6 @@
 
 namespace moe {
 
-// Order-preserving map of a float onto uint32 (NaN must be excluded).
-MOE_DEV uint32_t float_key(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-MOE_DEV float key_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 template <int CTRL>
 MOE_DEV uint32_t dpp_u32(uint32_t v) {
@@ -90,6 +82,38 @@ MOE_DEV float topk_weight(const float (&v)[NPL], int32_t E, int32_t K, int32_t r
 // (each lane's first pair is its lowest expert of that key).  The winning
 // lane drops its first pair.  Results are those of the rule "largest
 // logit, lower index on equal logits", round by round.
+// The K rounds over per-lane lists sorted by (key desc, expert asc) (key 0:
+// used or absent).  Each round: the maximum in every lane, the winning lane
+// (the lowest expert among equal keys, rare), the winner's expert by one
+// lane read, and the winner's list shifted with selects (no branch, no
+// exec-mask copies); lane k keeps round k's key and expert.
+template <int NPL>
+MOE_DEV void wave_topk_rounds(uint32_t (&key)[NPL], int (&idx)[NPL], int32_t K, uint32_t &my_key, int &my_e) {
+  const int lane = __lane_id();
+  my_key = 0u;
+  my_e = 0;
+  for (int k = 0; k < K; ++k) {
+    const uint32_t m = wave_max_all_u32(key[0]);
+    bool win = key[0] == m;
+    uint64_t hit = __ballot(win);
+    if (__popcll(hit) != 1) {
+      const uint32_t lo = wave_min_u32(win ? static_cast<uint32_t>(idx[0]) : 0xFFFFFFFFu);
+      win = win && static_cast<uint32_t>(idx[0]) == lo;
+      hit = __ballot(win);
+    }
+    const int sel = __builtin_amdgcn_readlane(idx[0], __builtin_ctzll(hit));
+#pragma unroll
+    for (int j = 0; j + 1 < NPL; ++j) {
+      key[j] = win ? key[j + 1] : key[j];
+      idx[j] = win ? idx[j + 1] : idx[j];
+    }
+    key[NPL - 1] = win ? 0u : key[NPL - 1];
+    const bool mine = lane == k;
+    my_key = mine ? m : my_key;
+    my_e = mine ? sel : my_e;
+  }
+}
+
 template <int NPL>
 MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t renorm, int &my_e, float &my_w) {
   const int lane = __lane_id();
@@ -118,32 +142,8 @@ MOE_DEV void wave_topk(const float (&v)[NPL], int32_t E, int32_t K, int32_t reno
       cswap(1, 3);
       cswap(1, 2);
     }
-    // Each round: the maximum in every lane, the winning lane (the lowest
-    // expert among equal keys, rare), the winner's expert by one lane read,
-    // and the winner's list shifted with selects (no branch, no exec-mask
-    // copies); lane k keeps round k's key and expert.
-    uint32_t my_key = 0u;
-    my_e = 0;
-    for (int k = 0; k < K; ++k) {
-      const uint32_t m = wave_max_all_u32(key[0]);
-      bool win = key[0] == m;
-      uint64_t hit = __ballot(win);
-      if (__popcll(hit) != 1) {
-        const uint32_t lo = wave_min_u32(win ? static_cast<uint32_t>(idx[0]) : 0xFFFFFFFFu);
-        win = win && static_cast<uint32_t>(idx[0]) == lo;
-        hit = __ballot(win);
-      }
-      const int sel = __builtin_amdgcn_readlane(idx[0], __builtin_ctzll(hit));
-#pragma unroll
-      for (int j = 0; j + 1 < NPL; ++j) {
-        key[j] = win ? key[j + 1] : key[j];
-        idx[j] = win ? idx[j + 1] : idx[j];
-      }
-      key[NPL - 1] = win ? 0u : key[NPL - 1];
-      const bool mine = lane == k;
-      my_key = mine ? m : my_key;
-      my_e = mine ? sel : my_e;
-    }
+    uint32_t my_key;
+    wave_topk_rounds<NPL>(key, idx, K, my_key, my_e);
     const float top_v = key_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(my_key, 0)));
     my_w = topk_weight<NPL>(v, E, K, renorm, key_float(my_key), top_v);
     return;
@@ -414,57 +414,77 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
   // the bias (when there is one) requested with the first partials
   float bias[NPL];
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) bias[j] = a.router_bias ? a.router_bias[min(lane + 64 * j, E - 1)] : 0.f;
+  for (int j = 0; j < NPL; ++j) bias[j] = a.router_bias && !a.sorted ? a.router_bias[min(lane + 64 * j, E - 1)] : 0.f;
   bool staged = false;
   for (int t = wave; t < T; t += nw) {
-    const float *__restrict__ part = a.part;
-    float acc[NPL];
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
-    if (S == 1) {
-      // whole logits (the previous launch formed them): one request each
-      float pv[NPL];
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) pv[j] = part[static_cast<size_t>(t) * Ep + min(lane + 64 * j, E - 1)];
-      if (!staged) {
-        stage();
-        staged = true;
-      }
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) acc[j] += pv[j];
-    }
-    for (int s0 = 0; S > 1 && s0 < S; s0 += 4) {
-      // every request of the batch at once (clamped, unconditional), then
-      // the slices added in order
-      float pv[NPL][4];
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ex = min(lane + 64 * j, E - 1);
-          const int sl = min(s0 + q, S - 1);
-          pv[j][q] = part[(static_cast<size_t>(sl) * T + t) * Ep + ex];
-        }
-      if (!staged) {
-        stage();
-        staged = true;
-      }
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[j] += (s0 + q < S) ? pv[j][q] : 0.f;
-    }
-    float v[NPL];
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int ex = lane + 64 * j;
-      const float sum = acc[j] + (a.router_bias && ex < E ? bias[j] : 0.f);
-      v[j] = (ex < E && sum == sum) ? sum : -INFINITY;  // NaN never outranks a number
-      if (publish && a.logits && ex < E) a.logits[static_cast<size_t>(t) * E + ex] = sum;
-    }
     int my_e;
     float my_w;
-    wave_topk<NPL>(v, E, K, a.renorm, my_e, my_w);
+    if (a.sorted) {
+      // the previous launch's sorted groups: lane l holds ranks 2 (l % 4)
+      // and 2 (l % 4) + 1 of group l / 4 (a sorted pair), so the rounds
+      // start from the token's 128 candidates with no sorting
+      const int G = route_sorted_groups(E), gi = lane >> 2;
+      const uint4 e = reinterpret_cast<const uint4 *>(
+          a.sorted + (static_cast<size_t>(t) * G + (gi < G ? gi : G - 1)) * kSortedKeep)[lane & 3];
+      if (!staged) {
+        stage();
+        staged = true;
+      }
+      uint32_t key[2] = {gi < G ? e.x : 0u, gi < G ? e.z : 0u};
+      int idx[2] = {static_cast<int>(e.y), static_cast<int>(e.w)};
+      uint32_t my_key;
+      wave_topk_rounds<2>(key, idx, K, my_key, my_e);
+      const float top_v = key_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(my_key, 0)));
+      const float none[1] = {0.f};  // (a softmax over the K selected: the logits are not read)
+      my_w = topk_weight<1>(none, E, K, 1, key_float(my_key), top_v);
+    } else {
+      const float *__restrict__ part = a.part;
+      float acc[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
+      if (S == 1) {
+        // whole logits (the previous launch formed them): one request each
+        float pv[NPL];
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) pv[j] = part[static_cast<size_t>(t) * Ep + min(lane + 64 * j, E - 1)];
+        if (!staged) {
+          stage();
+          staged = true;
+        }
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) acc[j] += pv[j];
+      }
+      for (int s0 = 0; S > 1 && s0 < S; s0 += 4) {
+        // every request of the batch at once (clamped, unconditional), then
+        // the slices added in order
+        float pv[NPL][4];
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ex = min(lane + 64 * j, E - 1);
+            const int sl = min(s0 + q, S - 1);
+            pv[j][q] = part[(static_cast<size_t>(sl) * T + t) * Ep + ex];
+          }
+        if (!staged) {
+          stage();
+          staged = true;
+        }
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[j] += (s0 + q < S) ? pv[j][q] : 0.f;
+      }
+      float v[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int ex = lane + 64 * j;
+        const float sum = acc[j] + (a.router_bias && ex < E ? bias[j] : 0.f);
+        v[j] = (ex < E && sum == sum) ? sum : -INFINITY;  // NaN never outranks a number
+        if (publish && a.logits && ex < E) a.logits[static_cast<size_t>(t) * E + ex] = sum;
+      }
+      wave_topk<NPL>(v, E, K, a.renorm, my_e, my_w);
+    }
     // the wave's own LDS operations run in order: clear, then set the bits
     if (lane < mwords) {
       L.mask[t][lane] = 0u;
