@@ -121,3 +121,37 @@ def test_stack_one_layer_is_the_layer_call(mb):
     one = pu.run_layer(dl, pu.dev_u16(x), T, residual=pu.dev_u16(x), with_logits=False)
     for key in ("y", "ids", "w", "residual_out", "normed_out"):
         assert np.array_equal(st[key], one[key]), key
+
+
+def test_stack_sorted_groups_exact_ties(mb):
+    """The stack's second layer routes from the sorted expert groups the
+    first layer's combine wrote.  Its router rows repeat with period 8 and
+    its bias too, so every logit is bit-equal to seven others in its group
+    and across groups: the selection must be the eight lowest copies of the
+    best row, ascending, exactly the oracle's selection, with equal weights."""
+    import dataclasses
+    import parity_util as pu
+    shape = dataclasses.replace(synth.CONFIGS[3], layers=2)
+    T, H, E, K = shape.tokens, shape.hidden, shape.n_experts, shape.top_k
+    l0 = synth.make_layer(shape, layer=0)
+    l1 = synth.make_layer(shape, layer=1)
+    period = np.arange(E) % 8
+    l1.router_w = np.ascontiguousarray(l1.router_w[period])
+    if l1.router_bias is not None:
+        l1.router_bias = np.ascontiguousarray(l1.router_bias[period])
+    d0, d1 = mb.layer_to_device(l0), mb.layer_to_device(l1)
+    ws = mb.make_workspace(d0, T)
+    x0 = synth.make_x(shape)
+    x_dev = pu.dev_u16(x0)
+    say("stack of 2 layers, second layer's router rows repeating")
+    one = _run_stack(mb, [d0.c()], x_dev, x_dev, ws, T, H, K)
+    two = _run_stack(mb, [d0.c(), d1.c()], x_dev, x_dev, ws, T, H, K)
+    lg = oracle.router_logits(l1, one["normed_out"])
+    assert np.array_equal(lg, lg[:, period]), "repeated rows must give equal oracle logits"
+    exp_ids, _ = oracle.select(lg, K, shape.renorm)
+    assert np.array_equal(two["ids"], exp_ids), "selection differs from the lowest-index rule"
+    best = np.argmax(lg[:, :8], axis=1)
+    assert np.array_equal(two["ids"], best[:, None] + 8 * np.arange(K)[None, :])
+    assert np.allclose(two["w"], 1.0 / K, rtol=0, atol=1e-7)
+    err, _ = pu.check_layer_against_oracle(l1, one["normed_out"], two)
+    say(f"  rel err {err:.2e}")
