@@ -180,10 +180,30 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
 // adds its four sums), then over the waves in order.
 constexpr int kCrRows = 16;
 
+// The (token, group) pair of block b of the T x G blocks.  Block b runs on
+// XCD b mod 8, and each XCD has its own L2: the pairs are laid out in bands
+// of kCrBand tokens, group-major within a band, and each XCD takes a
+// contiguous run of that order, so its blocks share the router rows of a few
+// groups and the expert rows of a few tokens.  (With t fastest in the block
+// id, every XCD held all groups and read the whole router matrix: eight
+// copies of it from HBM a launch.)
+constexpr int kCrBand = 8;
+
+MOE_DEV void cr_pair(int b, int T, int G, int &t, int &g) {
+  const int N = T * G, q = N >> 3, rem = N & 7, x = b & 7;
+  const int p = x * q + (x < rem ? x : rem) + (b >> 3);  // blocks on XCDs < x come first
+  const int full = T / kCrBand;
+  const int nb = p < full * kCrBand * G ? kCrBand : T - kCrBand * full;  // tokens in p's band
+  const int band = p / (kCrBand * G), r = p - band * kCrBand * G;
+  g = r / nb;
+  t = kCrBand * band + (r - g * nb);
+}
+
 __global__ void __launch_bounds__(kCombineThreads) combine_route_kernel(CombineRouteArgs a) {
   __shared__ float wave_sq[kCombineThreads / 64];
   __shared__ float wave_dot[kCombineThreads / 64][kCrRows];
-  const int t = blockIdx.x, g = blockIdx.y;
+  int t, g;
+  cr_pair(blockIdx.x, a.c.T, (a.Ep + kCrRows - 1) / kCrRows, t, g);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const CombineArgs &c = a.c;
   const int n4 = c.H / 4;
@@ -268,8 +288,8 @@ bool combine_route_ok(int H) { return H % 256 == 0 && H / 4 <= kCombineThreads; 
 hipError_t launch_combine_route(const CombineRouteArgs &a, hipStream_t s) {
   if (a.c.T == 0) return hipSuccess;
   if (!combine_route_ok(a.c.H) || !a.c.normed_out || !a.c.residual_out) return hipErrorInvalidValue;
-  const dim3 grid(a.c.T, (a.Ep + kCrRows - 1) / kCrRows);
-  combine_route_kernel<<<grid, kCombineThreads, 0, s>>>(a);
+  const int blocks = a.c.T * ((a.Ep + kCrRows - 1) / kCrRows);
+  combine_route_kernel<<<blocks, kCombineThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
