@@ -14,6 +14,14 @@ MOE_DEV uint32_t dpp_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 
+// Maximum over each 16-lane row, left in every lane of the row.
+MOE_DEV uint32_t row_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  return max(v, dpp_u32<0x140>(v));  // row_mirror
+}
+
 // Wave-wide maximum (uniform result).
 MOE_DEV uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
@@ -202,6 +210,7 @@ struct RouteLds {
   int active[kRouteMaxExperts];
   int scan[16];
   int n_active;
+  __attribute__((aligned(16))) uint2 lists[16 * 16 * kSortedKeep];  // sorted groups: (token, group) lists of (key, expert)
 };
 
 // Exclusive scan of one value per thread over the block (up to 16 waves);
@@ -402,6 +411,99 @@ struct NoStage {
   MOE_DEV void operator()() const {}
 };
 
+// The top-k from the previous launch's sorted groups (route_sorted_ok:
+// renormalised weights, K <= 8, E <= 256), four tokens a wave: 16-lane row
+// r holds token 4 (wave + nw j) + r, and lane i of the row the (up to)
+// eight pairs of group i (experts 16 i .. 16 i + 15), ranked by (key desc,
+// expert asc).  Every selected expert is among its group's first eight, and
+// the groups are in expert order, so each round is the row's largest head
+// key, won by the lowest lane that holds it (the lowest expert of that key
+// across groups, the group's lowest within one); the winner drops its head.
+// The weights are the softmax over the K selections with the sum in round
+// order, the arithmetic of topk_weight with renormalisation.
+template <class Stage>
+MOE_DEV void route_sorted_rows(const RouteFusedArgs &a, RouteLds &L, bool publish, const Stage &stage, bool &staged) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  const int T = a.T, E = a.E, K = a.K;
+  const int mwords = (E + 31) / 32;  // <= 8
+  const int N = a.tail_skip > 0 ? min(a.tail_skip, K) : 0;
+  const int G = route_sorted_groups(E);  // <= 16
+  const int r = lane >> 4, i = lane & 15;
+  for (int t0 = 4 * wave; t0 < T; t0 += 4 * nw) {
+    const int t = t0 + r;
+    const bool tv = t < T;
+    // the four tokens' lists (contiguous in the sorted array) into LDS,
+    // 16 bytes a lane a request; each lane then holds its own list's head
+    // and the pair after it, and reads the next pair ahead of each round
+    const int n16 = T * G * (kSortedKeep / 2);  // 16-byte pieces of the array
+    const int p0 = t0 * G * (kSortedKeep / 2);
+    uint4 pc[kSortedKeep / 2];
+#pragma unroll
+    for (int q = 0; q < kSortedKeep / 2; ++q)
+      pc[q] = reinterpret_cast<const uint4 *>(a.sorted)[min(p0 + lane + 64 * q, n16 - 1)];
+    if (!staged) {
+      stage();
+      staged = true;
+    }
+#pragma unroll
+    for (int q = 0; q < kSortedKeep / 2; ++q)
+      if (p0 + lane + 64 * q < n16) reinterpret_cast<uint4 *>(L.lists)[p0 + lane + 64 * q] = pc[q];
+    const bool gv = tv && i < G;
+    const uint2 *my = L.lists + ((tv ? t : t0) * G + (i < G ? i : G - 1)) * kSortedKeep;
+    const uint2 h0 = my[0], n0 = my[1];
+    uint32_t hk = gv ? h0.x : 0u, nk = gv ? n0.x : 0u;  // 0: used or absent
+    int hi = static_cast<int>(h0.y), ni = static_cast<int>(n0.y);
+    int c = 1;  // list position of (nk, ni)
+    // the row's own LDS operations run in order: clear, then (below) set the bits
+    if (tv && i < mwords) {
+      L.mask[t][i] = 0u;
+      L.early[t][i] = 0u;
+    }
+    uint32_t my_key = 0u, top_key = 0u;
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+      // the pair after (nk, ni), read ahead by every lane (a winner takes it)
+      const uint2 nx = my[c + 1 < kSortedKeep ? c + 1 : kSortedKeep - 1];
+      const uint32_t m = row_max_u32(hk);
+      bool win = hk == m;
+      // the row's lanes holding m (at least one: m is one of their keys)
+      const uint32_t rowbits = static_cast<uint32_t>(__ballot(win) >> (lane & 48)) & 0xFFFFu;
+      win = win && i == __builtin_ctz(rowbits);
+      if (win && tv) L.ids[t * K + k] = hi;
+      my_key = i == k ? m : my_key;
+      top_key = k == 0 ? m : top_key;
+      hk = win ? nk : hk;
+      hi = win ? ni : hi;
+      nk = win ? (c + 1 < kSortedKeep && gv ? nx.x : 0u) : nk;
+      ni = win ? static_cast<int>(nx.y) : ni;
+      c += win ? 1 : 0;
+    }
+    const bool sel = tv && i < K;
+    const int p = (tv ? t : 0) * K + i;
+    const float mine = i < K ? expf(key_float(my_key) - key_float(top_key)) : 0.f;
+    if (sel) L.w[p] = mine;
+    float denom = 0.f;
+    for (int k = 0; k < K; ++k) denom += L.w[(tv ? t : 0) * K + k];
+    if (sel) {
+      const float my_w = mine / denom;
+      const int my_e = L.ids[p];
+      L.w[p] = my_w;
+      if (publish) {
+        a.ids[p] = my_e;
+        a.w[p] = my_w;
+      }
+      atomicOr(&L.mask[t][my_e >> 5], 1u << (my_e & 31));
+      if (i < N) atomicOr(&L.early[t][my_e >> 5], 1u << (my_e & 31));
+    }
+    if (a.gate_w && tv) {
+      const float gv2 = route_gate(a, t);
+      if (publish && i == 0) a.gate[t] = gv2;
+    }
+  }
+}
+
 template <int NPL, class Stage = NoStage>
 MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish, const Stage &stage = Stage()) {
   static_assert(NPL <= 4, "E <= 256");
@@ -416,28 +518,11 @@ MOE_DEV void route_small_topk(const RouteFusedArgs &a, RouteLds &L, bool publish
 #pragma unroll
   for (int j = 0; j < NPL; ++j) bias[j] = a.router_bias && !a.sorted ? a.router_bias[min(lane + 64 * j, E - 1)] : 0.f;
   bool staged = false;
-  for (int t = wave; t < T; t += nw) {
+  if (a.sorted) route_sorted_rows(a, L, publish, stage, staged);
+  for (int t = wave; !a.sorted && t < T; t += nw) {
     int my_e;
     float my_w;
-    if (a.sorted) {
-      // the previous launch's sorted groups: lane l holds ranks 2 (l % 4)
-      // and 2 (l % 4) + 1 of group l / 4 (a sorted pair), so the rounds
-      // start from the token's 128 candidates with no sorting
-      const int G = route_sorted_groups(E), gi = lane >> 2;
-      const uint4 e = reinterpret_cast<const uint4 *>(
-          a.sorted + (static_cast<size_t>(t) * G + (gi < G ? gi : G - 1)) * kSortedKeep)[lane & 3];
-      if (!staged) {
-        stage();
-        staged = true;
-      }
-      uint32_t key[2] = {gi < G ? e.x : 0u, gi < G ? e.z : 0u};
-      int idx[2] = {static_cast<int>(e.y), static_cast<int>(e.w)};
-      uint32_t my_key;
-      wave_topk_rounds<2>(key, idx, K, my_key, my_e);
-      const float top_v = key_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(my_key, 0)));
-      const float none[1] = {0.f};  // (a softmax over the K selected: the logits are not read)
-      my_w = topk_weight<1>(none, E, K, 1, key_float(my_key), top_v);
-    } else {
+    {
       const float *__restrict__ part = a.part;
       float acc[NPL];
 #pragma unroll
