@@ -398,27 +398,29 @@ MOE_DEV int wave_incl_sum(int x) {
 }
 
 // The same routing for E <= 256 (NPL <= 4) in three phases with fewer
-// block-wide steps: each token's wave takes the token's top-k and builds
+// block-wide steps: each token's wave (four tokens a wave when the
+// previous launch left sorted groups) takes the token's top-k and builds
 // its expert bitmask (route_small_topk); wave 0 derives the counts,
 // offsets and active list from the masks (route_small_scan); every thread
 // then places pairs (route_small_rows).  The phases are separated by block
 // barriers, so a caller can start work that needs only the active list
 // before the rows are placed.  Results are identical to route_in_block's.
-// `stage` runs once per wave, after the wave's first partial-logit
-// requests are out and before they are used (the gate/up kernel stages its
-// x rows there, so their wait overlaps the partials' round trip).
+// `stage` runs once per wave, after the wave's first partial-logit (or
+// sorted-group) requests are out and before they are used (the gate/up
+// kernel stages its x rows there, so their wait overlaps that round trip).
 struct NoStage {
   MOE_DEV void operator()() const {}
 };
 
 // The top-k from the previous launch's sorted groups (route_sorted_ok:
 // renormalised weights, K <= 8, E <= 256), four tokens a wave: 16-lane row
-// r holds token 4 (wave + nw j) + r, and lane i of the row the (up to)
-// eight pairs of group i (experts 16 i .. 16 i + 15), ranked by (key desc,
-// expert asc).  Every selected expert is among its group's first eight, and
-// the groups are in expert order, so each round is the row's largest head
-// key, won by the lowest lane that holds it (the lowest expert of that key
-// across groups, the group's lowest within one); the winner drops its head.
+// r holds token 4 (wave + nw j) + r, and lane i of the row merges the (up
+// to) eight pairs of group i (experts 16 i .. 16 i + 15), ranked by (key
+// desc, expert asc) and staged in LDS.  Every selected expert is among its
+// group's first eight, and the groups are in expert order, so each round is
+// the row's largest head key, won by the lowest lane that holds it (the
+// lowest expert of that key across groups, the group's lowest within one);
+// the winner's list advances by one pair.
 // The weights are the softmax over the K selections with the sum in round
 // order, the arithmetic of topk_weight with renormalisation.
 template <class Stage>
